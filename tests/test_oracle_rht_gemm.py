@@ -1,0 +1,168 @@
+"""Pins of the oracle's random Hadamard transform and GEMM references.
+
+RHT: "Pretraining Large Language Models with NVFP4", Technische
+Zusammenfassung 2.B.2 -- a 16x16 Hadamard rotation, applied only to the inputs
+of the weight-gradient GEMM.  GEMM: the three passes of a linear layer
+(2.B.2 names Fprop, Dgrad and Wgrad).
+"""
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from quantize_precision_gemm_amd import workloads as wl
+from tests import exact_nvfp4 as ex
+
+
+def hadamard16():
+    """Sylvester Hadamard matrix from its closed form H[i][k] = (-1)^popcount(i & k)."""
+    return np.array([[(-1) ** bin(i & k).count("1") for k in range(16)] for i in range(16)],
+                    dtype=np.int64)
+
+
+def test_hadamard_orthogonality():
+    # I-7: H H^T = 16 I, exactly (integers)
+    H = hadamard16()
+    np.testing.assert_array_equal(H @ H.T, 16 * np.eye(16, dtype=np.int64))
+
+
+def test_rht16_equals_matrix_form_on_integers():
+    # On small integer vectors every butterfly sum is exact, so the transform must
+    # equal (1/4) H D v exactly, for every position and sign pattern.
+    H = hadamard16()
+    rng = np.random.default_rng(0)
+    for mask in [0, 1, 0x8000, 0xFFFF, 0x5A5A] + list(rng.integers(0, 65536, 20)):
+        mask = int(mask)
+        d = np.array([-1 if (mask >> i) & 1 else 1 for i in range(16)])
+        for _ in range(10):
+            v = rng.integers(-1000, 1000, 16)
+            want = (H @ (d * v)) / 4.0
+            got = oracle.rht16(v.astype(np.float32), mask)
+            np.testing.assert_array_equal(got, want)
+        for k in range(16):  # unit vectors give the columns of (1/4) H D
+            e = np.zeros(16)
+            e[k] = 1
+            np.testing.assert_array_equal(oracle.rht16(e.astype(np.float32), mask),
+                                          H[:, k] * d[k] / 4.0)
+
+
+def test_rht16_inverts_and_is_close_to_exact():
+    # Q = (1/4) H D is orthogonal: Q^T Q v = v.  On random fp32 data the fp32
+    # butterfly stays within a few ulps of the exact transform.
+    H = hadamard16().astype(np.float64)
+    rng = np.random.default_rng(1)
+    for _ in range(200):
+        mask = int(rng.integers(0, 65536))
+        d = np.array([-1.0 if (mask >> i) & 1 else 1.0 for i in range(16)])
+        v = (rng.standard_normal(16) * np.exp(rng.uniform(-5, 5))).astype(np.float32)
+        w = oracle.rht16(v, mask).astype(np.float64)
+        exact = (H @ (d * v.astype(np.float64))) / 4
+        scale = np.abs(v).astype(np.float64).sum() / 4
+        assert np.abs(w - exact).max() <= 8 * 2.0 ** -24 * scale
+        back = d * (H.T @ w) / 4
+        np.testing.assert_allclose(back, v, rtol=0, atol=1e-6 * np.abs(v).max())
+
+
+def test_rht_transform_preserves_wgrad_product():
+    # (Q dY)^T (Q X) = dY^T X for the unquantised operands (fp32 tolerance).
+    rng = np.random.default_rng(2)
+    dy = wl.normal(rng, (64, 48), 1.0)
+    x = wl.normal(rng, (64, 40), 1.0)
+    mask = oracle.rht_sign_mask(5)
+    A = oracle.rht_transform(dy, mask).astype(np.float64)   # 48 x 64
+    B = oracle.rht_transform(x, mask).astype(np.float64)    # 40 x 64
+    ref = wl.bf16_bits_to_f32(dy).astype(np.float64).T @ wl.bf16_bits_to_f32(x).astype(np.float64)
+    np.testing.assert_allclose(A @ B.T, ref, rtol=0, atol=1e-5 * np.abs(ref).max())
+
+
+def test_rht_quantize_brute_force():
+    # The quantised wgrad operand equals the exact-arithmetic quantiser applied to
+    # the oracle's fp32 transform (every transformed value is an fp32 number, so
+    # it is fed to the exact model as such).
+    rng = np.random.default_rng(3)
+    x = wl.normal(rng, (32, 3), 1.0)
+    mask = oracle.rht_sign_mask(9)
+    for rounding in (oracle.RNE, oracle.SR):
+        q = oracle.rht_quantize(x, mask, rounding, seed=77)
+        t = oracle.rht_transform(x, mask)  # 3 x 32 fp32
+        flat = [Fraction(float(v)) for v in t.reshape(-1)]
+        amax = max(abs(v) for v in flat)
+        assert np.float32(q.amax) == np.float32(float(amax))
+        s_enc = ex.tensor_scale(amax)
+        assert np.float32(q.s_enc) == np.float32(float(s_enc))
+        draws = oracle.sr_draws(77, 0, len(flat))
+        codes = oracle.unpack_codes(q.codes, 32).reshape(-1)
+        for b in range(len(flat) // 16):
+            blk = flat[16 * b: 16 * b + 16]
+            am = max(abs(v) for v in blk)
+            sb = ex.nearest_e4m3(ex.round_f32(ex.round_f32(am / 6) * s_enc))
+            assert q.scales.reshape(-1)[b] == sb
+            S = ex.E4M3_VAL[sb]
+            f = ex.round_f32(s_enc / S) if S > 0 else Fraction(0)
+            for i, v in enumerate(blk):
+                y = ex.round_f32(abs(v) * f)
+                c = ex.nearest_e2m1_code(y) if rounding == oracle.RNE else \
+                    ex.sr_e2m1_code(y, int(draws[16 * b + i]))
+                sign = 8 if np.signbit(t.reshape(-1)[16 * b + i]) else 0
+                assert codes[16 * b + i] == (sign | c)
+
+
+def _exact_gemm(a, b, dgrad=False):
+    """Exact rational GEMM of dequantised operands (q * S / s_enc)."""
+    A = oracle.dequantize_qs(a)
+    B = oracle.dequantize_qs(b)
+    if dgrad:
+        B = B.T
+    alpha = Fraction(1) / (Fraction(a.s_enc) * Fraction(b.s_enc))
+    M, N = A.shape[0], B.shape[0]
+    out = np.empty((M, N))
+    for m in range(M):
+        for n in range(N):
+            s = sum(Fraction(float(A[m, k])) * Fraction(float(B[n, k])) for k in range(A.shape[1]))
+            out[m, n] = float(s * alpha)
+    return out
+
+
+def test_gemm_reference_matches_exact_rationals():
+    # I-10 (exactness part): the fp64 reference equals the exact product of the
+    # dequantised operands to fp64 rounding, for all three passes.
+    rng = np.random.default_rng(4)
+    x = wl.normal(rng, (4, 32), 1.0)
+    w = wl.normal(rng, (16, 32), 0.02)
+    dy = wl.lognormal_rows(rng, (4, 16))
+    qx = oracle.quantize(x)
+    qw = oracle.quantize(w, oracle.BLOCK_16X16)
+    qdy = oracle.quantize(dy, rounding=oracle.SR, seed=3)
+    y = oracle.gemm(oracle.FPROP, qx, qw)
+    np.testing.assert_allclose(y, _exact_gemm(qx, qw), rtol=1e-13, atol=0)
+    dx = oracle.gemm(oracle.DGRAD, qdy, qw)
+    np.testing.assert_allclose(dx, _exact_gemm(qdy, qw, dgrad=True), rtol=1e-13, atol=0)
+    mask = oracle.rht_sign_mask(1)
+    dyt = oracle.rht_quantize(wl.normal(rng, (32, 4), 1.0), mask, oracle.SR, 5)
+    xt = oracle.rht_quantize(wl.normal(rng, (32, 5), 1.0), mask, oracle.RNE)
+    dw = oracle.gemm(oracle.WGRAD, dyt, xt)
+    np.testing.assert_allclose(dw, _exact_gemm(dyt, xt), rtol=1e-13, atol=0)
+
+
+def test_gemm_fp32_accumulation_within_budget():
+    # I-10 (tolerance part): an fp32 GEMM that sums exact 16-block partials in
+    # order stays within 1e-6 relative Frobenius of the fp64 reference at the
+    # longest contraction of the layer shapes (20480), well inside the 1e-5 budget.
+    rng = np.random.default_rng(5)
+    K = 20480
+    a = oracle.quantize(wl.lognormal_rows(rng, (8, K)), rounding=oracle.SR, seed=9)
+    b = oracle.quantize(wl.normal(rng, (32, K), 0.02), oracle.BLOCK_16X16)
+    ref = oracle.gemm(oracle.FPROP, a, b)
+    f32 = oracle.gemm_fp32_blocks(a, b).astype(np.float64)
+    err = np.linalg.norm(f32 - ref) / np.linalg.norm(ref)
+    assert err < 1e-6
+
+
+def test_gemm_sampled_rows_match_full():
+    rng = np.random.default_rng(6)
+    a = oracle.quantize(wl.normal(rng, (40, 64), 1.0))
+    b = oracle.quantize(wl.normal(rng, (32, 64), 0.02), oracle.BLOCK_16X16)
+    full = oracle.gemm(oracle.FPROP, a, b)
+    rows = np.array([0, 7, 39])
+    np.testing.assert_array_equal(oracle.gemm(oracle.FPROP, a, b, rows=rows), full[rows])
