@@ -1,0 +1,200 @@
+/*
+ * nvfp4.h -- C ABI of the NVFP4 quantize -> GEMM library for MI355X (gfx950).
+ *
+ * The library computes the data-parallel hot path of a linear layer trained
+ * with the NVFP4 recipe described on the pages about NVIDIA's report
+ * "Pretraining Large Language Models with NVFP4" (gist.science summary of that
+ * title, "Technische Zusammenfassung" sections 2.A and 2.B):
+ *   - NVFP4 tensors: 4-bit E2M1 elements in 16-element blocks, one E4M3 scale
+ *     per block and one FP32 scale per tensor (section 2.A);
+ *   - weights use 16x16 blocks so that forward and backward see the same
+ *     quantised values (section 2.B.3);
+ *   - the inputs of the weight-gradient GEMM get a 16-point random Hadamard
+ *     transform (section 2.B.2);
+ *   - gradients are rounded stochastically, everything else to nearest even
+ *     (section 2.B.4);
+ *   - GEMMs for the forward (fprop), activation-gradient (dgrad) and
+ *     weight-gradient (wgrad) passes (section 2.B.2 names all three).
+ *
+ * Conventions for every entry point:
+ *   - Every data pointer is a DEVICE pointer on the current HIP device and is
+ *     owned by the caller, who keeps it alive until the work queued on
+ *     `stream` has finished.  `nvfp4_tensor*` arguments are HOST pointers to
+ *     descriptors of device buffers.
+ *   - `stream` is a hipStream_t passed as void* (NULL = default stream).  The
+ *     calls only enqueue work: they never synchronise, never allocate device
+ *     or host memory, and keep no state between calls, so they are reentrant.
+ *   - All argument checks happen on the host before anything is enqueued; a
+ *     failed check returns a negative status and enqueues nothing.
+ *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
+ *   - bf16 data is passed as its 16-bit patterns (uint16).
+ *   - Packed codes: element (r, c) of a rows x cols NVFP4 matrix is the
+ *     4-bit code in byte codes[r * ld_codes + c / 2], low nibble for even c.
+ *     Code = sign << 3 | exponent << 1 | mantissa (OCP E2M1: values 0, 0.5,
+ *     1, 1.5, 2, 3, 4, 6).  Scales are OCP E4M3 bytes (bias 7, max 448).
+ *   - The value an NVFP4 element stands for is  e2m1(code) * e4m3(scale) /
+ *     s_enc.
+ */
+#ifndef NVFP4_H
+#define NVFP4_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Status codes. */
+#define NVFP4_OK 0
+#define NVFP4_ERR_NULL (-1)     /* a required pointer is NULL */
+#define NVFP4_ERR_SHAPE (-2)    /* a size is negative or breaks a multiple-of rule */
+#define NVFP4_ERR_ALIGN (-3)    /* a pointer or leading dimension is misaligned */
+#define NVFP4_ERR_MODE (-4)     /* unknown block, rounding, pass or dtype */
+#define NVFP4_ERR_MISMATCH (-5) /* GEMM operands inconsistent with the pass */
+#define NVFP4_ERR_LAUNCH (-6)   /* the HIP runtime reported a launch error */
+
+/* Block layouts. */
+#define NVFP4_BLOCK_1X16 0      /* one scale per 16 consecutive elements of a row */
+#define NVFP4_BLOCK_16X16 1     /* one scale per 16x16 tile (weights) */
+
+/* Rounding of the elements. */
+#define NVFP4_RNE 0             /* round to nearest, ties to even */
+#define NVFP4_SR 1              /* stochastic rounding, Philox4x32-10 */
+
+/* GEMM passes. */
+#define NVFP4_FPROP 0
+#define NVFP4_DGRAD 1
+#define NVFP4_WGRAD 2
+
+/* Output element types. */
+#define NVFP4_OUT_BF16 0
+#define NVFP4_OUT_FP32 1
+
+/*
+ * Descriptor of an NVFP4 tensor (rows x cols, blocks along cols).
+ * The caller allocates the buffers and fills the pointer and leading
+ * dimension fields; the quantisers fill rows, cols and block.
+ *   codes     rows x ld_codes bytes. ld_codes is a multiple of 16 and at
+ *             least round_up(cols, 32) / 2; bytes past cols/2 may hold any
+ *             value (the GEMM masks them).  16-byte aligned.
+ *   scales    1x16 : rows x ld_scales bytes, ld_scales >= cols / 16;
+ *             16x16: rows/16 x ld_scales bytes, ld_scales >= cols / 16.
+ *             ld_scales is even; 2-byte aligned.
+ *   codes_t   optional, 16x16 only: the codes of the transposed matrix
+ *             (cols x ld_codes_t bytes, ld_codes_t a multiple of 16 and at
+ *             least round_up(rows, 32) / 2).  Needed by the DGRAD GEMM.
+ *   scales_t  optional, 16x16 only: the transposed tile scales
+ *             (cols/16 x ld_scales_t bytes, ld_scales_t even and at least
+ *             rows / 16).  Needed by the DGRAD GEMM.
+ *   amax      1 float: max |x| over the tensor as quantised.
+ *   s_enc     1 float: the tensor's FP32 encode scale.
+ */
+typedef struct nvfp4_tensor {
+    uint8_t* codes;
+    uint8_t* scales;
+    uint8_t* codes_t;
+    uint8_t* scales_t;
+    float* amax;
+    float* s_enc;
+    int64_t rows;
+    int64_t cols;
+    int64_t ld_codes;
+    int64_t ld_scales;
+    int64_t ld_codes_t;
+    int64_t ld_scales_t;
+    int32_t block;
+    int32_t reserved;
+} nvfp4_tensor;
+
+/*
+ * nvfp4_quantize -- NVFP4-quantise a row-major bf16 matrix.
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.A (format, two-level scaling), 2.B.3 (16x16 blocks for
+ * weights), 2.B.4 (RNE for activations and weights, SR for gradients).
+ *   x         device bf16, rows x ld_x elements, row-major; 16-byte aligned,
+ *             ld_x >= cols and a multiple of 8.
+ *   rows      >= 0; a multiple of 16 for NVFP4_BLOCK_16X16.
+ *   cols      >= 0 and a multiple of 16 (a block has 16 elements).
+ *   block     NVFP4_BLOCK_1X16 or NVFP4_BLOCK_16X16.
+ *   rounding  NVFP4_RNE or NVFP4_SR.
+ *   seed      Philox key for SR: the 16-bit draw of element (r, c) comes from
+ *             counter (r*cols + c) / 8; ignored for RNE.
+ *   amax_in   optional device float: if not NULL it is used as the tensor
+ *             amax instead of computing one (e.g. a precomputed amax); it is
+ *             copied to out->amax.
+ *   out       descriptor with codes, scales, amax, s_enc set (and, for
+ *             16x16, optionally codes_t / scales_t, which are then written).
+ * Tensor scale s_enc = 2688 / amax (1 if amax = 0, FLT_MAX if that
+ * overflows); block scale = E4M3(RN(amax_b / 6) * s_enc) rounded to nearest
+ * even and saturated at 448; element code = E2M1 rounding of
+ * x * (s_enc / scale) (a zero scale gives signed zeros).
+ * Returns NVFP4_OK or a negative status.
+ */
+int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block,
+                   int32_t rounding, uint64_t seed, const float* amax_in, nvfp4_tensor* out,
+                   void* stream);
+
+/*
+ * nvfp4_rht_quantize -- weight-gradient operand: 16-point random Hadamard
+ * transform along the token dimension, transpose, then 1x16 quantisation.
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.B.2 (16x16 random Hadamard transform on the inputs of the
+ * weight-gradient GEMM only) and 2.B.4 (SR for gradients).
+ *   x         device bf16, tokens x ld_x elements (row = token); 16-byte
+ *             aligned, ld_x >= channels and a multiple of 8.
+ *   tokens    >= 0, a multiple of 16 (the transform acts on aligned
+ *             16-token chunks).
+ *   channels  >= 0, a multiple of 8.
+ *   sign_mask bit i set means the i-th sign of the random diagonal is -1.
+ *             The transform of a chunk v is (1/4) * H16 * diag(d) * v with
+ *             H16 the Sylvester Hadamard matrix, evaluated as a radix-2
+ *             butterfly (strides 1, 2, 4, 8) in fp32.  Use the same mask for
+ *             both operands of one weight-gradient GEMM.
+ *   rounding, seed, amax_in  as for nvfp4_quantize; SR draws are indexed by
+ *             c * tokens + t in the transposed layout; amax is taken over the
+ *             transformed values.
+ *   out       1x16 descriptor of the channels x tokens result.
+ */
+int nvfp4_rht_quantize(const void* x, int64_t tokens, int64_t channels, int64_t ld_x,
+                       uint32_t sign_mask, int32_t rounding, uint64_t seed,
+                       const float* amax_in, nvfp4_tensor* out, void* stream);
+
+/*
+ * nvfp4_rht_sign_mask -- host helper: the 16 random signs of the Hadamard
+ * transform drawn from a seed: the low 16 bits of word 0 of
+ * Philox4x32-10(key = seed, counter = (0, 0, 0, 1)).
+ */
+uint32_t nvfp4_rht_sign_mask(uint64_t seed);
+
+/*
+ * nvfp4_gemm -- GEMM over NVFP4 operands for the three passes of a linear
+ * layer; fp32 accumulation, alpha = 1 / (s_enc(a) * s_enc(b)) applied in the
+ * epilogue from the device scalars.
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.B.2 (Fprop, Dgrad, Wgrad) and 2.B.3 (the weight keeps its
+ * quantised values in both passes).
+ *   FPROP: a = X  (M x K, 1x16),  b = W (N x K, 1x16 or 16x16)
+ *          c[m, n] = sum_k x^[m,k] * w^[n,k]                  (M x N)
+ *   DGRAD: a = dY (M x N, 1x16),  b = W (N x K, 16x16 with codes_t, scales_t)
+ *          c[m, k] = sum_n dy^[m,n] * w^[n,k]                  (M x K)
+ *   WGRAD: a = RHT(dY)^T (N x M), b = RHT(X)^T (K x M), both 1x16 from
+ *          nvfp4_rht_quantize with one sign mask
+ *          c[n, k] = sum_m a^[n,m] * b^[k,m]                   (N x K)
+ *   c         device output, row-major with leading dimension ldc elements;
+ *             16-byte aligned (8-byte for BF16), ldc a multiple of 4.
+ *   c_dtype   NVFP4_OUT_BF16 (fp32 result rounded to nearest even) or
+ *             NVFP4_OUT_FP32.
+ * The descriptors must be the ones filled by the quantisers (shapes, block
+ * and the device amax/s_enc buffers).  Returns NVFP4_OK or a negative status.
+ */
+int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+               int64_t ldc, int32_t c_dtype, void* stream);
+
+/* Human-readable name of a status code (static string). */
+const char* nvfp4_status_string(int32_t status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* NVFP4_H */

@@ -1,0 +1,218 @@
+"""Python binding of libnvfp4 -- the NVFP4 quantize -> GEMM path for MI355X.
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+``libnvfp4.so`` (C ABI in include/nvfp4.h).  PyTorch provides device memory
+and the current stream.  There is no CPU fallback: if the library is not
+built, every call raises.
+
+Recipe (web pages about NVIDIA's report "Pretraining Large Language Models
+with NVFP4", gist.science summary, Technische Zusammenfassung 2.A-2.B):
+activations X are quantised 1x16 with round-to-nearest-even, weights W 16x16
+with RNE, gradients dY 1x16 with stochastic rounding; the weight-gradient
+GEMM gets both inputs through a 16-point random Hadamard transform along the
+token dimension.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
+    "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm",
+    "nvfp4_rht_sign_mask", "lib_path", "load_library",
+]
+
+BLOCK_1X16 = 0
+BLOCK_16X16 = 1
+RNE = 0
+SR = 1
+FPROP = 0
+DGRAD = 1
+WGRAD = 2
+OUT_BF16 = 0
+OUT_FP32 = 1
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_NAME = "libnvfp4.so"
+_lib = None
+
+
+def lib_path() -> str:
+    return os.path.join(_HERE, _LIB_NAME)
+
+
+class _Desc(ctypes.Structure):
+    """Mirror of struct nvfp4_tensor."""
+    _fields_ = [
+        ("codes", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+        ("codes_t", ctypes.c_void_p), ("scales_t", ctypes.c_void_p),
+        ("amax", ctypes.c_void_p), ("s_enc", ctypes.c_void_p),
+        ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
+        ("ld_codes", ctypes.c_int64), ("ld_scales", ctypes.c_int64),
+        ("ld_codes_t", ctypes.c_int64), ("ld_scales_t", ctypes.c_int64),
+        ("block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+    ]
+
+
+def load_library():
+    """Load libnvfp4.so; raises if it has not been built (no fallback)."""
+    global _lib
+    if _lib is None:
+        path = lib_path()
+        if not os.path.exists(path):
+            raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                               "or python quantize_precision_gemm_amd/build.py")
+        L = ctypes.CDLL(path)
+        P, i64, i32, u32, u64 = (ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32,
+                                 ctypes.c_uint32, ctypes.c_uint64)
+        D = ctypes.POINTER(_Desc)
+        L.nvfp4_quantize.argtypes = [P, i64, i64, i64, i32, i32, u64, P, D, P]
+        L.nvfp4_quantize.restype = ctypes.c_int
+        L.nvfp4_rht_quantize.argtypes = [P, i64, i64, i64, u32, i32, u64, P, D, P]
+        L.nvfp4_rht_quantize.restype = ctypes.c_int
+        L.nvfp4_gemm.argtypes = [i32, D, D, P, i64, i32, P]
+        L.nvfp4_gemm.restype = ctypes.c_int
+        L.nvfp4_rht_sign_mask.argtypes = [u64]
+        L.nvfp4_rht_sign_mask.restype = u32
+        L.nvfp4_status_string.argtypes = [i32]
+        L.nvfp4_status_string.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status, what):
+    if status != 0:
+        msg = load_library().nvfp4_status_string(status).decode()
+        raise RuntimeError(f"{what} failed: status {status} ({msg})")
+
+
+def _round_up(v, m):
+    return (v + m - 1) // m * m
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+class NVFP4Tensor:
+    """Device buffers of an NVFP4 tensor (rows x cols, blocks along cols).
+
+    codes  uint8 [rows, ld_codes]     two E2M1 codes per byte, low nibble first
+    scales uint8 [rows or rows/16, ld_scales]   E4M3 block scales
+    codes_t / scales_t  (16x16 only, optional) the transposed copy used by dgrad
+    amax, s_enc  float32 [1]  tensor amax and FP32 encode scale (device)
+    """
+
+    def __init__(self, codes, scales, amax, s_enc, rows, cols, block, codes_t=None,
+                 scales_t=None):
+        self.codes, self.scales, self.amax, self.s_enc = codes, scales, amax, s_enc
+        self.codes_t, self.scales_t = codes_t, scales_t
+        self.rows, self.cols, self.block = rows, cols, block
+
+    def descriptor(self) -> _Desc:
+        d = _Desc()
+        d.codes, d.scales = self.codes.data_ptr(), self.scales.data_ptr()
+        d.codes_t = self.codes_t.data_ptr() if self.codes_t is not None else None
+        d.scales_t = self.scales_t.data_ptr() if self.scales_t is not None else None
+        d.amax, d.s_enc = self.amax.data_ptr(), self.s_enc.data_ptr()
+        d.rows, d.cols = self.rows, self.cols
+        d.ld_codes, d.ld_scales = self.codes.shape[1], self.scales.shape[1]
+        d.ld_codes_t = self.codes_t.shape[1] if self.codes_t is not None else 0
+        d.ld_scales_t = self.scales_t.shape[1] if self.scales_t is not None else 0
+        d.block = self.block
+        return d
+
+    # --- host copies in the tight layout (for checks) ---
+    def codes_host(self):
+        return self.codes[:, : self.cols // 2].cpu().numpy()
+
+    def scales_host(self):
+        return self.scales[:, : self.cols // 16].cpu().numpy()
+
+    def codes_t_host(self):
+        return self.codes_t[:, : self.rows // 2].cpu().numpy()
+
+    def scales_t_host(self):
+        return self.scales_t[:, : self.rows // 16].cpu().numpy()
+
+
+def alloc_nvfp4(rows, cols, block=BLOCK_1X16, with_transpose=False, device=None):
+    """Allocate the device buffers of a rows x cols NVFP4 tensor (padded leading dims)."""
+    device = device or torch.device("cuda", torch.cuda.current_device())
+    ld_c = _round_up(cols, 32) // 2
+    ld_s = _round_up(max(cols // 16, 1), 4)
+    srows = rows if block == BLOCK_1X16 else rows // 16
+    codes = torch.empty((rows, ld_c), dtype=torch.uint8, device=device)
+    scales = torch.empty((srows, ld_s), dtype=torch.uint8, device=device)
+    amax = torch.empty(1, dtype=torch.float32, device=device)
+    s_enc = torch.empty(1, dtype=torch.float32, device=device)
+    ct = st = None
+    if with_transpose:
+        ct = torch.empty((cols, _round_up(rows, 32) // 2), dtype=torch.uint8, device=device)
+        st = torch.empty((cols // 16, _round_up(max(rows // 16, 1), 4)), dtype=torch.uint8,
+                         device=device)
+    return NVFP4Tensor(codes, scales, amax, s_enc, rows, cols, block, ct, st)
+
+
+def _check_bf16(x):
+    if not (isinstance(x, torch.Tensor) and x.is_cuda and x.dtype == torch.bfloat16 and x.dim() == 2):
+        raise TypeError("expected a 2-D bfloat16 CUDA tensor")
+    if x.stride(1) != 1:
+        raise ValueError("the last dimension must be contiguous")
+
+
+def nvfp4_quantize(x, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None,
+                   with_transpose=False, out=None, stream=None):
+    """Quantise a row-major bf16 matrix to NVFP4 (see nvfp4_quantize in nvfp4.h)."""
+    _check_bf16(x)
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_nvfp4(rows, cols, block, with_transpose and block == BLOCK_16X16, x.device)
+    d = out.descriptor()
+    st = load_library().nvfp4_quantize(_ptr(x), rows, cols, x.stride(0), block, rounding,
+                                       seed, _ptr(amax_in), ctypes.byref(d), _stream(stream))
+    _check(st, "nvfp4_quantize")
+    out.rows, out.cols, out.block = d.rows, d.cols, d.block
+    return out
+
+
+def nvfp4_rht_quantize(x, sign_mask, rounding=RNE, seed=0, amax_in=None, out=None, stream=None):
+    """RHT along tokens + transpose + 1x16 quantisation (see nvfp4_rht_quantize)."""
+    _check_bf16(x)
+    tokens, channels = x.shape
+    if out is None:
+        out = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device)
+    d = out.descriptor()
+    st = load_library().nvfp4_rht_quantize(_ptr(x), tokens, channels, x.stride(0), sign_mask,
+                                           rounding, seed, _ptr(amax_in), ctypes.byref(d),
+                                           _stream(stream))
+    _check(st, "nvfp4_rht_quantize")
+    out.rows, out.cols, out.block = d.rows, d.cols, d.block
+    return out
+
+
+def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None):
+    """NVFP4 GEMM for FPROP / DGRAD / WGRAD (see nvfp4_gemm in nvfp4.h)."""
+    M = a.rows
+    N = b.cols if pass_ == DGRAD else b.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
+        raise TypeError("output must be float32 or bfloat16 with a contiguous last dimension")
+    da, db = a.descriptor(), b.descriptor()
+    st = load_library().nvfp4_gemm(pass_, ctypes.byref(da), ctypes.byref(db), _ptr(out),
+                                   out.stride(0), dt, _stream(stream))
+    _check(st, "nvfp4_gemm")
+    return out
+
+
+def nvfp4_rht_sign_mask(seed):
+    """The 16 random signs of the Hadamard transform drawn from `seed` (bit i: d_i = -1)."""
+    return int(load_library().nvfp4_rht_sign_mask(seed))

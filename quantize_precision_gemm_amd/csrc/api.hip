@@ -1,0 +1,219 @@
+// api.hip -- the C ABI declared in include/nvfp4.h: argument validation and
+// dispatch to the kernels.  Every check runs on the host before anything is
+// enqueued; a failed check returns a negative status and launches nothing.
+#include <stdint.h>
+
+#include "../../include/nvfp4.h"
+#include "internal.hpp"
+
+namespace {
+
+using nvfp4::GemmOperand;
+using nvfp4::QOut;
+
+inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
+
+int launch_status()
+{
+    hipError_t e = hipGetLastError();
+    return e == hipSuccess ? NVFP4_OK : NVFP4_ERR_LAUNCH;
+}
+
+// Checks of an output descriptor for a rows x cols NVFP4 tensor.
+int check_out(const nvfp4_tensor* o, int64_t rows, int64_t cols, int block)
+{
+    const bool empty = rows == 0 || cols == 0;  // empty tensors need no code buffers
+    if (!o || !o->amax || !o->s_enc) return NVFP4_ERR_NULL;
+    if (!empty && (!o->codes || !o->scales)) return NVFP4_ERR_NULL;
+    if (!aligned(o->codes, 16) || o->ld_codes % 16 != 0) return NVFP4_ERR_ALIGN;
+    if (!aligned(o->scales, 4) || o->ld_scales % 4 != 0) return NVFP4_ERR_ALIGN;
+    if (!aligned(o->amax, 4) || !aligned(o->s_enc, 4)) return NVFP4_ERR_ALIGN;
+    if (o->ld_codes < round_up(cols, 32) / 2 || o->ld_scales < cols / 16) return NVFP4_ERR_SHAPE;
+    if (o->codes_t || o->scales_t) {
+        if (block != NVFP4_BLOCK_16X16) return NVFP4_ERR_MODE;
+        if (!empty && (!o->codes_t || !o->scales_t)) return NVFP4_ERR_NULL;
+        if (!aligned(o->codes_t, 16) || o->ld_codes_t % 16 != 0) return NVFP4_ERR_ALIGN;
+        if (!aligned(o->scales_t, 4) || o->ld_scales_t % 4 != 0) return NVFP4_ERR_ALIGN;
+        if (o->ld_codes_t < round_up(rows, 32) / 2 || o->ld_scales_t < rows / 16)
+            return NVFP4_ERR_SHAPE;
+    }
+    return NVFP4_OK;
+}
+
+QOut qout_of(const nvfp4_tensor* o)
+{
+    QOut q;
+    q.codes = o->codes;
+    q.ld_codes = o->ld_codes;
+    q.scales = o->scales;
+    q.ld_scales = o->ld_scales;
+    q.codes_t = o->codes_t;
+    q.ld_codes_t = o->ld_codes_t;
+    q.scales_t = o->scales_t;
+    q.ld_scales_t = o->ld_scales_t;
+    q.amax = o->amax;
+    q.s_enc = o->s_enc;
+    return q;
+}
+
+// A GEMM operand is a descriptor filled by a quantiser: codes, scales and
+// s_enc present, shapes consistent with its block layout.
+int check_operand(const nvfp4_tensor* t)
+{
+    if (!t || !t->s_enc) return NVFP4_ERR_NULL;
+    if (t->rows > 0 && t->cols > 0 && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
+    if (t->block != NVFP4_BLOCK_1X16 && t->block != NVFP4_BLOCK_16X16) return NVFP4_ERR_MODE;
+    if (t->rows < 0 || t->cols < 0 || t->cols % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (t->block == NVFP4_BLOCK_16X16 && t->rows % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (!aligned(t->codes, 16) || t->ld_codes % 16 != 0) return NVFP4_ERR_ALIGN;
+    if (!aligned(t->scales, 4) || t->ld_scales % 4 != 0) return NVFP4_ERR_ALIGN;
+    if (t->ld_codes < round_up(t->cols, 32) / 2 || t->ld_scales < t->cols / 16)
+        return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block,
+                   int32_t rounding, uint64_t seed, const float* amax_in, nvfp4_tensor* out,
+                   void* stream)
+{
+    if (block != NVFP4_BLOCK_1X16 && block != NVFP4_BLOCK_16X16) return NVFP4_ERR_MODE;
+    if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_MODE;
+    if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (block == NVFP4_BLOCK_16X16 && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (!x && rows > 0 && cols > 0) return NVFP4_ERR_NULL;
+    if (ld_x < cols) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld_x % 8 != 0) return NVFP4_ERR_ALIGN;
+    if (amax_in && !aligned(amax_in, 4)) return NVFP4_ERR_ALIGN;
+    int st = check_out(out, rows, cols, block);
+    if (st != NVFP4_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const float* amax_src = amax_in;
+    if (!amax_src) {
+        nvfp4::launch_amax_rows(xb, rows, cols, ld_x, out->amax, s);
+        amax_src = out->amax;
+    }
+    nvfp4::launch_quant(xb, rows, cols, ld_x, block, rounding, seed, amax_src, qout_of(out), s);
+    out->rows = rows;
+    out->cols = cols;
+    out->block = block;
+    return launch_status();
+}
+
+int nvfp4_rht_quantize(const void* x, int64_t tokens, int64_t channels, int64_t ld_x,
+                       uint32_t sign_mask, int32_t rounding, uint64_t seed,
+                       const float* amax_in, nvfp4_tensor* out, void* stream)
+{
+    if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_MODE;
+    if (tokens < 0 || channels < 0 || tokens % 16 != 0 || channels % 8 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!x && tokens > 0 && channels > 0) return NVFP4_ERR_NULL;
+    if (ld_x < channels) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld_x % 8 != 0) return NVFP4_ERR_ALIGN;
+    if (amax_in && !aligned(amax_in, 4)) return NVFP4_ERR_ALIGN;
+    if (out && (out->codes_t || out->scales_t)) return NVFP4_ERR_MODE;
+    int st = check_out(out, channels, tokens, NVFP4_BLOCK_1X16);
+    if (st != NVFP4_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint32_t mask = sign_mask & 0xFFFFu;
+    const float* amax_src = amax_in;
+    if (!amax_src) {
+        nvfp4::launch_rht_amax(xb, tokens, channels, ld_x, mask, out->amax, s);
+        amax_src = out->amax;
+    }
+    nvfp4::launch_rht_quant(xb, tokens, channels, ld_x, mask, rounding, seed, amax_src,
+                            qout_of(out), s);
+    out->rows = channels;
+    out->cols = tokens;
+    out->block = NVFP4_BLOCK_1X16;
+    return launch_status();
+}
+
+// Philox4x32-10 block function on the host (Salmon et al., SC'11).
+static void philox_host(uint32_t c[4], uint32_t k0, uint32_t k1)
+{
+    for (int r = 0; r < 10; ++r) {
+        uint64_t p0 = (uint64_t)0xD2511F53u * c[0];
+        uint64_t p1 = (uint64_t)0xCD9E8D57u * c[2];
+        uint32_t n0 = (uint32_t)(p1 >> 32) ^ c[1] ^ k0;
+        uint32_t n2 = (uint32_t)(p0 >> 32) ^ c[3] ^ k1;
+        c[1] = (uint32_t)p1;
+        c[3] = (uint32_t)p0;
+        c[0] = n0;
+        c[2] = n2;
+        k0 += 0x9E3779B9u;
+        k1 += 0xBB67AE85u;
+    }
+}
+
+uint32_t nvfp4_rht_sign_mask(uint64_t seed)
+{
+    uint32_t c[4] = {0u, 0u, 0u, 1u};
+    philox_host(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    return c[0] & 0xFFFFu;
+}
+
+int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+               int64_t ldc, int32_t c_dtype, void* stream)
+{
+    if (pass != NVFP4_FPROP && pass != NVFP4_DGRAD && pass != NVFP4_WGRAD) return NVFP4_ERR_MODE;
+    if (c_dtype != NVFP4_OUT_BF16 && c_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_MODE;
+    int st = check_operand(a);
+    if (st != NVFP4_OK) return st;
+    st = check_operand(b);
+    if (st != NVFP4_OK) return st;
+    if (!c && a->rows > 0 && (pass == NVFP4_DGRAD ? b->cols : b->rows) > 0) return NVFP4_ERR_NULL;
+    if (!aligned(c, c_dtype == NVFP4_OUT_FP32 ? 16 : 8) || ldc % 4 != 0) return NVFP4_ERR_ALIGN;
+    if (a->block != NVFP4_BLOCK_1X16) return NVFP4_ERR_MISMATCH;
+
+    GemmOperand A{a->codes, a->ld_codes, a->scales, a->ld_scales, 0, a->s_enc};
+    GemmOperand B;
+    int64_t M = a->rows, N, K = a->cols;
+    if (pass == NVFP4_DGRAD) {
+        // c = dY (M x N) * W (N x K): W^T (K x N) is the 16x16-block operand
+        if (b->block != NVFP4_BLOCK_16X16) return NVFP4_ERR_MISMATCH;
+        if (b->rows > 0 && b->cols > 0 && (!b->codes_t || !b->scales_t)) return NVFP4_ERR_NULL;
+        if (b->rows != a->cols) return NVFP4_ERR_MISMATCH;
+        if (!aligned(b->codes_t, 16) || b->ld_codes_t % 16 != 0) return NVFP4_ERR_ALIGN;
+        if (!aligned(b->scales_t, 4) || b->ld_scales_t % 4 != 0) return NVFP4_ERR_ALIGN;
+        if (b->ld_codes_t < round_up(b->rows, 32) / 2 || b->ld_scales_t < b->rows / 16)
+            return NVFP4_ERR_SHAPE;
+        B = GemmOperand{b->codes_t, b->ld_codes_t, b->scales_t, b->ld_scales_t, 4, b->s_enc};
+        N = b->cols;
+    } else {
+        if (b->cols != a->cols) return NVFP4_ERR_MISMATCH;
+        if (pass == NVFP4_WGRAD && b->block != NVFP4_BLOCK_1X16) return NVFP4_ERR_MISMATCH;
+        B = GemmOperand{b->codes, b->ld_codes, b->scales, b->ld_scales,
+                        b->block == NVFP4_BLOCK_16X16 ? 4 : 0, b->s_enc};
+        N = b->rows;
+    }
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    nvfp4::launch_gemm_nt(A, B, M, N, K, c, ldc, c_dtype == NVFP4_OUT_FP32,
+                          static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
+const char* nvfp4_status_string(int32_t status)
+{
+    switch (status) {
+    case NVFP4_OK: return "ok";
+    case NVFP4_ERR_NULL: return "null pointer";
+    case NVFP4_ERR_SHAPE: return "invalid shape";
+    case NVFP4_ERR_ALIGN: return "misaligned pointer or leading dimension";
+    case NVFP4_ERR_MODE: return "unknown mode";
+    case NVFP4_ERR_MISMATCH: return "operands inconsistent with the pass";
+    case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+    }
+}
+
+}  // extern "C"

@@ -1,0 +1,51 @@
+// internal.hpp -- launch functions shared between the C-ABI layer and the
+// kernel translation units.  Callers have validated every argument.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace nvfp4 {
+
+// Quantiser outputs (device pointers; codes_t / scales_t may be null).
+struct QOut {
+    uint8_t* codes;
+    int64_t ld_codes;
+    uint8_t* scales;
+    int64_t ld_scales;
+    uint8_t* codes_t;
+    int64_t ld_codes_t;
+    uint8_t* scales_t;
+    int64_t ld_scales_t;
+    float* amax;
+    float* s_enc;
+};
+
+// One GEMM operand: rows x K NVFP4 codes with 16-element blocks along K.
+// The scale of block b of row r is scales[(r >> scale_row_shift) * ld_scales + b].
+struct GemmOperand {
+    const uint8_t* codes;
+    int64_t ld_codes;
+    const uint8_t* scales;
+    int64_t ld_scales;
+    int scale_row_shift;
+    const float* s_enc;
+};
+
+void launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
+                      hipStream_t s);
+void launch_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int block,
+                  int rounding, uint64_t seed, const float* amax_src, const QOut& o,
+                  hipStream_t s);
+void launch_rht_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
+                     uint32_t mask, float* amax, hipStream_t s);
+void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
+                      uint32_t mask, int rounding, uint64_t seed, const float* amax_src,
+                      const QOut& o, hipStream_t s);
+
+// C[m, n] = (1/s_enc_a) (1/s_enc_b) sum_k a^[m, k] b^[n, k]; out_fp32 selects
+// fp32 or bf16 (round to nearest even) output.
+void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
+                    int64_t K, void* c, int64_t ldc, bool out_fp32, hipStream_t s);
+
+}  // namespace nvfp4

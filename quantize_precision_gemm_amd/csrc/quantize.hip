@@ -1,0 +1,454 @@
+// quantize.hip -- NVFP4 quantisers for gfx950: tensor amax, 1x16 and 16x16
+// block quantisation (RNE or stochastic rounding), and the random-Hadamard
+// transposing quantiser for weight-gradient operands.
+//
+// Recipe: "Pretraining Large Language Models with NVFP4" (gist.science
+// summary), Technische Zusammenfassung 2.A (16-element blocks, E4M3 block
+// scale, FP32 tensor scale), 2.B.2 (16x16 random Hadamard transform on the
+// weight-gradient inputs), 2.B.3 (16x16 blocks for weights), 2.B.4 (stochastic
+// rounding for gradients, RNE otherwise).
+//
+// Every quantiser is two streaming passes over the bf16 input: a tensor-amax
+// reduction (one atomic max per workgroup on the fp32 bit pattern, which
+// orders like the value for non-negative floats) and an encode pass that
+// reads the amax back from device memory.  Both are HBM-bound streams.
+#include "internal.hpp"
+#include "nvfp4_device.hpp"
+
+namespace nvfp4 {
+
+// ---------------------------------------------------------------------------
+// amax
+// ---------------------------------------------------------------------------
+
+__global__ void k_zero_u32(uint32_t* p) { *p = 0u; }
+
+// Empty tensors: only the tensor amax and encode scale are published.
+__global__ void k_publish(const float* __restrict__ amax_src, float* __restrict__ amax_out,
+                          float* __restrict__ s_enc_out)
+{
+    const float amax = *amax_src;
+    *amax_out = amax;
+    *s_enc_out = tensor_scale(amax);
+}
+
+// max |x| of a row-major bf16 matrix (rows x cols, leading dimension ld, all
+// multiples of 8 elements), as fp32 bits, atomically merged into *amax_bits.
+__global__ __launch_bounds__(256) void k_amax_rows(const uint16_t* __restrict__ x, int64_t rows,
+                                                   int64_t cols, int64_t ld,
+                                                   uint32_t* __restrict__ amax_bits)
+{
+    const int64_t vpr = cols >> 3;  // 16-byte vectors per row
+    const int64_t nvec = rows * vpr;
+    uint32_t m = 0u;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
+        int64_t r = v / vpr;
+        int64_t cv = v - r * vpr;
+        uint4 q = *reinterpret_cast<const uint4*>(x + r * ld + cv * 8);
+        m = max(m, max(max(bf16_absmax2(q.x), bf16_absmax2(q.y)),
+                       max(bf16_absmax2(q.z), bf16_absmax2(q.w))));
+    }
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t mm = max(max(red[0], red[1]), max(red[2], red[3]));
+        atomicMax(amax_bits, mm << 16);
+    }
+}
+
+// Contiguous fast path (ld == cols): a flat stream of 16-byte vectors.
+__global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, int64_t nvec,
+                                                   uint32_t* __restrict__ amax_bits)
+{
+    uint32_t m = 0u;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; v + stride < nvec; v += 2 * stride) {
+        uint4 q0 = x[v], q1 = x[v + stride];
+        m = max(m, max(max(bf16_absmax2(q0.x), bf16_absmax2(q0.y)),
+                       max(bf16_absmax2(q0.z), bf16_absmax2(q0.w))));
+        m = max(m, max(max(bf16_absmax2(q1.x), bf16_absmax2(q1.y)),
+                       max(bf16_absmax2(q1.z), bf16_absmax2(q1.w))));
+    }
+    if (v < nvec) {
+        uint4 q0 = x[v];
+        m = max(m, max(max(bf16_absmax2(q0.x), bf16_absmax2(q0.y)),
+                       max(bf16_absmax2(q0.z), bf16_absmax2(q0.w))));
+    }
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t mm = max(max(red[0], red[1]), max(red[2], red[3]));
+        atomicMax(amax_bits, mm << 16);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Encode helpers
+// ---------------------------------------------------------------------------
+
+// 16 bf16 values (two 16-byte vectors) -> fp32
+__device__ __forceinline__ void unpack16(const uint4& a, const uint4& b, float (&v)[16])
+{
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        v[2 * i] = bf16_lo(w[i]);
+        v[2 * i + 1] = bf16_hi(w[i]);
+    }
+}
+
+__device__ __forceinline__ float absmax16(const float (&v)[16])
+{
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(v[i]));
+    return m;
+}
+
+// 16 values times f, RNE-encoded into 8 packed bytes.
+__device__ __forceinline__ uint2 encode16_rne(const float (&v)[16], float f)
+{
+    uint32_t lo = 0u, hi = 0u;
+    lo = e2m1_rne_pk<0>(lo, v[0] * f, v[1] * f);
+    lo = e2m1_rne_pk<1>(lo, v[2] * f, v[3] * f);
+    lo = e2m1_rne_pk<2>(lo, v[4] * f, v[5] * f);
+    lo = e2m1_rne_pk<3>(lo, v[6] * f, v[7] * f);
+    hi = e2m1_rne_pk<0>(hi, v[8] * f, v[9] * f);
+    hi = e2m1_rne_pk<1>(hi, v[10] * f, v[11] * f);
+    hi = e2m1_rne_pk<2>(hi, v[12] * f, v[13] * f);
+    hi = e2m1_rne_pk<3>(hi, v[14] * f, v[15] * f);
+    return make_uint2(lo, hi);
+}
+
+// 16 values times f, stochastically rounded with the draws of elements
+// 8*g8 .. 8*g8+15 (two Philox blocks), into 8 packed bytes.
+__device__ __forceinline__ uint2 encode16_sr(const float (&v)[16], float f, uint64_t seed,
+                                             uint64_t g8)
+{
+    Draws8 d0 = sr_draws8(seed, g8);
+    Draws8 d1 = sr_draws8(seed, g8 + 1);
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) lo |= e2m1_sr(v[i] * f, d0.get(i)) << (4 * i);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) hi |= e2m1_sr(v[8 + i] * f, d1.get(i)) << (4 * i);
+    return make_uint2(lo, hi);
+}
+
+// ---------------------------------------------------------------------------
+// 1x16 quantiser: one thread per 16-element block.
+// ---------------------------------------------------------------------------
+
+template <bool kSR>
+__global__ __launch_bounds__(256) void k_quant_1x16(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
+    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    float* __restrict__ amax_out, float* __restrict__ s_enc_out)
+{
+    const int64_t nb = cols >> 4;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const float amax = *amax_src;
+    const float s_enc = tensor_scale(amax);
+    if (t == 0) {
+        *amax_out = amax;
+        *s_enc_out = s_enc;
+    }
+    if (t >= rows * nb) return;
+    const int64_t r = t / nb;
+    const int64_t b = t - r * nb;
+    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 16);
+    float v[16];
+    unpack16(src[0], src[1], v);
+    const uint32_t sb = block_scale(absmax16(v), s_enc);
+    const float f = block_factor(sb, s_enc);
+    uint2 pk;
+    if constexpr (kSR)
+        pk = encode16_sr(v, f, seed, (uint64_t)(r * cols + b * 16) >> 3);
+    else
+        pk = encode16_rne(v, f);
+    *reinterpret_cast<uint2*>(codes + r * ld_codes + b * 8) = pk;
+    scales[r * ld_scales + b] = (uint8_t)sb;
+}
+
+// ---------------------------------------------------------------------------
+// 16x16 quantiser (weights): a workgroup covers one 16-row strip and 64 tile
+// columns; lane l of wave w holds rows 4w..4w+3 of tile column l.
+// ---------------------------------------------------------------------------
+
+template <bool kSR>
+__global__ __launch_bounds__(256) void k_quant_16x16(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
+    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    uint8_t* __restrict__ codes_t, int64_t ld_codes_t, uint8_t* __restrict__ scales_t,
+    int64_t ld_scales_t, float* __restrict__ amax_out, float* __restrict__ s_enc_out)
+{
+    __shared__ float red[4][64];
+    __shared__ uint8_t tcodes[64][16][17];  // [tile col][row i][col j], padded
+
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t nb = cols >> 4;
+    const int64_t tr = blockIdx.y;
+    const int64_t tc = (int64_t)blockIdx.x * 64 + lane;
+    const bool valid = tc < nb;
+    const float amax = *amax_src;
+    const float s_enc = tensor_scale(amax);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        *amax_out = amax;
+        *s_enc_out = s_enc;
+    }
+
+    float v[4][16];
+    float m = 0.0f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = tr * 16 + wave * 4 + i;
+        if (valid) {
+            const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + tc * 16);
+            unpack16(src[0], src[1], v[i]);
+        } else {
+#pragma unroll
+            for (int j = 0; j < 16; ++j) v[i][j] = 0.0f;
+        }
+        m = __builtin_fmaxf(m, absmax16(v[i]));
+    }
+    red[wave][lane] = m;
+    __syncthreads();
+    const float tile_amax =
+        __builtin_fmaxf(__builtin_fmaxf(red[0][lane], red[1][lane]),
+                        __builtin_fmaxf(red[2][lane], red[3][lane]));
+    const uint32_t sb = block_scale(tile_amax, s_enc);
+    const float f = block_factor(sb, s_enc);
+
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int64_t r = tr * 16 + wave * 4 + i;
+        uint2 pk;
+        if constexpr (kSR)
+            pk = encode16_sr(v[i], f, seed, (uint64_t)(r * cols + tc * 16) >> 3);
+        else
+            pk = encode16_rne(v[i], f);
+        if (valid) *reinterpret_cast<uint2*>(codes + r * ld_codes + tc * 8) = pk;
+        if (codes_t) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                uint32_t w = (j < 4 ? pk.x : pk.y) >> (8 * (j & 3));
+                tcodes[lane][wave * 4 + i][2 * j] = (uint8_t)(w & 15u);
+                tcodes[lane][wave * 4 + i][2 * j + 1] = (uint8_t)((w >> 4) & 15u);
+            }
+        }
+    }
+    if (valid && wave == 0) {
+        scales[tr * ld_scales + tc] = (uint8_t)sb;
+        if (scales_t) scales_t[tc * ld_scales_t + tr] = (uint8_t)sb;
+    }
+    if (codes_t == nullptr) return;
+    __syncthreads();
+    // transposed codes: row k = 16*tc + j of W^T holds W[16*tr .. 16*tr+15, k]
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = it * 256 + threadIdx.x;  // 64 tile columns x 16 columns j
+        const int tcl = idx >> 4, j = idx & 15;
+        const int64_t tcg = (int64_t)blockIdx.x * 64 + tcl;
+        if (tcg >= nb) continue;
+        uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lo |= (uint32_t)tcodes[tcl][i][j] << (4 * i);
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hi |= (uint32_t)tcodes[tcl][8 + i][j] << (4 * i);
+        *reinterpret_cast<uint2*>(codes_t + (tcg * 16 + j) * ld_codes_t + tr * 8) = make_uint2(lo, hi);
+    }
+}
+
+// ---------------------------------------------------------------------------
+// RHT + transpose + 1x16 quantiser (weight-gradient operands).
+// A workgroup covers 256 tokens x 64 channels; thread t takes channels
+// 4*(t%16) .. +3 of the tile and the 16-token chunk t/16.
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ void load_rht_chunk(const uint16_t* __restrict__ x, int64_t ld,
+                                               int64_t tok0, int64_t ch0, float (&v)[4][16])
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        uint2 q = *reinterpret_cast<const uint2*>(x + (tok0 + i) * ld + ch0);
+        v[0][i] = bf16_lo(q.x);
+        v[1][i] = bf16_hi(q.x);
+        v[2][i] = bf16_lo(q.y);
+        v[3][i] = bf16_hi(q.y);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x, int64_t tokens,
+                                                  int64_t channels, int64_t ld, uint32_t mask,
+                                                  uint32_t* __restrict__ amax_bits)
+{
+    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int64_t ch0 = (int64_t)blockIdx.x * 64 + cg * 4;
+    const int64_t tok0 = (int64_t)blockIdx.y * 256 + j * 16;
+    uint32_t m = 0u;
+    if (ch0 < channels && tok0 < tokens) {
+        float v[4][16];
+        load_rht_chunk(x, ld, tok0, ch0, v);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            rht16(v[c], mask);
+            m = max(m, __float_as_uint(absmax16(v[c])));
+        }
+    }
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) atomicMax(amax_bits, max(max(red[0], red[1]), max(red[2], red[3])));
+}
+
+template <bool kSR>
+__global__ __launch_bounds__(256) void k_rht_quant(
+    const uint16_t* __restrict__ x, int64_t tokens, int64_t channels, int64_t ld, uint32_t mask,
+    const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
+    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    float* __restrict__ amax_out, float* __restrict__ s_enc_out)
+{
+    __shared__ uint2 scodes[64][17];    // [channel][chunk], padded
+    __shared__ uint8_t sscale[64][16];  // [channel][chunk]
+
+    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int64_t chb = (int64_t)blockIdx.x * 64, tokb = (int64_t)blockIdx.y * 256;
+    const int64_t ch0 = chb + cg * 4;
+    const int64_t tok0 = tokb + j * 16;
+    const float amax = *amax_src;
+    const float s_enc = tensor_scale(amax);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        *amax_out = amax;
+        *s_enc_out = s_enc;
+    }
+    if (ch0 < channels && tok0 < tokens) {
+        float v[4][16];
+        load_rht_chunk(x, ld, tok0, ch0, v);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            rht16(v[c], mask);
+            const uint32_t sb = block_scale(absmax16(v[c]), s_enc);
+            const float f = block_factor(sb, s_enc);
+            uint2 pk;
+            if constexpr (kSR)
+                pk = encode16_sr(v[c], f, seed, (uint64_t)((ch0 + c) * tokens + tok0) >> 3);
+            else
+                pk = encode16_rne(v[c], f);
+            scodes[cg * 4 + c][j] = pk;
+            sscale[cg * 4 + c][j] = (uint8_t)sb;
+        }
+    }
+    __syncthreads();
+    // 64 channel rows x 16 chunks of 8 code bytes; 16 consecutive threads
+    // write one row's 128 contiguous bytes.
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+        const int idx = it * 256 + threadIdx.x;
+        const int row = idx >> 4, q = idx & 15;
+        const int64_t ch = chb + row, tk = tokb + q * 16;
+        if (ch < channels && tk < tokens) {
+            *reinterpret_cast<uint2*>(codes + ch * ld_codes + (tk >> 1)) = scodes[row][q];
+            scales[ch * ld_scales + (tk >> 4)] = sscale[row][q];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+static int grid_for(int64_t work, int64_t per_block, int64_t cap)
+{
+    int64_t g = (work + per_block - 1) / per_block;
+    if (g < 1) g = 1;
+    return (int)(g < cap ? g : cap);
+}
+
+void launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
+                      hipStream_t s)
+{
+    uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, bits);
+    const int64_t nvec = rows * (cols >> 3);
+    if (nvec == 0) return;
+    if (ld == cols) {
+        hipLaunchKernelGGL(k_amax_flat, dim3(grid_for(nvec, 512, 4096)), dim3(256), 0, s,
+                           reinterpret_cast<const uint4*>(x), nvec, bits);
+    } else {
+        hipLaunchKernelGGL(k_amax_rows, dim3(grid_for(nvec, 256, 4096)), dim3(256), 0, s, x, rows,
+                           cols, ld, bits);
+    }
+}
+
+void launch_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int block,
+                  int rounding, uint64_t seed, const float* amax_src, const QOut& o, hipStream_t s)
+{
+    const bool sr = rounding == 1;
+    if (rows == 0 || cols == 0) {
+        hipLaunchKernelGGL(k_publish, dim3(1), dim3(1), 0, s, amax_src, o.amax, o.s_enc);
+        return;
+    }
+    if (block == 0) {
+        const int64_t work = rows * (cols >> 4);
+        dim3 g(grid_for(work, 256, INT32_MAX));
+        if (sr)
+            hipLaunchKernelGGL(k_quant_1x16<true>, g, dim3(256), 0, s, x, rows, cols, ld, amax_src,
+                               seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc);
+        else
+            hipLaunchKernelGGL(k_quant_1x16<false>, g, dim3(256), 0, s, x, rows, cols, ld, amax_src,
+                               seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc);
+    } else {
+        dim3 g((unsigned)(((cols >> 4) + 63) / 64), (unsigned)(rows >> 4));
+        if (sr)
+            hipLaunchKernelGGL(k_quant_16x16<true>, g, dim3(256), 0, s, x, rows, cols, ld,
+                               amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales,
+                               o.codes_t, o.ld_codes_t, o.scales_t, o.ld_scales_t, o.amax, o.s_enc);
+        else
+            hipLaunchKernelGGL(k_quant_16x16<false>, g, dim3(256), 0, s, x, rows, cols, ld,
+                               amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales,
+                               o.codes_t, o.ld_codes_t, o.scales_t, o.ld_scales_t, o.amax, o.s_enc);
+    }
+}
+
+void launch_rht_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
+                     uint32_t mask, float* amax, hipStream_t s)
+{
+    uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, bits);
+    if (tokens == 0 || channels == 0) return;
+    dim3 g((unsigned)((channels + 63) / 64), (unsigned)((tokens + 255) / 256));
+    hipLaunchKernelGGL(k_rht_amax, g, dim3(256), 0, s, x, tokens, channels, ld, mask, bits);
+}
+
+void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
+                      uint32_t mask, int rounding, uint64_t seed, const float* amax_src,
+                      const QOut& o, hipStream_t s)
+{
+    if (tokens == 0 || channels == 0) {
+        hipLaunchKernelGGL(k_publish, dim3(1), dim3(1), 0, s, amax_src, o.amax, o.s_enc);
+        return;
+    }
+    dim3 g((unsigned)((channels + 63) / 64), (unsigned)((tokens + 255) / 256));
+    if (rounding == 1)
+        hipLaunchKernelGGL(k_rht_quant<true>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
+                           amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax,
+                           o.s_enc);
+    else
+        hipLaunchKernelGGL(k_rht_quant<false>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
+                           amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax,
+                           o.s_enc);
+}
+
+}  // namespace nvfp4

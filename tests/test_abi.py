@@ -1,0 +1,129 @@
+"""The C-ABI library loads and exports every function include/nvfp4.h declares;
+host-side argument validation rejects bad calls before anything is enqueued.
+CPU only: no compute call is made."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "nvfp4.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from quantize_precision_gemm_amd import lib_path, load_library
+    if not os.path.exists(lib_path()):
+        from quantize_precision_gemm_amd import build as hip_build
+        hip_build.build()
+    return load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(nvfp4_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    for f in ["nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm", "nvfp4_rht_sign_mask",
+              "nvfp4_status_string"]:
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    from quantize_precision_gemm_amd import lib_path
+    out = subprocess.run(["nm", "-D", "--defined-only", lib_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    for name in declared_functions():
+        assert name in exported, name
+        assert hasattr(lib, name)
+
+
+def test_status_strings(lib):
+    for st, s in [(0, b"ok"), (-1, b"null pointer"), (-2, b"invalid shape"),
+                  (-3, b"misaligned pointer or leading dimension"), (-4, b"unknown mode"),
+                  (-5, b"operands inconsistent with the pass"), (-6, b"kernel launch failed")]:
+        assert lib.nvfp4_status_string(st) == s
+
+
+def test_sign_mask_matches_oracle(lib):
+    import oracle
+    for seed in [0, 1, 1000, 2 ** 63 + 7]:
+        assert lib.nvfp4_rht_sign_mask(seed) == oracle.rht_sign_mask(seed)
+
+
+def _desc(**kw):
+    from quantize_precision_gemm_amd import _Desc
+    d = _Desc()
+    for k, v in kw.items():
+        setattr(d, k, v)
+    return d
+
+
+FAKE = 0x10000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("args,status", [
+    # x, rows, cols, ld_x, block, rounding
+    ((FAKE, 16, 17, 32, 0, 0), -2),          # cols not a multiple of 16
+    ((FAKE, 8, 32, 32, 1, 0), -2),           # 16x16 needs rows % 16 == 0
+    ((FAKE, 16, 32, 32, 2, 0), -4),          # unknown block
+    ((FAKE, 16, 32, 32, 0, 5), -4),          # unknown rounding
+    ((None, 16, 32, 32, 0, 0), -1),          # null input
+    ((FAKE, 16, 32, 16, 0, 0), -2),          # ld_x < cols
+    ((FAKE + 2, 16, 32, 32, 0, 0), -3),      # misaligned input
+    ((FAKE, 16, 32, 36, 0, 0), -3),          # ld_x not a multiple of 8
+    ((FAKE, -1, 32, 32, 0, 0), -2),          # negative rows
+])
+def test_quantize_validation(lib, args, status):
+    x, rows, cols, ld, block, rnd = args
+    d = _desc(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, ld_codes=16, ld_scales=4)
+    st = lib.nvfp4_quantize(x, rows, cols, ld, block, rnd, 0, None, ctypes.byref(d), None)
+    assert st == status
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("codes", None, -1), ("amax", None, -1), ("s_enc", None, -1),
+    ("codes", FAKE + 8, -3), ("ld_codes", 8, -3), ("ld_scales", 2, -3), ("ld_codes", 0, -2),
+    ("codes_t", FAKE, -4),   # transposed copy only for 16x16 blocks
+])
+def test_quantize_out_validation(lib, field, value, status):
+    d = _desc(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, ld_codes=16, ld_scales=4)
+    setattr(d, field, value)
+    st = lib.nvfp4_quantize(FAKE, 16, 32, 32, 0, 0, 0, None, ctypes.byref(d), None)
+    assert st == status
+
+
+def test_rht_validation(lib):
+    d = _desc(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, ld_codes=16, ld_scales=4)
+    assert lib.nvfp4_rht_quantize(FAKE, 24, 16, 16, 1, 0, 0, None, ctypes.byref(d), None) == -2
+    assert lib.nvfp4_rht_quantize(FAKE, 32, 12, 16, 1, 0, 0, None, ctypes.byref(d), None) == -2
+    assert lib.nvfp4_rht_quantize(FAKE, 32, 16, 16, 1, 3, 0, None, ctypes.byref(d), None) == -4
+    d.ld_codes = 0
+    assert lib.nvfp4_rht_quantize(FAKE, 32, 16, 16, 1, 0, 0, None, ctypes.byref(d), None) == -2
+
+
+def test_gemm_validation(lib):
+    def op(rows, cols, block=0, **kw):
+        base = dict(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, rows=rows, cols=cols,
+                    ld_codes=max(16, ((cols + 31) // 32) * 16), ld_scales=max(4, cols // 16),
+                    block=block)
+        base.update(kw)
+        return _desc(**base)
+
+    a, w = op(32, 64), op(48, 64, 1)
+    assert lib.nvfp4_gemm(7, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 0, None) == -4
+    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 3, None) == -4
+    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(op(48, 32, 1)), FAKE, 64, 0, None) == -5
+    assert lib.nvfp4_gemm(0, ctypes.byref(w), ctypes.byref(a), FAKE, 64, 0, None) == -5
+    assert lib.nvfp4_gemm(1, ctypes.byref(op(32, 48)), ctypes.byref(w), FAKE, 64, 0, None) == -1
+    assert lib.nvfp4_gemm(2, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 0, None) == -5
+    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE + 2, 64, 0, None) == -3
+    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 66, 0, None) == -3
+    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 16, 0, None) == -2
+    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(op(40, 64, 1)), FAKE, 64, 0, None) == -2

@@ -1,0 +1,130 @@
+"""GPU parity of the NVFP4 GEMM (fprop, dgrad, wgrad) against the fp64 oracle.
+
+Bar: relative Frobenius error <= 1e-5 on the kernel's fp32 output; the bf16
+output is bit-equal to round-to-nearest-even of that fp32 output.
+Passes: "Pretraining Large Language Models with NVFP4" (gist.science
+summary), Technische Zusammenfassung 2.B.2 (Fprop, Dgrad, Wgrad).
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import bf16_rne_bits, ensure_built, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def env():
+    import torch
+    ensure_built()
+    import oracle
+    import quantize_precision_gemm_amd as q
+    from quantize_precision_gemm_amd import workloads as wl
+    dev = torch.device("cuda:0")
+    return torch, oracle, q, wl, dev
+
+
+def _check_both_dtypes(torch, q, pass_, ga, gb, want):
+    y32 = q.nvfp4_gemm(pass_, ga, gb, torch.float32)
+    y16 = q.nvfp4_gemm(pass_, ga, gb, torch.bfloat16)
+    torch.cuda.synchronize()
+    g32 = y32.cpu().numpy()
+    err = rel_fro(g32, want)
+    assert err <= TOL, f"relative Frobenius error {err:.3e}"
+    b16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(b16, bf16_rne_bits(g32))
+    return g32
+
+
+# (M, K, N): several 256-tiles, ragged M/N, K tails (K % 128 != 0, K % 32 == 16)
+SHAPES = [(1, 16, 16), (16, 48, 32), (300, 336, 272), (257, 1040, 528), (512, 512, 768),
+          (64, 4112, 96)]
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_fprop(env, shape):
+    torch, oracle, q, wl, dev = env
+    M, K, N = shape
+    rng = np.random.default_rng(M + K + N)
+    x = wl.student_t_unit_var(rng, (M, K), 4)
+    w = wl.normal(rng, (N, K), 0.02)
+    print(f"fprop {shape}", flush=True)
+    gx = q.nvfp4_quantize(to_dev(x, dev), q.BLOCK_1X16, q.RNE)
+    gw = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, q.RNE, with_transpose=True)
+    want = oracle.gemm(oracle.FPROP, oracle.quantize(x), oracle.quantize(w, oracle.BLOCK_16X16))
+    _check_both_dtypes(torch, q, q.FPROP, gx, gw, want)
+    # a 1x16-quantised B operand takes the same path with per-row scales
+    gw1 = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_1X16, q.RNE)
+    want1 = oracle.gemm(oracle.FPROP, oracle.quantize(x), oracle.quantize(w))
+    _check_both_dtypes(torch, q, q.FPROP, gx, gw1, want1)
+
+
+@pytest.mark.parametrize("shape", SHAPES)
+def test_dgrad(env, shape):
+    torch, oracle, q, wl, dev = env
+    M, K, N = shape  # dX (M x K) = dY (M x N) W (N x K)
+    rng = np.random.default_rng(3 * M + K + N)
+    dy = wl.lognormal_rows(rng, (M, N))
+    w = wl.normal(rng, (N, K), 0.02)
+    print(f"dgrad {shape}", flush=True)
+    gdy = q.nvfp4_quantize(to_dev(dy, dev), q.BLOCK_1X16, q.SR, 17)
+    gw = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, q.RNE, with_transpose=True)
+    want = oracle.gemm(oracle.DGRAD, oracle.quantize(dy, oracle.BLOCK_1X16, oracle.SR, 17),
+                       oracle.quantize(w, oracle.BLOCK_16X16))
+    _check_both_dtypes(torch, q, q.DGRAD, gdy, gw, want)
+
+
+@pytest.mark.parametrize("shape", [(16, 16, 16), (48, 40, 24), (272, 264, 200), (1040, 512, 264)])
+def test_wgrad(env, shape):
+    torch, oracle, q, wl, dev = env
+    M, K, N = shape  # dW (N x K) = sum over M tokens
+    rng = np.random.default_rng(5 * M + K + N)
+    dy = wl.lognormal_rows(rng, (M, N))
+    x = wl.student_t_unit_var(rng, (M, K), 4)
+    mask = q.nvfp4_rht_sign_mask(M)
+    print(f"wgrad {shape}", flush=True)
+    gdyt = q.nvfp4_rht_quantize(to_dev(dy, dev), mask, q.SR, 23)
+    gxt = q.nvfp4_rht_quantize(to_dev(x, dev), mask, q.RNE)
+    want = oracle.gemm(oracle.WGRAD, oracle.rht_quantize(dy, mask, oracle.SR, 23),
+                       oracle.rht_quantize(x, mask, oracle.RNE))
+    _check_both_dtypes(torch, q, q.WGRAD, gdyt, gxt, want)
+
+
+def test_wgrad_rht_cancels(env):
+    # With the same sign mask on both operands the transform cancels in the
+    # product: the NVFP4 wgrad stays close to the unquantised dY^T X.
+    torch, oracle, q, wl, dev = env
+    rng = np.random.default_rng(9)
+    M, K, N = 1024, 64, 96
+    dy = wl.normal(rng, (M, N), 1.0)
+    x = wl.normal(rng, (M, K), 1.0)
+    mask = q.nvfp4_rht_sign_mask(4)
+    gdyt = q.nvfp4_rht_quantize(to_dev(dy, dev), mask, q.SR, 1)
+    gxt = q.nvfp4_rht_quantize(to_dev(x, dev), mask, q.RNE)
+    dw = q.nvfp4_gemm(q.WGRAD, gdyt, gxt, torch.float32)
+    torch.cuda.synchronize()
+    ref = wl.bf16_bits_to_f32(dy).astype(np.float64).T @ wl.bf16_bits_to_f32(x).astype(np.float64)
+    assert rel_fro(dw.cpu().numpy(), ref) < 0.2  # 4-bit quantisation noise, not a parity bar
+
+
+def test_empty_contraction_and_determinism(env):
+    torch, oracle, q, wl, dev = env
+    a = q.alloc_nvfp4(32, 0)
+    b = q.alloc_nvfp4(48, 0)
+    a.amax.fill_(0)
+    a.s_enc.fill_(1)
+    b.s_enc.fill_(1)
+    y = q.nvfp4_gemm(q.FPROP, a, b, torch.float32)
+    torch.cuda.synchronize()
+    assert (y == 0).all()
+    rng = np.random.default_rng(1)
+    x = to_dev(wl.normal(rng, (700, 640), 1.0), dev)
+    w = to_dev(wl.normal(rng, (528, 640), 0.02), dev)
+    gx = q.nvfp4_quantize(x)
+    gw = q.nvfp4_quantize(w, q.BLOCK_16X16, q.RNE, with_transpose=True)
+    y1 = q.nvfp4_gemm(q.FPROP, gx, gw, torch.float32)
+    y2 = q.nvfp4_gemm(q.FPROP, gx, gw, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
