@@ -1,0 +1,129 @@
+"""Parity at the full 12B-layer sizes, in the launch configuration bench.py times.
+
+Workload: tokens M = 8192, in K = 5120, out N = 20480 (the bench step), plus
+the 256^3 fprop with outliers.  Every quantised tensor is compared with the
+oracle in full, bit for bit; GEMMs are compared on sampled output rows
+(fp32 output, relative Frobenius <= 1e-5), and the bf16 outputs the bench
+produces are checked to be round-to-nearest-even of the fp32 result of the
+same kernel over the whole matrix.
+"""
+import numpy as np
+import pytest
+
+from tests.gpu_util import assert_same_quant, ensure_built, rel_fro, to_dev
+
+pytestmark = pytest.mark.gpu
+
+TOL = 1e-5
+
+
+@pytest.fixture(scope="module")
+def full():
+    import torch
+    ensure_built()
+    import oracle
+    import quantize_precision_gemm_amd as q
+    import bench
+
+    dev = torch.device("cuda:0")
+    print("generating full-size inputs", flush=True)
+    data, t = bench.make_inputs(dev)
+    step = bench.Step(q, torch, dev, t["X"], t["W"], t["dY"])
+    print("running one bench step", flush=True)
+    step.run()
+    torch.cuda.synchronize()
+    return torch, oracle, q, bench, data, step
+
+
+def _rows(n, k=40, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1], rng.choice(n, k, replace=False)]))
+
+
+def test_full_quantisers(full):
+    torch, oracle, q, bench, data, step = full
+    print("oracle X", flush=True)
+    assert_same_quant(step.gx, oracle.quantize(data["X"]), "X 8192x5120 1x16 RNE")
+    print("oracle W", flush=True)
+    ow = oracle.quantize(data["W"], oracle.BLOCK_16X16)
+    assert_same_quant(step.gw, ow, "W 20480x5120 16x16 RNE")
+    # the transposed copy used by dgrad is the nibble transpose of W's codes
+    ct = oracle.unpack_codes(step.gw.codes_t_host(), bench.N)
+    np.testing.assert_array_equal(ct, oracle.unpack_codes(ow.codes, bench.K).T)
+    np.testing.assert_array_equal(step.gw.scales_t_host(), ow.scales.T)
+
+
+def test_full_sr_quantiser(full):
+    torch, oracle, q, bench, data, step = full
+    print("oracle dY SR", flush=True)
+    assert_same_quant(step.gdy, oracle.quantize(data["dY"], oracle.BLOCK_1X16, oracle.SR,
+                                                bench.SEED + 100), "dY 8192x20480 1x16 SR")
+
+
+def test_full_rht_quantisers(full):
+    torch, oracle, q, bench, data, step = full
+    print("oracle RHT", flush=True)
+    assert step.mask == oracle.rht_sign_mask(bench.SEED + 1000)
+    assert_same_quant(step.gdyt, oracle.rht_quantize(data["dY"], step.mask, oracle.SR,
+                                                     bench.SEED + 101), "RHT(dY)^T SR")
+    assert_same_quant(step.gxt, oracle.rht_quantize(data["X"], step.mask, oracle.RNE),
+                      "RHT(X)^T RNE")
+
+
+def _sampled_gemm(torch, oracle, q, pass_, ga, gb, oa, ob, rows):
+    y32 = q.nvfp4_gemm(pass_, ga, gb, torch.float32)
+    torch.cuda.synchronize()
+    want = oracle.gemm(pass_, oa, ob, rows=rows)
+    got = y32[torch.as_tensor(rows, device=y32.device)].double().cpu().numpy()
+    err = rel_fro(got, want)
+    assert err <= TOL, f"pass {pass_}: relative Frobenius error {err:.3e} on {len(rows)} rows"
+    return y32
+
+
+def test_full_fprop(full):
+    torch, oracle, q, bench, data, step = full
+    print("fprop sampled rows", flush=True)
+    ox = oracle.quantize(data["X"])
+    ow = oracle.quantize(data["W"], oracle.BLOCK_16X16)
+    y32 = _sampled_gemm(torch, oracle, q, q.FPROP, step.gx, step.gw, ox, ow, _rows(bench.M))
+    assert torch.equal(y32.to(torch.bfloat16), step.y)
+
+
+def test_full_dgrad(full):
+    torch, oracle, q, bench, data, step = full
+    print("dgrad sampled rows", flush=True)
+    ody = oracle.quantize(data["dY"], oracle.BLOCK_1X16, oracle.SR, bench.SEED + 100)
+    ow = oracle.quantize(data["W"], oracle.BLOCK_16X16)
+    y32 = _sampled_gemm(torch, oracle, q, q.DGRAD, step.gdy, step.gw, ody, ow, _rows(bench.M, seed=1))
+    assert torch.equal(y32.to(torch.bfloat16), step.dx)
+
+
+def test_full_wgrad(full):
+    torch, oracle, q, bench, data, step = full
+    print("wgrad sampled rows", flush=True)
+    oa = oracle.rht_quantize(data["dY"], step.mask, oracle.SR, bench.SEED + 101)
+    ob = oracle.rht_quantize(data["X"], step.mask, oracle.RNE)
+    y32 = _sampled_gemm(torch, oracle, q, q.WGRAD, step.gdyt, step.gxt, oa, ob, _rows(bench.N, seed=2))
+    assert torch.equal(y32, step.dw)
+
+
+def test_small_fprop_with_outliers():
+    # 256^3 fprop: X ~ N(0,1) with 0.1 % x50 outliers, W ~ N(0, 0.02), seed 0, bf16 out
+    import torch
+    ensure_built()
+    import oracle
+    import quantize_precision_gemm_amd as q
+    from quantize_precision_gemm_amd import workloads as wl
+
+    dev = torch.device("cuda:0")
+    X, W = wl.small_fprop(0)
+    gx = q.nvfp4_quantize(to_dev(X, dev), q.BLOCK_1X16, q.RNE)
+    gw = q.nvfp4_quantize(to_dev(W, dev), q.BLOCK_16X16, q.RNE, with_transpose=True)
+    y32 = q.nvfp4_gemm(q.FPROP, gx, gw, torch.float32)
+    y16 = q.nvfp4_gemm(q.FPROP, gx, gw, torch.bfloat16)
+    torch.cuda.synchronize()
+    ox, ow = oracle.quantize(X), oracle.quantize(W, oracle.BLOCK_16X16)
+    assert_same_quant(gx, ox, "X 256x256")
+    assert_same_quant(gw, ow, "W 256x256")
+    assert rel_fro(y32.cpu().numpy(), oracle.gemm(oracle.FPROP, ox, ow)) <= TOL
+    assert torch.equal(y32.to(torch.bfloat16), y16)
