@@ -126,7 +126,7 @@ def quant_bytes():
             "rht_dY": one(e_dy), "rht_X": one(e_x)}
 
 
-def cpu_baseline(data, tokens=1024):
+def cpu_baseline(data, tokens=M):
     """The oracle on a token slice of the step; W's quantisation, which does not
     scale with tokens, is timed in full and counted at tokens/M of its time."""
     import numpy as np

@@ -3,7 +3,7 @@
 // enqueued; a failed check returns a negative status and launches nothing.
 #include <stdint.h>
 
-#include "../../include/nvfp4.h"
+#include "nvfp4.h"
 #include "internal.hpp"
 
 namespace {

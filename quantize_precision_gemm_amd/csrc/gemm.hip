@@ -16,16 +16,21 @@
 //
 // Both operands are "rows x K" with K contiguous, so one kernel serves all
 // passes (the dgrad weight operand is the transposed 16x16-block copy written
-// by the quantiser).  A workgroup of 4 waves computes a 256x256 tile; each
-// wave owns 128x128 (4x4 MFMA 32x32x16 tiles, 256 fp32 accumulators per lane)
-// and decodes its own fragments straight from global memory into registers,
-// one 128-wide K step ahead of the MFMAs.  No LDS is used.
+// by the quantiser).  A workgroup of 4 waves computes a 256x256 tile in K
+// steps of 64.  Per step every thread decodes one row of A and one row of B
+// (32 code bytes, 4 scales each) into an fp16 tile in LDS, so each element is
+// decoded once per workgroup; each wave then runs 4x4 MFMA 32x32x16 tiles
+// (its 128x128 quarter, 256 fp32 accumulators in AGPRs) over the tile.  Two
+// LDS stages alternate: while the MFMAs consume one, the next step's codes
+// (loaded from global memory one step earlier) are decoded into the other,
+// and the global loads two steps ahead are in flight.  The epilogue stages
+// 32 output rows per wave through LDS and stores 16-byte row segments.
 //
 // Lane layout of v_mfma_f32_32x32x16_f16: lane l supplies row (A) or column
-// (B) l % 32 and 8 consecutive k of group l / 32; accumulator j of lane l is
-// row (j/4)*8 + (l/32)*4 + j%4, column l % 32.  Within a 128-wide K step the
-// lane group g = l / 32 owns k in [64g, 64g + 64): the same permutation of k
-// is used for A and B, so the sum is unchanged.
+// (B) l % 32 and the 8 consecutive k 8*(l/32) .. +7 of the 16-wide step;
+// accumulator j of lane l is row (j/4)*8 + (l/32)*4 + j%4, column l % 32.
+#include <utility>
+
 #include "internal.hpp"
 #include "nvfp4_device.hpp"
 
@@ -33,100 +38,61 @@ namespace nvfp4 {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kKT = 128;
-constexpr int kTM = 4, kTN = 4;  // 32x32 MFMA tiles per wave (128 x 128)
+constexpr int kBM = 256, kBN = 256, kKS = 64;  // workgroup tile and K step
+constexpr int kRowBytes = 144;                 // LDS row: 64 fp16 (128 B) + 16 B pad
+constexpr int kOpBytes = 256 * kRowBytes;      // one operand, one stage
 
-struct Raw {
-    uint4 c[4][2];  // per 32-row tile: 32 code bytes (64 k) of this lane's row
-    uint32_t s[4];  // per 32-row tile: 4 scale bytes (blocks 4g .. 4g+3 of the step)
+// This thread's row of A and of B for one K step: 32 code bytes (64 k) and
+// 4 scale bytes each.
+struct Stage {
+    uint4 ca0, ca1, cb0, cb1;
+    uint32_t sa, sb;
 };
 
-__device__ __forceinline__ void load_full(const uint8_t* __restrict__ codes,
-                                          const uint8_t* __restrict__ scales,
-                                          const int64_t (&oc)[4], const int64_t (&os)[4],
-                                          int64_t k0, int g, Raw& r)
+__device__ __forceinline__ void load_row(const uint8_t* __restrict__ codes,
+                                         const uint8_t* __restrict__ scales, int64_t oc,
+                                         int64_t os, int64_t k0, int64_t nblk, uint4& c0,
+                                         uint4& c1, uint32_t& s)
 {
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint4* p = reinterpret_cast<const uint4*>(codes + oc[t] + (k0 >> 1) + 32 * g);
-        r.c[t][0] = p[0];
-        r.c[t][1] = p[1];
-        r.s[t] = *reinterpret_cast<const uint32_t*>(scales + os[t] + (k0 >> 4) + 4 * g);
-    }
-}
-
-// Last, partial K step: 16-byte granules (two blocks) past the end read as
-// zero codes, and scales of blocks past the end read as zero, so their
-// products vanish.
-__device__ __forceinline__ void load_tail(const uint8_t* __restrict__ codes,
-                                          const uint8_t* __restrict__ scales,
-                                          const int64_t (&oc)[4], const int64_t (&os)[4],
-                                          int64_t k0, int g, int64_t nblk, Raw& r)
-{
-    const int64_t b0 = (k0 >> 4) + 4 * g;  // first block of this lane's range
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const uint4* p = reinterpret_cast<const uint4*>(codes + oc[t] + (k0 >> 1) + 32 * g);
-        r.c[t][0] = (b0 < nblk) ? p[0] : make_uint4(0, 0, 0, 0);
-        r.c[t][1] = (b0 + 2 < nblk) ? p[1] : make_uint4(0, 0, 0, 0);
-        uint32_t s = 0u;
+    const int64_t b0 = k0 >> 4;
+    const uint4* p = reinterpret_cast<const uint4*>(codes + oc + (k0 >> 1));
+    if (b0 + 4 <= nblk) {
+        c0 = p[0];
+        c1 = p[1];
+        s = *reinterpret_cast<const uint32_t*>(scales + os + b0);
+    } else {  // partial last step: missing blocks get zero codes and zero scales
+        c0 = (b0 < nblk) ? p[0] : make_uint4(0, 0, 0, 0);
+        c1 = (b0 + 2 < nblk) ? p[1] : make_uint4(0, 0, 0, 0);
+        s = 0u;
 #pragma unroll
         for (int j = 0; j < 4; ++j)
-            if (b0 + j < nblk) s |= (uint32_t)scales[os[t] + b0 + j] << (8 * j);
-        r.s[t] = s;
+            if (b0 + j < nblk) s |= (uint32_t)scales[os + b0 + j] << (8 * j);
     }
 }
 
-// Eight codes (one dword, k ascending from the low nibble) times the block
-// scale pair -> the MFMA fragment, exact in fp16.
-__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t ss)
+// Decode 64 codes (4 blocks) of one row to exact fp16 q * S and store them to
+// the row's 128 bytes in LDS.
+__device__ __forceinline__ void decode_row(const uint4& c0, const uint4& c1, uint32_t s,
+                                           uint8_t* __restrict__ dst)
 {
-    half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * ss;
-    half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * ss;
-    half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * ss;
-    half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * ss;
-    half8_t r;
-    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
-    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
-    return r;
-}
-
-// The four E4M3 scale bytes of a step as fp16 pairs {S_j, S_j}.
-__device__ __forceinline__ void scale_pairs(uint32_t s, half2_t (&ss)[4])
-{
-    half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false);
-    half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true);
-    ss[0] = __builtin_shufflevector(a, a, 0, 0);
-    ss[1] = __builtin_shufflevector(a, a, 1, 1);
-    ss[2] = __builtin_shufflevector(b, b, 0, 0);
-    ss[3] = __builtin_shufflevector(b, b, 1, 1);
-}
-
-__device__ __forceinline__ void compute_step(const Raw& ra, const Raw& rb, float16_t (&acc)[4][4])
-{
-    half2_t sa[4][4], sb[4][4];
+    const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, false);
+    const half2_t sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(s, 1.0f, true);
+    const half2_t ss[4] = {__builtin_shufflevector(sa, sa, 0, 0), __builtin_shufflevector(sa, sa, 1, 1),
+                           __builtin_shufflevector(sb, sb, 0, 0), __builtin_shufflevector(sb, sb, 1, 1)};
+    const uint32_t w[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        scale_pairs(ra.s[t], sa[t]);
-        scale_pairs(rb.s[t], sb[t]);
-    }
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {  // 8 sub-steps of 16 k (8 per lane group)
-        half8_t af[4], bf[4];
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint4& ca = ra.c[t][i >> 2];
-            const uint4& cb = rb.c[t][i >> 2];
-            const uint32_t wa = (i & 3) == 0 ? ca.x : (i & 3) == 1 ? ca.y : (i & 3) == 2 ? ca.z : ca.w;
-            const uint32_t wb = (i & 3) == 0 ? cb.x : (i & 3) == 1 ? cb.y : (i & 3) == 2 ? cb.z : cb.w;
-            af[t] = decode8(wa, sa[t][i >> 1]);
-            bf[t] = decode8(wb, sb[t][i >> 1]);
-        }
-#pragma unroll
-        for (int tm = 0; tm < 4; ++tm)
-#pragma unroll
-            for (int tn = 0; tn < 4; ++tn)
-                acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[tm], bf[tn], acc[tm][tn], 0, 0, 0);
+    for (int d = 0; d < 8; ++d) {  // dword d: elements 8d .. 8d+7, block d / 2
+        const half2_t S = ss[d >> 1];
+        half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d], 1.0f, 0) * S;
+        half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d], 1.0f, 1) * S;
+        half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d], 1.0f, 2) * S;
+        half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w[d], 1.0f, 3) * S;
+        uint4 v;
+        v.x = __builtin_bit_cast(uint32_t, p0);
+        v.y = __builtin_bit_cast(uint32_t, p1);
+        v.z = __builtin_bit_cast(uint32_t, p2);
+        v.w = __builtin_bit_cast(uint32_t, p3);
+        *reinterpret_cast<uint4*>(dst + 16 * d) = v;
     }
 }
 
@@ -139,6 +105,38 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 
 }  // namespace
 
+// One workgroup (4 waves) computes a 256 x 256 tile.  Per K step of 64:
+// every thread decodes one row of A and one row of B into the fp16 LDS
+// stage, so each element is decoded once per workgroup; each wave then runs
+// 4 x 4 MFMA 32x32x16 tiles (128 x 128) over the stage.  Two LDS stages
+// alternate; the global loads of step s+2 are issued before the MFMAs of
+// step s, and step s+1 (loaded one iteration earlier) is decoded after them.
+// Instruction-schedule hint for one K step (64 MFMAs per wave): the first
+// half of the MFMAs is interleaved with the LDS fragment reads only; the
+// second half also carries the decode of the next step (4 VALU per MFMA) and
+// its LDS writes, which gives the global loads feeding that decode as much
+// time as possible to land.
+template <int kM>
+__device__ __forceinline__ void interleave_slot()
+{
+    constexpr int sub = kM / 16;
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
+    if constexpr (kM < 32) {
+        if constexpr (sub < 3 && kM % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    } else {
+        __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
+        if constexpr (kM % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+        if constexpr (sub < 3 && kM % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+}
+
+template <int... kMs>
+__device__ __forceinline__ void interleave_step(std::integer_sequence<int, kMs...>)
+{
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // fragments of the first sub-step
+    (interleave_slot<kMs>(), ...);
+}
+
 template <bool kOutF32>
 __global__ __launch_bounds__(256, 1) void k_gemm_nt(
     const uint8_t* __restrict__ a_codes, int64_t a_ldc, const uint8_t* __restrict__ a_scales,
@@ -147,7 +145,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(
     int64_t b_lds, int b_shift, const float* __restrict__ b_senc, int64_t M, int64_t N,
     int64_t K, void* __restrict__ c, int64_t ldc)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kOpBytes];  // [stage][A/B]
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, lr = lane & 31;
 
     // Tile order: workgroups are dealt round-robin to the 8 XCDs; renumber so
@@ -165,21 +166,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(
     const int64_t tile_m = first_m + in_group % gsz;
     const int64_t tile_n = in_group / gsz;
 
-    const int64_t m0 = tile_m * kBM + (wave >> 1) * 128;
-    const int64_t n0 = tile_n * kBN + (wave & 1) * 128;
-
-    int64_t oca[4], osa[4], ocb[4], osb[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        int64_t ra = m0 + 32 * t + lr;
-        ra = ra < M ? ra : M - 1;
-        int64_t rb = n0 + 32 * t + lr;
-        rb = rb < N ? rb : N - 1;
-        oca[t] = ra * a_ldc;
-        osa[t] = (ra >> a_shift) * a_lds;
-        ocb[t] = rb * b_ldc;
-        osb[t] = (rb >> b_shift) * b_lds;
-    }
+    // rows this thread loads and decodes (clamped; the extra rows are never stored)
+    int64_t ra = tile_m * kBM + tid, rb = tile_n * kBN + tid;
+    ra = ra < M ? ra : M - 1;
+    rb = rb < N ? rb : N - 1;
+    const int64_t oca = ra * a_ldc, osa = (ra >> a_shift) * a_lds;
+    const int64_t ocb = rb * b_ldc, osb = (rb >> b_shift) * b_lds;
 
     float16_t acc[4][4];
 #pragma unroll
@@ -190,46 +182,146 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const int64_t nblk = K >> 4;
-    const int64_t nfull = K / kKT;
-    Raw ra, rb;
-    if (nfull > 0) {
-        load_full(a_codes, a_scales, oca, osa, 0, g, ra);
-        load_full(b_codes, b_scales, ocb, osb, 0, g, rb);
-    }
-    for (int64_t s = 0; s < nfull; ++s) {
-        Raw na, nb;
-        if (s + 1 < nfull) {
-            load_full(a_codes, a_scales, oca, osa, (s + 1) * kKT, g, na);
-            load_full(b_codes, b_scales, ocb, osb, (s + 1) * kKT, g, nb);
+    const int64_t nsteps = (K + kKS - 1) / kKS;
+    const int wm = wave >> 1, wn = wave & 1;
+    // fragment read offsets within a stage: row (32 t + lr) of the wave's
+    // 128-row slab, k = 16 i + 8 g
+    const int a_frag = (wm * 128 + lr) * kRowBytes + 16 * g;
+    const int b_frag = (wn * 128 + lr) * kRowBytes + 16 * g;
+
+    auto load = [&](int64_t step, Stage& st) {
+        const int64_t k0 = step * kKS;
+        load_row(a_codes, a_scales, oca, osa, k0, nblk, st.ca0, st.ca1, st.sa);
+        load_row(b_codes, b_scales, ocb, osb, k0, nblk, st.cb0, st.cb1, st.sb);
+    };
+    auto decode = [&](const Stage& st, int stage) {
+        decode_row(st.ca0, st.ca1, st.sa, &lds[stage][0][tid * kRowBytes]);
+        decode_row(st.cb0, st.cb1, st.sb, &lds[stage][1][tid * kRowBytes]);
+    };
+    auto compute = [&](int stage) {
+        const uint8_t* As = lds[stage][0];
+        const uint8_t* Bs = lds[stage][1];
+        half8_t af[2][4], bf[2][4];  // fragments of two sub-steps in flight
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            af[0][t] = *reinterpret_cast<const half8_t*>(As + a_frag + t * 32 * kRowBytes);
+            bf[0][t] = *reinterpret_cast<const half8_t*>(Bs + b_frag + t * 32 * kRowBytes);
         }
-        compute_step(ra, rb, acc);
-        ra = na;
-        rb = nb;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cur = i & 1, nxt = cur ^ 1;
+            if (i < 3) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t) {
+                    af[nxt][t] = *reinterpret_cast<const half8_t*>(As + a_frag + t * 32 * kRowBytes + 32 * (i + 1));
+                    bf[nxt][t] = *reinterpret_cast<const half8_t*>(Bs + b_frag + t * 32 * kRowBytes + 32 * (i + 1));
+                }
+            }
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 4; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][tm], bf[cur][tn], acc[tm][tn], 0, 0, 0);
+        }
+    };
+
+    // Main loop over full K steps (no partial-step code inside it).
+    const int64_t nfull = K / kKS;
+    auto load_full = [&](int64_t step, Stage& st) {
+        const int64_t k0 = step * kKS;
+        const uint4* pa = reinterpret_cast<const uint4*>(a_codes + oca + (k0 >> 1));
+        const uint4* pb = reinterpret_cast<const uint4*>(b_codes + ocb + (k0 >> 1));
+        st.ca0 = pa[0];
+        st.ca1 = pa[1];
+        st.cb0 = pb[0];
+        st.cb1 = pb[1];
+        st.sa = *reinterpret_cast<const uint32_t*>(a_scales + osa + (k0 >> 4));
+        st.sb = *reinterpret_cast<const uint32_t*>(b_scales + osb + (k0 >> 4));
+    };
+    Stage g0, g1;
+    if (nfull > 0) {
+        load_full(0, g0);
+        decode(g0, 0);
+        load_full(nfull > 1 ? 1 : 0, g1);
     }
-    if (nfull * kKT < K) {
-        load_tail(a_codes, a_scales, oca, osa, nfull * kKT, g, nblk, ra);
-        load_tail(b_codes, b_scales, ocb, osb, nfull * kKT, g, nblk, rb);
-        compute_step(ra, rb, acc);
+    __syncthreads();
+    int64_t s = 0;
+    for (; s + 2 <= nfull; s += 2) {
+        // even step s: LDS stage 0 holds s, g1 holds s+1, g0 is free
+        // unconditional (clamped) loads keep the wait counts exact
+        load_full(s + 2 < nfull ? s + 2 : nfull - 1, g0);
+        compute(0);
+        decode(g1, 1);
+        interleave_step(std::make_integer_sequence<int, 64>{});
+        __syncthreads();
+        // odd step s+1: stage 1 holds s+1, g0 holds s+2, g1 is free
+        load_full(s + 3 < nfull ? s + 3 : nfull - 1, g1);
+        compute(1);
+        decode(g0, 0);  // harmless on the last pass: stage 0 is not read again
+        interleave_step(std::make_integer_sequence<int, 64>{});
+        __syncthreads();
+    }
+    if (s < nfull) compute(0);  // odd number of full steps: the last one is in stage 0
+    if (nfull < nsteps) {       // partial last step
+        load(nfull, g1);
+        __syncthreads();
+        decode(g1, 1);
+        __syncthreads();
+        compute(1);
     }
 
+    // Epilogue: each wave stages 32 output rows at a time through LDS (fp32,
+    // alpha applied) and writes them back as 16-byte row segments.
     const float alpha = (1.0f / *a_senc) * (1.0f / *b_senc);
+    const int64_t m0 = tile_m * kBM + wm * 128, n0 = tile_n * kBN + wn * 128;
+    constexpr int kEpiStride = 132;  // floats per staged row (128 + 4 pad)
+    __syncthreads();                 // every wave is done reading the operand stages
+    float* stage_out = reinterpret_cast<float*>(&lds[0][0][0]) + wave * 32 * kEpiStride;
 #pragma unroll
-    for (int tm = 0; tm < 4; ++tm)
+    for (int tm = 0; tm < 4; ++tm) {
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn) {
-            const int64_t col = n0 + 32 * tn + lr;
-            if (col >= N) continue;
+        for (int tn = 0; tn < 4; ++tn)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-                const int64_t row = m0 + 32 * tm + (e >> 2) * 8 + g * 4 + (e & 3);
-                if (row >= M) continue;
-                const float v = acc[tm][tn][e] * alpha;
-                if constexpr (kOutF32)
-                    static_cast<float*>(c)[row * ldc + col] = v;
-                else
-                    static_cast<uint16_t*>(c)[row * ldc + col] = f32_to_bf16_rne(v);
+                const int r = (e >> 2) * 8 + g * 4 + (e & 3);
+                stage_out[r * kEpiStride + 32 * tn + lr] = acc[tm][tn][e] * alpha;
+            }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // 32 rows x 128 columns = 32 x 32 float4; lane handles float4 (row, q)
+#pragma unroll
+        for (int it = 0; it < 16; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx >> 5, q = idx & 31;
+            const float4 v = *reinterpret_cast<const float4*>(stage_out + r * kEpiStride + 4 * q);
+            const int64_t row = m0 + 32 * tm + r, col = n0 + 4 * q;
+            if (row < M && col < N) {
+                if constexpr (kOutF32) {
+                    float* dst = static_cast<float*>(c) + row * ldc + col;
+                    if (col + 4 <= N) {
+                        *reinterpret_cast<float4*>(dst) = v;
+                    } else {
+                        dst[0] = v.x;
+                        if (col + 1 < N) dst[1] = v.y;
+                        if (col + 2 < N) dst[2] = v.z;
+                    }
+                } else {
+                    uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
+                    const uint16_t b0 = f32_to_bf16_rne(v.x), b1 = f32_to_bf16_rne(v.y);
+                    const uint16_t b2 = f32_to_bf16_rne(v.z), b3 = f32_to_bf16_rne(v.w);
+                    if (col + 4 <= N) {
+                        *reinterpret_cast<uint2*>(dst) =
+                            make_uint2(b0 | ((uint32_t)b1 << 16), b2 | ((uint32_t)b3 << 16));
+                    } else {
+                        dst[0] = b0;
+                        if (col + 1 < N) dst[1] = b1;
+                        if (col + 2 < N) dst[2] = b2;
+                    }
+                }
             }
         }
+        __builtin_amdgcn_wave_barrier();
+    }
 }
 
 // Output of a GEMM with an empty contraction: alpha * 0.
