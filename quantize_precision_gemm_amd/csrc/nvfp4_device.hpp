@@ -87,32 +87,25 @@ __device__ __forceinline__ uint32_t e2m1_rne_pk(uint32_t old, float y0, float y1
 
 // Stochastic rounding of one fp32 value onto the E2M1 grid with a 16-bit
 // draw u16: with lo the grid point at or below |y| and g the gap above it,
-// round up iff u16 < trunc((|y| - lo) / g * 2^16); |y| >= 6 gives 6.
+// round up iff u16 < P = trunc((|y| - lo) / g * 2^16); |y| >= 6 gives 6.
+// Evaluated without branches on the fp32 bit pattern b of |y|:
+//   1 <= |y| < 6 : the grid keeps one mantissa bit, so lo's code is
+//                  (b >> 22) - 252 and (|y| - lo) / g is mantissa bits
+//                  [21:0] / 2^22, i.e. P = bits [21:6];
+//   |y| < 1      : Q = trunc(|y| * 2^17) (exact) has lo's code in bit 16
+//                  (0 or 0.5) and P in bits [15:0].
 __device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16)
 {
-    float a = __builtin_fabsf(y);
-    uint32_t sign = (__float_as_uint(y) >> 28) & 8u;
-    float lo, sc;
-    uint32_t cl;
-    if (a < 2.0f) {
-        float f2 = __builtin_floorf(a * 2.0f);
-        lo = f2 * 0.5f;
-        cl = (uint32_t)f2;
-        sc = 131072.0f;
-    } else if (a < 4.0f) {
-        float f1 = __builtin_floorf(a);
-        lo = f1;
-        cl = (uint32_t)f1 + 2u;
-        sc = 65536.0f;
-    } else {
-        lo = 4.0f;
-        cl = 6u;
-        sc = 32768.0f;
-    }
-    uint32_t P = (uint32_t)((a - lo) * sc);
+    const uint32_t yb = __float_as_uint(y);
+    const uint32_t ab = yb & 0x7FFFFFFFu;
+    // only read when |y| < 1; the clamp keeps the conversion in range
+    const uint32_t q = (uint32_t)(__uint_as_float(min(ab, 0x3F7FFFFFu)) * 131072.0f);
+    const bool small = ab < 0x3F800000u;  // |y| < 1
+    const uint32_t cl = small ? (q >> 16) : ((ab >> 22) - 252u);
+    const uint32_t P = small ? (q & 0xFFFFu) : ((ab >> 6) & 0xFFFFu);
     uint32_t code = cl + (u16 < P ? 1u : 0u);
-    code = (a >= 6.0f) ? 7u : code;
-    return code | sign;
+    code = (ab >= 0x40C00000u) ? 7u : code;  // |y| >= 6 (also Inf)
+    return code | ((yb >> 28) & 8u);
 }
 
 // Philox4x32-10 block function (Salmon, Moraes, Dror, Shaw, "Parallel Random
@@ -160,8 +153,8 @@ __device__ __forceinline__ Draws8 sr_draws8(uint64_t seed, uint64_t g8)
 __device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask)
 {
 #pragma unroll
-    for (int i = 0; i < 16; ++i)
-        if ((mask >> i) & 1u) v[i] = -v[i];
+    for (int i = 0; i < 16; ++i)  // negation as a sign-bit flip (exact, branch-free)
+        v[i] = __uint_as_float(__float_as_uint(v[i]) ^ (((mask >> i) & 1u) << 31));
 #pragma unroll
     for (int h = 1; h < 16; h <<= 1)
 #pragma unroll

@@ -60,25 +60,24 @@ __global__ __launch_bounds__(256) void k_amax_rows(const uint16_t* __restrict__ 
     }
 }
 
-// Contiguous fast path (ld == cols): a flat stream of 16-byte vectors.
+// Contiguous fast path (ld == cols): a flat stream of 16-byte vectors, four
+// in flight per thread.
+__device__ __forceinline__ uint32_t absmax8(const uint4& q)
+{
+    return max(max(bf16_absmax2(q.x), bf16_absmax2(q.y)), max(bf16_absmax2(q.z), bf16_absmax2(q.w)));
+}
+
 __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, int64_t nvec,
                                                    uint32_t* __restrict__ amax_bits)
 {
     uint32_t m = 0u;
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; v + stride < nvec; v += 2 * stride) {
-        uint4 q0 = x[v], q1 = x[v + stride];
-        m = max(m, max(max(bf16_absmax2(q0.x), bf16_absmax2(q0.y)),
-                       max(bf16_absmax2(q0.z), bf16_absmax2(q0.w))));
-        m = max(m, max(max(bf16_absmax2(q1.x), bf16_absmax2(q1.y)),
-                       max(bf16_absmax2(q1.z), bf16_absmax2(q1.w))));
+    for (; v + 3 * stride < nvec; v += 4 * stride) {
+        const uint4 q0 = x[v], q1 = x[v + stride], q2 = x[v + 2 * stride], q3 = x[v + 3 * stride];
+        m = max(m, max(max(absmax8(q0), absmax8(q1)), max(absmax8(q2), absmax8(q3))));
     }
-    if (v < nvec) {
-        uint4 q0 = x[v];
-        m = max(m, max(max(bf16_absmax2(q0.x), bf16_absmax2(q0.y)),
-                       max(bf16_absmax2(q0.z), bf16_absmax2(q0.w))));
-    }
+    for (; v < nvec; v += stride) m = max(m, absmax8(x[v]));
     m = wave_max_u32(m);
     __shared__ uint32_t red[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -180,9 +179,14 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
 }
 
 // ---------------------------------------------------------------------------
-// 16x16 quantiser (weights): a workgroup covers one 16-row strip and 64 tile
-// columns; lane l of wave w holds rows 4w..4w+3 of tile column l.
+// 16x16 quantiser (weights).  A workgroup covers 128 rows x 128 columns
+// (8 x 8 tiles).  Thread t takes tile column t % 8 and rows 4*(t/8) .. +3, so
+// the 4 threads sharing one tile sit in lanes 8 apart of the same wave and
+// the tile amax is two lane shuffles.  The transposed copy is assembled in
+// LDS and written as 64-byte rows.
 // ---------------------------------------------------------------------------
+
+constexpr int kW2Rows = 128, kW2Cols = 128;
 
 template <bool kSR>
 __global__ __launch_bounds__(256) void k_quant_16x16(
@@ -192,17 +196,16 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
     uint8_t* __restrict__ codes_t, int64_t ld_codes_t, uint8_t* __restrict__ scales_t,
     int64_t ld_scales_t, float* __restrict__ amax_out, float* __restrict__ s_enc_out)
 {
-    __shared__ float red[4][64];
-    __shared__ uint8_t tcodes[64][16][17];  // [tile col][row i][col j], padded
+    __shared__ __attribute__((aligned(16))) uint8_t tcodes[kW2Cols][kW2Rows / 2 + 16];  // [col][row/2]
 
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t nb = cols >> 4;
-    const int64_t tr = blockIdx.y;
-    const int64_t tc = (int64_t)blockIdx.x * 64 + lane;
-    const bool valid = tc < nb;
+    const int t = threadIdx.x;
+    const int tcl = t & 7, rg = t >> 3;            // tile column in block, row group (4 rows)
+    const int64_t col0 = (int64_t)blockIdx.x * kW2Cols + tcl * 16;
+    const int64_t row0 = (int64_t)blockIdx.y * kW2Rows + rg * 4;
+    const bool valid = col0 < cols && row0 < rows;  // rows, cols are multiples of 16
     const float amax = *amax_src;
     const float s_enc = tensor_scale(amax);
-    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+    if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
         *amax_out = amax;
         *s_enc_out = s_enc;
     }
@@ -211,9 +214,8 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t r = tr * 16 + wave * 4 + i;
         if (valid) {
-            const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + tc * 16);
+            const uint4* src = reinterpret_cast<const uint4*>(x + (row0 + i) * ld + col0);
             unpack16(src[0], src[1], v[i]);
         } else {
 #pragma unroll
@@ -221,70 +223,84 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
         }
         m = __builtin_fmaxf(m, absmax16(v[i]));
     }
-    red[wave][lane] = m;
-    __syncthreads();
-    const float tile_amax =
-        __builtin_fmaxf(__builtin_fmaxf(red[0][lane], red[1][lane]),
-                        __builtin_fmaxf(red[2][lane], red[3][lane]));
-    const uint32_t sb = block_scale(tile_amax, s_enc);
+    // the tile's four row groups are lanes l, l^8, l^16, l^24 of this wave
+    uint32_t mb = __float_as_uint(m);
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 8, 64));
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16, 64));
+    const uint32_t sb = block_scale(__uint_as_float(mb), s_enc);
     const float f = block_factor(sb, s_enc);
 
+    uint2 pk[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int64_t r = tr * 16 + wave * 4 + i;
-        uint2 pk;
         if constexpr (kSR)
-            pk = encode16_sr(v[i], f, seed, (uint64_t)(r * cols + tc * 16) >> 3);
+            pk[i] = encode16_sr(v[i], f, seed, (uint64_t)((row0 + i) * cols + col0) >> 3);
         else
-            pk = encode16_rne(v[i], f);
-        if (valid) *reinterpret_cast<uint2*>(codes + r * ld_codes + tc * 8) = pk;
-        if (codes_t) {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                uint32_t w = (j < 4 ? pk.x : pk.y) >> (8 * (j & 3));
-                tcodes[lane][wave * 4 + i][2 * j] = (uint8_t)(w & 15u);
-                tcodes[lane][wave * 4 + i][2 * j + 1] = (uint8_t)((w >> 4) & 15u);
-            }
-        }
+            pk[i] = encode16_rne(v[i], f);
+        if (valid) *reinterpret_cast<uint2*>(codes + (row0 + i) * ld_codes + (col0 >> 1)) = pk[i];
     }
-    if (valid && wave == 0) {
+    const int64_t tr = row0 >> 4, tc = col0 >> 4;
+    if (valid && (rg & 3) == 0) {
         scales[tr * ld_scales + tc] = (uint8_t)sb;
         if (scales_t) scales_t[tc * ld_scales_t + tr] = (uint8_t)sb;
     }
     if (codes_t == nullptr) return;
+
+    // column k of this thread's 16 columns: rows 4rg..4rg+3 -> two bytes of the
+    // transposed row k (rows 4rg, 4rg+1 in the first, 4rg+2, 4rg+3 in the second)
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int sh = 4 * (k & 7);
+        const uint32_t c0 = ((k < 8 ? pk[0].x : pk[0].y) >> sh) & 15u;
+        const uint32_t c1 = ((k < 8 ? pk[1].x : pk[1].y) >> sh) & 15u;
+        const uint32_t c2 = ((k < 8 ? pk[2].x : pk[2].y) >> sh) & 15u;
+        const uint32_t c3 = ((k < 8 ? pk[3].x : pk[3].y) >> sh) & 15u;
+        const uint16_t two = (uint16_t)(c0 | (c1 << 4) | (c2 << 8) | (c3 << 12));
+        *reinterpret_cast<uint16_t*>(&tcodes[tcl * 16 + k][rg * 2]) = two;
+    }
     __syncthreads();
-    // transposed codes: row k = 16*tc + j of W^T holds W[16*tr .. 16*tr+15, k]
+    // 128 transposed rows x 64 bytes: 4 threads per row, 16 bytes each
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-        const int idx = it * 256 + threadIdx.x;  // 64 tile columns x 16 columns j
-        const int tcl = idx >> 4, j = idx & 15;
-        const int64_t tcg = (int64_t)blockIdx.x * 64 + tcl;
-        if (tcg >= nb) continue;
-        uint32_t lo = 0u, hi = 0u;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) lo |= (uint32_t)tcodes[tcl][i][j] << (4 * i);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) hi |= (uint32_t)tcodes[tcl][8 + i][j] << (4 * i);
-        *reinterpret_cast<uint2*>(codes_t + (tcg * 16 + j) * ld_codes_t + tr * 8) = make_uint2(lo, hi);
+    for (int it = 0; it < 2; ++it) {
+        const int idx = it * 256 + t;
+        const int kr = idx >> 2, q = idx & 3;
+        const int64_t kcol = (int64_t)blockIdx.x * kW2Cols + kr;          // row of W^T
+        const int64_t nrow = (int64_t)blockIdx.y * kW2Rows + q * 32;      // first W row of the piece
+        if (kcol < cols && nrow < rows) {
+            const uint4 val = *reinterpret_cast<const uint4*>(&tcodes[kr][q * 16]);
+            uint8_t* dst = codes_t + kcol * ld_codes_t + (nrow >> 1);
+            if (nrow + 32 <= rows) {
+                *reinterpret_cast<uint4*>(dst) = val;
+            } else {  // rows end inside this 32-row piece (rows is a multiple of 16)
+                *reinterpret_cast<uint2*>(dst) = make_uint2(val.x, val.y);
+            }
+        }
     }
 }
 
 // ---------------------------------------------------------------------------
 // RHT + transpose + 1x16 quantiser (weight-gradient operands).
-// A workgroup covers 256 tokens x 64 channels; thread t takes channels
-// 4*(t%16) .. +3 of the tile and the 16-token chunk t/16.
+// A workgroup covers 256 tokens x 128 channels; thread t takes channels
+// 8*(t%16) .. +7 of the tile (one 16-byte load per token row) and the
+// 16-token chunk t/16.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void load_rht_chunk(const uint16_t* __restrict__ x, int64_t ld,
-                                               int64_t tok0, int64_t ch0, float (&v)[4][16])
+constexpr int kRhtTok = 256, kRhtCh = 128;
+
+__device__ __forceinline__ void load_rht_raw(const uint16_t* __restrict__ x, int64_t ld,
+                                             int64_t tok0, int64_t ch0, uint4 (&raw)[16])
+{
+#pragma unroll
+    for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const uint4*>(x + (tok0 + i) * ld + ch0);
+}
+
+// channel c (0..7) of the 8 loaded per row -> 16 fp32 values over the chunk
+__device__ __forceinline__ void unpack_channel(const uint4 (&raw)[16], int c, float (&v)[16])
 {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-        uint2 q = *reinterpret_cast<const uint2*>(x + (tok0 + i) * ld + ch0);
-        v[0][i] = bf16_lo(q.x);
-        v[1][i] = bf16_hi(q.x);
-        v[2][i] = bf16_lo(q.y);
-        v[3][i] = bf16_hi(q.y);
+        const uint32_t w = (c >> 1) == 0 ? raw[i].x : (c >> 1) == 1 ? raw[i].y : (c >> 1) == 2 ? raw[i].z : raw[i].w;
+        v[i] = (c & 1) ? bf16_hi(w) : bf16_lo(w);
     }
 }
 
@@ -293,16 +309,18 @@ __global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x
                                                   uint32_t* __restrict__ amax_bits)
 {
     const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
-    const int64_t ch0 = (int64_t)blockIdx.x * 64 + cg * 4;
-    const int64_t tok0 = (int64_t)blockIdx.y * 256 + j * 16;
+    const int64_t ch0 = (int64_t)blockIdx.x * kRhtCh + cg * 8;
+    const int64_t tok0 = (int64_t)blockIdx.y * kRhtTok + j * 16;
     uint32_t m = 0u;
     if (ch0 < channels && tok0 < tokens) {
-        float v[4][16];
-        load_rht_chunk(x, ld, tok0, ch0, v);
+        uint4 raw[16];
+        load_rht_raw(x, ld, tok0, ch0, raw);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            rht16(v[c], mask);
-            m = max(m, __float_as_uint(absmax16(v[c])));
+        for (int c = 0; c < 8; ++c) {
+            float v[16];
+            unpack_channel(raw, c, v);
+            rht16(v, mask);
+            m = max(m, __float_as_uint(absmax16(v)));
         }
     }
     m = wave_max_u32(m);
@@ -320,12 +338,12 @@ __global__ __launch_bounds__(256) void k_rht_quant(
     int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
     float* __restrict__ amax_out, float* __restrict__ s_enc_out)
 {
-    __shared__ uint2 scodes[64][17];    // [channel][chunk], padded
-    __shared__ uint8_t sscale[64][16];  // [channel][chunk]
+    __shared__ uint2 scodes[kRhtCh][17];    // [channel][chunk], padded
+    __shared__ uint8_t sscale[kRhtCh][16];  // [channel][chunk]
 
     const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
-    const int64_t chb = (int64_t)blockIdx.x * 64, tokb = (int64_t)blockIdx.y * 256;
-    const int64_t ch0 = chb + cg * 4;
+    const int64_t chb = (int64_t)blockIdx.x * kRhtCh, tokb = (int64_t)blockIdx.y * kRhtTok;
+    const int64_t ch0 = chb + cg * 8;
     const int64_t tok0 = tokb + j * 16;
     const float amax = *amax_src;
     const float s_enc = tensor_scale(amax);
@@ -334,27 +352,29 @@ __global__ __launch_bounds__(256) void k_rht_quant(
         *s_enc_out = s_enc;
     }
     if (ch0 < channels && tok0 < tokens) {
-        float v[4][16];
-        load_rht_chunk(x, ld, tok0, ch0, v);
+        uint4 raw[16];
+        load_rht_raw(x, ld, tok0, ch0, raw);
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            rht16(v[c], mask);
-            const uint32_t sb = block_scale(absmax16(v[c]), s_enc);
+        for (int c = 0; c < 8; ++c) {
+            float v[16];
+            unpack_channel(raw, c, v);
+            rht16(v, mask);
+            const uint32_t sb = block_scale(absmax16(v), s_enc);
             const float f = block_factor(sb, s_enc);
             uint2 pk;
             if constexpr (kSR)
-                pk = encode16_sr(v[c], f, seed, (uint64_t)((ch0 + c) * tokens + tok0) >> 3);
+                pk = encode16_sr(v, f, seed, (uint64_t)((ch0 + c) * tokens + tok0) >> 3);
             else
-                pk = encode16_rne(v[c], f);
-            scodes[cg * 4 + c][j] = pk;
-            sscale[cg * 4 + c][j] = (uint8_t)sb;
+                pk = encode16_rne(v, f);
+            scodes[cg * 8 + c][j] = pk;
+            sscale[cg * 8 + c][j] = (uint8_t)sb;
         }
     }
     __syncthreads();
-    // 64 channel rows x 16 chunks of 8 code bytes; 16 consecutive threads
+    // 128 channel rows x 16 chunks of 8 code bytes; 16 consecutive threads
     // write one row's 128 contiguous bytes.
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
+    for (int it = 0; it < 8; ++it) {
         const int idx = it * 256 + threadIdx.x;
         const int row = idx >> 4, q = idx & 15;
         const int64_t ch = chb + row, tk = tokb + q * 16;
@@ -384,7 +404,7 @@ void launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
     const int64_t nvec = rows * (cols >> 3);
     if (nvec == 0) return;
     if (ld == cols) {
-        hipLaunchKernelGGL(k_amax_flat, dim3(grid_for(nvec, 512, 4096)), dim3(256), 0, s,
+        hipLaunchKernelGGL(k_amax_flat, dim3(grid_for(nvec, 1024, 2048)), dim3(256), 0, s,
                            reinterpret_cast<const uint4*>(x), nvec, bits);
     } else {
         hipLaunchKernelGGL(k_amax_rows, dim3(grid_for(nvec, 256, 4096)), dim3(256), 0, s, x, rows,
@@ -410,7 +430,7 @@ void launch_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int
             hipLaunchKernelGGL(k_quant_1x16<false>, g, dim3(256), 0, s, x, rows, cols, ld, amax_src,
                                seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc);
     } else {
-        dim3 g((unsigned)(((cols >> 4) + 63) / 64), (unsigned)(rows >> 4));
+        dim3 g((unsigned)((cols + kW2Cols - 1) / kW2Cols), (unsigned)((rows + kW2Rows - 1) / kW2Rows));
         if (sr)
             hipLaunchKernelGGL(k_quant_16x16<true>, g, dim3(256), 0, s, x, rows, cols, ld,
                                amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales,
@@ -428,7 +448,7 @@ void launch_rht_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_
     uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
     hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, bits);
     if (tokens == 0 || channels == 0) return;
-    dim3 g((unsigned)((channels + 63) / 64), (unsigned)((tokens + 255) / 256));
+    dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
     hipLaunchKernelGGL(k_rht_amax, g, dim3(256), 0, s, x, tokens, channels, ld, mask, bits);
 }
 
@@ -440,7 +460,7 @@ void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64
         hipLaunchKernelGGL(k_publish, dim3(1), dim3(1), 0, s, amax_src, o.amax, o.s_enc);
         return;
     }
-    dim3 g((unsigned)((channels + 63) / 64), (unsigned)((tokens + 255) / 256));
+    dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
     if (rounding == 1)
         hipLaunchKernelGGL(k_rht_quant<true>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
                            amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax,
