@@ -18,8 +18,9 @@ X Student-t(4) at unit variance, W ~ N(0, 0.02), dY with log-normal row
 magnitudes.  They are resident in HBM before timing starts.
 
 value = 3 * 2*M*N*K / (wall time of one step), in TFLOP/s, quantisation
-included.  Per-operation times come from HIP events on the stream the
-library launches on.  The roofline entry is for the dominant kernel, the
+included; dgrad and wgrad run concurrently on two streams.  Per-operation
+times come from separate serialised passes with HIP events on the stream
+the library launches on.  The roofline entry is for the dominant kernel, the
 bf16-output GEMM (fprop and dgrad launches).  The CPU baseline is the
 oracle run on a token slice of the same step.
 """
@@ -76,7 +77,13 @@ def make_inputs(dev):
 
 
 class Step:
-    """Buffers and launch sequence of one step (no allocation inside run())."""
+    """Buffers and launch sequence of one step (no allocation inside run()).
+
+    dgrad and wgrad only depend on the quantised dY, W and X, so wgrad's
+    operands are quantised and its GEMM runs on a second stream, concurrently
+    with dgrad: each GEMM's last, partial wave of workgroups is filled by the
+    other's (dgrad is 2.5 and wgrad 6.25 waves of 256 tiles on 256 CUs).
+    """
 
     def __init__(self, q, torch, dev, x, w, dy):
         self.q, self.torch = q, torch
@@ -90,40 +97,66 @@ class Step:
         self.dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
         self.mask = q.nvfp4_rht_sign_mask(SEED + 1000)
-        self.ops = ["quant_X", "quant_W", "fprop", "quant_dY", "dgrad", "rht_dY", "rht_X", "wgrad"]
-        self.events = None
+        f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
+        self.ax, self.ax_rht, self.ady, self.ady_rht = f32(), f32(), f32(), f32()
+        self.side = torch.cuda.Stream(device=dev)  # default priority
+        self.ops = ["amax_X", "quant_X", "quant_W", "fprop", "amax_dY", "quant_dY", "dgrad",
+                    "rht_dY", "rht_X", "wgrad"]
 
-    def run(self, timed=False):
-        q, torch = self.q, self.torch
-        calls = [
-            lambda: q.nvfp4_quantize(self.x, q.BLOCK_1X16, q.RNE, out=self.gx),
+    def calls(self):
+        q = self.q
+        # X and dY are each quantised twice (1x16, and through the RHT for
+        # wgrad): one fused pass computes both tensor maxima of each.
+        return [
+            lambda: q.nvfp4_amax(self.x, self.mask, self.ax, self.ax_rht),
+            lambda: q.nvfp4_quantize(self.x, q.BLOCK_1X16, q.RNE, amax_in=self.ax, out=self.gx),
             lambda: q.nvfp4_quantize(self.w, q.BLOCK_16X16, q.RNE, out=self.gw),
             lambda: q.nvfp4_gemm(q.FPROP, self.gx, self.gw, out=self.y),
-            lambda: q.nvfp4_quantize(self.dy, q.BLOCK_1X16, q.SR, SEED + 100, out=self.gdy),
+            lambda: q.nvfp4_amax(self.dy, self.mask, self.ady, self.ady_rht),
+            lambda: q.nvfp4_quantize(self.dy, q.BLOCK_1X16, q.SR, SEED + 100, amax_in=self.ady,
+                                     out=self.gdy),
             lambda: q.nvfp4_gemm(q.DGRAD, self.gdy, self.gw, out=self.dx),
-            lambda: q.nvfp4_rht_quantize(self.dy, self.mask, q.SR, SEED + 101, out=self.gdyt),
-            lambda: q.nvfp4_rht_quantize(self.x, self.mask, q.RNE, out=self.gxt),
+            lambda: q.nvfp4_rht_quantize(self.dy, self.mask, q.SR, SEED + 101,
+                                         amax_in=self.ady_rht, out=self.gdyt),
+            lambda: q.nvfp4_rht_quantize(self.x, self.mask, q.RNE, amax_in=self.ax_rht,
+                                         out=self.gxt),
             lambda: q.nvfp4_gemm(q.WGRAD, self.gdyt, self.gxt, out=self.dw),
         ]
-        if not timed:
-            for c in calls:
-                c()
-            return None
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)]
+
+    def run(self):
+        """One step: wgrad's branch on the side stream, joined at the end."""
+        torch = self.torch
+        c = self.calls()
+        main = torch.cuda.current_stream()
+        for f in c[:6]:          # quantise X, W; fprop; amax and 1x16 SR of dY
+            f()
+        self.side.wait_stream(main)
+        c[6]()                   # dgrad on the main stream
+        with torch.cuda.stream(self.side):
+            c[7](); c[8](); c[9]()   # RHT operands and wgrad on the side stream
+        main.wait_stream(self.side)
+
+    def run_timed_ops(self):
+        """One step, serialised on one stream, with an event around every
+        operation (for per-operation times; events add small gaps)."""
+        torch = self.torch
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(self.ops) + 1)]
         ev[0].record()
-        for i, c in enumerate(calls):
-            c()
+        for i, f in enumerate(self.calls()):
+            f()
             ev[i + 1].record()
         return ev
 
 
 def quant_bytes():
-    """Algorithmic HBM bytes of each quantisation (amax pass + encode pass)."""
+    """Algorithmic HBM bytes of each quantisation operation: the fused amax
+    passes read their tensor once; the encode passes read it and write codes
+    and scales; W is quantised with its own amax pass and a transposed copy."""
     e_x, e_w, e_dy = M * K, N * K, M * N
-    one = lambda e: 2 * e + 2 * e + e // 2 + e // 16          # 1x16: read, read, codes, scales
-    two = lambda e: 2 * e + 2 * e + 2 * (e // 2 + e // 256)   # 16x16 + transposed copy
-    return {"quant_X": one(e_x), "quant_W": two(e_w), "quant_dY": one(e_dy),
-            "rht_dY": one(e_dy), "rht_X": one(e_x)}
+    enc = lambda e: 2 * e + e // 2 + e // 16                  # read bf16, write codes, scales
+    return {"amax_X": 2 * e_x, "quant_X": enc(e_x),
+            "quant_W": 2 * e_w + 2 * e_w + 2 * (e_w // 2 + e_w // 256),
+            "amax_dY": 2 * e_dy, "quant_dY": enc(e_dy), "rht_dY": enc(e_dy), "rht_X": enc(e_x)}
 
 
 def cpu_baseline(data, tokens=M):
@@ -183,14 +216,17 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    per_op = {k: [] for k in step.ops}
-    torch.cuda.synchronize()
+    # timed steps: nothing but the step itself between the two synchronisations
     t0 = time.perf_counter()
-    evs = []
     for _ in range(args.steps):
-        evs.append(step.run(timed=True))
+        step.run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    # per-operation times: separate, serialised passes with events
+    per_op = {k: [] for k in step.ops}
+    evs = [step.run_timed_ops() for _ in range(max(5, args.steps // 2))]
+    torch.cuda.synchronize()
     for ev in evs:
         for i, k in enumerate(step.ops):
             per_op[k].append(ev[i].elapsed_time(ev[i + 1]))

@@ -79,13 +79,13 @@ extern "C" {
  *             value (the GEMM masks them).  16-byte aligned.
  *   scales    1x16 : rows x ld_scales bytes, ld_scales >= cols / 16;
  *             16x16: rows/16 x ld_scales bytes, ld_scales >= cols / 16.
- *             ld_scales is even; 2-byte aligned.
+ *             ld_scales is a multiple of 4; 4-byte aligned.
  *   codes_t   optional, 16x16 only: the codes of the transposed matrix
  *             (cols x ld_codes_t bytes, ld_codes_t a multiple of 16 and at
  *             least round_up(rows, 32) / 2).  Needed by the DGRAD GEMM.
  *   scales_t  optional, 16x16 only: the transposed tile scales
- *             (cols/16 x ld_scales_t bytes, ld_scales_t even and at least
- *             rows / 16).  Needed by the DGRAD GEMM.
+ *             (cols/16 x ld_scales_t bytes, ld_scales_t a multiple of 4 and
+ *             at least rows / 16).  Needed by the DGRAD GEMM.
  *   amax      1 float: max |x| over the tensor as quantised.
  *   s_enc     1 float: the tensor's FP32 encode scale.
  */
@@ -158,6 +158,27 @@ int nvfp4_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int3
 int nvfp4_rht_quantize(const void* x, int64_t tokens, int64_t channels, int64_t ld_x,
                        uint32_t sign_mask, int32_t rounding, uint64_t seed,
                        const float* amax_in, nvfp4_tensor* out, void* stream);
+
+/*
+ * nvfp4_amax -- tensor amax of a bf16 matrix and, optionally, of its 16-point
+ * random Hadamard transform along the rows, in one pass over the data.
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.A (the FP32 tensor-level scale is taken from the tensor
+ * amax) and 2.B.2 (the wgrad inputs are quantised after the transform).
+ * A tensor that is quantised twice -- 1x16 for fprop or dgrad and through
+ * the RHT for wgrad -- needs both maxima; passing them as amax_in to
+ * nvfp4_quantize and nvfp4_rht_quantize replaces their own amax passes with
+ * this single read.  The results are identical to those passes' (a maximum
+ * does not depend on the order of evaluation).
+ *   x         device bf16, rows x ld_x elements, 16-byte aligned, ld_x >= cols
+ *             and a multiple of 8; cols a multiple of 8.
+ *   amax      device float: max |x|.
+ *   amax_rht  device float or NULL: max |RHT(x)| over aligned 16-row chunks
+ *             with sign_mask as in nvfp4_rht_quantize (rows = tokens, a
+ *             multiple of 16).  NULL skips the transform.
+ */
+int nvfp4_amax(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t sign_mask,
+               float* amax, float* amax_rht, void* stream);
 
 /*
  * nvfp4_rht_sign_mask -- host helper: the 16 random signs of the Hadamard

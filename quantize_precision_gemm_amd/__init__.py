@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm",
-    "nvfp4_rht_sign_mask", "lib_path", "load_library",
+    "nvfp4_rht_sign_mask", "nvfp4_amax", "lib_path", "load_library",
 ]
 
 BLOCK_1X16 = 0
@@ -73,6 +73,8 @@ def load_library():
         L.nvfp4_rht_quantize.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [i32, D, D, P, i64, i32, P]
         L.nvfp4_gemm.restype = ctypes.c_int
+        L.nvfp4_amax.argtypes = [P, i64, i64, i64, u32, P, P, P]
+        L.nvfp4_amax.restype = ctypes.c_int
         L.nvfp4_rht_sign_mask.argtypes = [u64]
         L.nvfp4_rht_sign_mask.restype = u32
         L.nvfp4_status_string.argtypes = [i32]
@@ -211,6 +213,25 @@ def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None):
                                    out.stride(0), dt, _stream(stream))
     _check(st, "nvfp4_gemm")
     return out
+
+
+def nvfp4_amax(x, sign_mask=None, amax=None, amax_rht=None, stream=None):
+    """max |x| and, if sign_mask is given, max |RHT(x)| in one pass (see nvfp4_amax).
+
+    Returns (amax, amax_rht) as 1-element float32 device tensors (amax_rht None
+    without a sign mask); pass them as amax_in to the quantisers.
+    """
+    _check_bf16(x)
+    rows, cols = x.shape
+    amax = amax if amax is not None else torch.empty(1, dtype=torch.float32, device=x.device)
+    if sign_mask is not None and amax_rht is None:
+        amax_rht = torch.empty(1, dtype=torch.float32, device=x.device)
+    st = load_library().nvfp4_amax(_ptr(x), rows, cols, x.stride(0),
+                                   0 if sign_mask is None else sign_mask, _ptr(amax),
+                                   _ptr(amax_rht) if sign_mask is not None else None,
+                                   _stream(stream))
+    _check(st, "nvfp4_amax")
+    return amax, (amax_rht if sign_mask is not None else None)
 
 
 def nvfp4_rht_sign_mask(seed):

@@ -138,6 +138,25 @@ int nvfp4_rht_quantize(const void* x, int64_t tokens, int64_t channels, int64_t 
     return launch_status();
 }
 
+int nvfp4_amax(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t sign_mask,
+               float* amax, float* amax_rht, void* stream)
+{
+    if (rows < 0 || cols < 0 || cols % 8 != 0) return NVFP4_ERR_SHAPE;
+    if (amax_rht && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (!amax) return NVFP4_ERR_NULL;
+    if (!x && rows > 0 && cols > 0) return NVFP4_ERR_NULL;
+    if (ld_x < cols) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld_x % 8 != 0) return NVFP4_ERR_ALIGN;
+    if (!aligned(amax, 4) || (amax_rht && !aligned(amax_rht, 4))) return NVFP4_ERR_ALIGN;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    if (amax_rht)
+        nvfp4::launch_amax_dual(xb, rows, cols, ld_x, sign_mask & 0xFFFFu, amax, amax_rht, s);
+    else
+        nvfp4::launch_amax_rows(xb, rows, cols, ld_x, amax, s);
+    return launch_status();
+}
+
 // Philox4x32-10 block function on the host (Salmon et al., SC'11).
 static void philox_host(uint32_t c[4], uint32_t k0, uint32_t k1)
 {

@@ -39,6 +39,8 @@ void launch_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int
                   hipStream_t s);
 void launch_rht_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
                      uint32_t mask, float* amax, hipStream_t s);
+void launch_amax_dual(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
+                      uint32_t mask, float* amax, float* amax_rht, hipStream_t s);
 void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
                       uint32_t mask, int rounding, uint64_t seed, const float* amax_src,
                       const QOut& o, hipStream_t s);

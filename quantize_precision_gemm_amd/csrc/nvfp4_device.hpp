@@ -146,11 +146,10 @@ __device__ __forceinline__ Draws8 sr_draws8(uint64_t seed, uint64_t g8)
     return d;
 }
 
-// 16-point random Hadamard transform of v (in place): sign flips from
-// `mask`, radix-2 butterfly with strides 1, 2, 4, 8 (each sum and difference
-// rounded to fp32), then the exact multiplication by 1/4.  This fixes the
-// rounding order that the codes depend on.
-__device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask)
+// 16-point random Hadamard transform of v (in place), without the final
+// factor 1/4: sign flips from `mask`, then the radix-2 butterfly with strides
+// 1, 2, 4, 8 (each sum and difference rounded to fp32).
+__device__ __forceinline__ void rht16_unscaled(float (&v)[16], uint32_t mask)
 {
 #pragma unroll
     for (int i = 0; i < 16; ++i)  // negation as a sign-bit flip (exact, branch-free)
@@ -164,6 +163,13 @@ __device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask)
                 v[i] = a + b;
                 v[i + h] = a - b;
             }
+}
+
+// The full transform: the butterfly above, then the exact multiplication by
+// 1/4.  This fixes the rounding order that the codes depend on.
+__device__ __forceinline__ void rht16(float (&v)[16], uint32_t mask)
+{
+    rht16_unscaled(v, mask);
 #pragma unroll
     for (int i = 0; i < 16; ++i) v[i] *= 0.25f;
 }

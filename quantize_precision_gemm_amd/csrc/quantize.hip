@@ -22,6 +22,11 @@ namespace nvfp4 {
 // ---------------------------------------------------------------------------
 
 __global__ void k_zero_u32(uint32_t* p) { *p = 0u; }
+__global__ void k_zero_u32x2(uint32_t* p, uint32_t* q)
+{
+    *p = 0u;
+    *q = 0u;
+}
 
 // Empty tensors: only the tensor amax and encode scale are published.
 __global__ void k_publish(const float* __restrict__ amax_src, float* __restrict__ amax_out,
@@ -30,6 +35,15 @@ __global__ void k_publish(const float* __restrict__ amax_src, float* __restrict_
     const float amax = *amax_src;
     *amax_out = amax;
     *s_enc_out = tensor_scale(amax);
+}
+
+// Merge a workgroup's max into the tensor amax.  Same-address atomics from
+// thousands of workgroups serialise in L2, so the atomic is skipped when the
+// value already stored is at least as large (a stale read only costs an
+// unnecessary atomic; the final value is the same).
+__device__ __forceinline__ void merge_amax(uint32_t* amax_bits, uint32_t v)
+{
+    if (v > __atomic_load_n(amax_bits, __ATOMIC_RELAXED)) atomicMax(amax_bits, v);
 }
 
 // max |x| of a row-major bf16 matrix (rows x cols, leading dimension ld, all
@@ -56,7 +70,7 @@ __global__ __launch_bounds__(256) void k_amax_rows(const uint16_t* __restrict__ 
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t mm = max(max(red[0], red[1]), max(red[2], red[3]));
-        atomicMax(amax_bits, mm << 16);
+        merge_amax(amax_bits, mm << 16);
     }
 }
 
@@ -70,14 +84,17 @@ __device__ __forceinline__ uint32_t absmax8(const uint4& q)
 __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, int64_t nvec,
                                                    uint32_t* __restrict__ amax_bits)
 {
+    // each workgroup reads 4 x 256 consecutive vectors, each thread 4 of them
+    const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
     uint32_t m = 0u;
-    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-    int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    for (; v + 3 * stride < nvec; v += 4 * stride) {
-        const uint4 q0 = x[v], q1 = x[v + stride], q2 = x[v + 2 * stride], q3 = x[v + 3 * stride];
-        m = max(m, max(max(absmax8(q0), absmax8(q1)), max(absmax8(q2), absmax8(q3))));
+    if (base + 768 < nvec) {
+        const uint4 q0 = x[base], q1 = x[base + 256], q2 = x[base + 512], q3 = x[base + 768];
+        m = max(max(absmax8(q0), absmax8(q1)), max(absmax8(q2), absmax8(q3)));
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            if (base + 256 * j < nvec) m = max(m, absmax8(x[base + 256 * j]));
     }
-    for (; v < nvec; v += stride) m = max(m, absmax8(x[v]));
     m = wave_max_u32(m);
     __shared__ uint32_t red[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -85,7 +102,7 @@ __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, 
     __syncthreads();
     if (threadIdx.x == 0) {
         uint32_t mm = max(max(red[0], red[1]), max(red[2], red[3]));
-        atomicMax(amax_bits, mm << 16);
+        merge_amax(amax_bits, mm << 16);
     }
 }
 
@@ -315,20 +332,66 @@ __global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x
     if (ch0 < channels && tok0 < tokens) {
         uint4 raw[16];
         load_rht_raw(x, ld, tok0, ch0, raw);
+        float mu = 0.0f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) {
             float v[16];
             unpack_channel(raw, c, v);
-            rht16(v, mask);
-            m = max(m, __float_as_uint(absmax16(v)));
+            rht16_unscaled(v, mask);
+            mu = __builtin_fmaxf(mu, absmax16(v));
         }
+        // rounding is monotonic: the max of the scaled values is the scaled max
+        m = __float_as_uint(mu * 0.25f);
     }
     m = wave_max_u32(m);
     __shared__ uint32_t red[4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) red[wave] = m;
     __syncthreads();
-    if (threadIdx.x == 0) atomicMax(amax_bits, max(max(red[0], red[1]), max(red[2], red[3])));
+    if (threadIdx.x == 0) merge_amax(amax_bits, max(max(red[0], red[1]), max(red[2], red[3])));
+}
+
+// One pass over a tokens x channels matrix: max |x| and max |RHT(x)| (the
+// transform nvfp4_rht_quantize applies), for callers that quantise the same
+// tensor both ways.
+__global__ __launch_bounds__(256) void k_amax_dual(const uint16_t* __restrict__ x, int64_t tokens,
+                                                   int64_t channels, int64_t ld, uint32_t mask,
+                                                   uint32_t* __restrict__ amax_bits,
+                                                   uint32_t* __restrict__ amax_rht_bits)
+{
+    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int64_t ch0 = (int64_t)blockIdx.x * kRhtCh + cg * 8;
+    const int64_t tok0 = (int64_t)blockIdx.y * kRhtTok + j * 16;
+    uint32_t m = 0u, mr = 0u;
+    if (ch0 < channels && tok0 < tokens) {
+        uint4 raw[16];
+        load_rht_raw(x, ld, tok0, ch0, raw);
+#pragma unroll
+        for (int i = 0; i < 16; ++i) m = max(m, absmax8(raw[i]));
+        float mu = 0.0f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float v[16];
+            unpack_channel(raw, c, v);
+            rht16_unscaled(v, mask);
+            mu = __builtin_fmaxf(mu, absmax16(v));
+        }
+        // rounding is monotonic: the max of the scaled values is the scaled max
+        mr = __float_as_uint(mu * 0.25f);
+    }
+    m = wave_max_u32(m);
+    mr = wave_max_u32(mr);
+    __shared__ uint32_t red[2][4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) {
+        red[0][wave] = m;
+        red[1][wave] = mr;
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        merge_amax(amax_bits, max(max(red[0][0], red[0][1]), max(red[0][2], red[0][3])) << 16);
+        merge_amax(amax_rht_bits, max(max(red[1][0], red[1][1]), max(red[1][2], red[1][3])));
+    }
 }
 
 template <bool kSR>
@@ -404,7 +467,7 @@ void launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
     const int64_t nvec = rows * (cols >> 3);
     if (nvec == 0) return;
     if (ld == cols) {
-        hipLaunchKernelGGL(k_amax_flat, dim3(grid_for(nvec, 1024, 2048)), dim3(256), 0, s,
+        hipLaunchKernelGGL(k_amax_flat, dim3(grid_for(nvec, 1024, INT32_MAX)), dim3(256), 0, s,
                            reinterpret_cast<const uint4*>(x), nvec, bits);
     } else {
         hipLaunchKernelGGL(k_amax_rows, dim3(grid_for(nvec, 256, 4096)), dim3(256), 0, s, x, rows,
@@ -450,6 +513,17 @@ void launch_rht_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_
     if (tokens == 0 || channels == 0) return;
     dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
     hipLaunchKernelGGL(k_rht_amax, g, dim3(256), 0, s, x, tokens, channels, ld, mask, bits);
+}
+
+void launch_amax_dual(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
+                      uint32_t mask, float* amax, float* amax_rht, hipStream_t s)
+{
+    uint32_t* b0 = reinterpret_cast<uint32_t*>(amax);
+    uint32_t* b1 = reinterpret_cast<uint32_t*>(amax_rht);
+    hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, b0, b1);
+    if (tokens == 0 || channels == 0) return;
+    dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
+    hipLaunchKernelGGL(k_amax_dual, g, dim3(256), 0, s, x, tokens, channels, ld, mask, b0, b1);
 }
 
 void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,

@@ -127,3 +127,13 @@ def test_gemm_validation(lib):
     assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 66, 0, None) == -3
     assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 16, 0, None) == -2
     assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(op(40, 64, 1)), FAKE, 64, 0, None) == -2
+
+
+def test_amax_validation(lib):
+    out = FAKE
+    assert lib.nvfp4_amax(FAKE, 16, 12, 16, 1, out, out, None) == -2      # cols % 8
+    assert lib.nvfp4_amax(FAKE, 24, 16, 16, 1, out, out, None) == -2      # RHT rows % 16
+    assert lib.nvfp4_amax(FAKE, 16, 16, 16, 1, None, out, None) == -1     # no amax output
+    assert lib.nvfp4_amax(None, 16, 16, 16, 1, out, None, None) == -1     # null input
+    assert lib.nvfp4_amax(FAKE + 8, 16, 16, 16, 1, out, None, None) == -3  # misaligned input
+    assert lib.nvfp4_amax(FAKE, 16, 16, 8, 1, out, None, None) == -2      # ld < cols

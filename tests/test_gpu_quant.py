@@ -234,3 +234,31 @@ def test_error_paths(env):
     with pytest.raises(RuntimeError, match="status -1"):
         q.nvfp4_gemm(q.DGRAD, a, w)                           # no transposed copy
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("shape", [(16, 8), (272, 200), (512, 264), (48, 1040)])
+def test_fused_amax_matches_quantisers(env, shape):
+    # one pass gives max |x| and max |RHT(x)|; fed back as amax_in the
+    # quantisers produce exactly the oracle's codes and scales
+    torch, oracle, q, wl, dev = env
+    rng = np.random.default_rng(shape[0] * 3 + shape[1])
+    x = wl.lognormal_rows(rng, shape)
+    mask = int(rng.integers(0, 65536))
+    xd = to_dev(x, dev)
+    print(f"fused amax {shape}", flush=True)
+    a, ar = q.nvfp4_amax(xd, mask)
+    a_only, none = q.nvfp4_amax(xd)
+    torch.cuda.synchronize()
+    assert none is None
+    o1 = oracle.quantize(x, oracle.BLOCK_1X16, oracle.SR, 4) if shape[1] % 16 == 0 else None
+    orht = oracle.rht_quantize(x, mask, oracle.SR, 5)
+    assert np.float32(ar.item()) == np.float32(orht.amax)
+    assert np.float32(a.item()) == np.float32(a_only.item())
+    assert np.float32(a.item()) == np.float32(np.abs(wl.bf16_bits_to_f32(x)).max())
+    g = q.nvfp4_rht_quantize(xd, mask, q.SR, 5, amax_in=ar)
+    torch.cuda.synchronize()
+    assert_same_quant(g, orht, f"rht with fused amax {shape}")
+    if o1 is not None:
+        g1 = q.nvfp4_quantize(xd, q.BLOCK_1X16, q.SR, 4, amax_in=a)
+        torch.cuda.synchronize()
+        assert_same_quant(g1, o1, f"1x16 with fused amax {shape}")
