@@ -16,15 +16,16 @@
 //
 // Both operands are "rows x K" with K contiguous, so one kernel serves all
 // passes (the dgrad weight operand is the transposed 16x16-block copy written
-// by the quantiser).  A workgroup of 4 waves computes a 256x256 tile in K
-// steps of 64.  Per step every thread decodes one row of A and one row of B
-// (32 code bytes, 4 scales each) into an fp16 tile in LDS, so each element is
-// decoded once per workgroup; each wave then runs 4x4 MFMA 32x32x16 tiles
-// (its 128x128 quarter, 256 fp32 accumulators in AGPRs) over the tile.  Two
-// LDS stages alternate: while the MFMAs consume one, the next step's codes
-// (loaded from global memory one step earlier) are decoded into the other,
-// and the global loads two steps ahead are in flight.  The epilogue stages
-// 32 output rows per wave through LDS and stores 16-byte row segments.
+// by the quantiser).  A workgroup of 8 waves (two per SIMD) computes a
+// 256x256 tile in K steps of 64.  Per step each thread decodes one row of A
+// (threads 0-255) or of B (256-511) -- 32 code bytes, 4 scales -- into an
+// fp16 tile in LDS, so each element is decoded once per workgroup; each wave
+// then runs 4x2 MFMA 32x32x16 tiles (a 128x64 slab, 128 fp32 accumulators)
+// over the tile.  Two LDS stages alternate: while the MFMAs consume one, the
+// next step's codes (loaded from global memory one step earlier) are decoded
+// into the other, and the global loads two steps ahead are in flight.  Two
+// waves per SIMD let one wave's MFMAs cover the other's waits.  The epilogue
+// stages 32 output rows per wave through LDS and stores 16-byte segments.
 //
 // Lane layout of v_mfma_f32_32x32x16_f16: lane l supplies row (A) or column
 // (B) l % 32 and the 8 consecutive k 8*(l/32) .. +7 of the 16-wide step;
@@ -111,7 +112,7 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 // 4 x 4 MFMA 32x32x16 tiles (128 x 128) over the stage.  Two LDS stages
 // alternate; the global loads of step s+2 are issued before the MFMAs of
 // step s, and step s+1 (loaded one iteration earlier) is decoded after them.
-// Instruction-schedule hint for one K step (64 MFMAs per wave): the first
+// Instruction-schedule hint for one K step (32 MFMAs per wave): the first
 // half of the MFMAs is interleaved with the LDS fragment reads only; the
 // second half also carries the decode of the next step (4 VALU per MFMA) and
 // its LDS writes, which gives the global loads feeding that decode as much
@@ -119,9 +120,9 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 template <int kM>
 __device__ __forceinline__ void interleave_slot()
 {
-    constexpr int sub = kM / 16;
+    constexpr int sub = kM / 8;
     __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one MFMA
-    if constexpr (kM < 32) {
+    if constexpr (kM < 16) {
         if constexpr (sub < 3 && kM % 2 == 1) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     } else {
         __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // VALU
@@ -133,12 +134,12 @@ __device__ __forceinline__ void interleave_slot()
 template <int... kMs>
 __device__ __forceinline__ void interleave_step(std::integer_sequence<int, kMs...>)
 {
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // fragments of the first sub-step
+    __builtin_amdgcn_sched_group_barrier(0x100, 6, 0);  // fragments of the first sub-step
     (interleave_slot<kMs>(), ...);
 }
 
 template <bool kOutF32>
-__global__ __launch_bounds__(256, 1) void k_gemm_nt(
+__global__ __launch_bounds__(512, 1) void k_gemm_nt(
     const uint8_t* __restrict__ a_codes, int64_t a_ldc, const uint8_t* __restrict__ a_scales,
     int64_t a_lds, int a_shift, const float* __restrict__ a_senc,
     const uint8_t* __restrict__ b_codes, int64_t b_ldc, const uint8_t* __restrict__ b_scales,
@@ -166,61 +167,63 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(
     const int64_t tile_m = first_m + in_group % gsz;
     const int64_t tile_n = in_group / gsz;
 
-    // rows this thread loads and decodes (clamped; the extra rows are never stored)
-    int64_t ra = tile_m * kBM + tid, rb = tile_n * kBN + tid;
-    ra = ra < M ? ra : M - 1;
-    rb = rb < N ? rb : N - 1;
-    const int64_t oca = ra * a_ldc, osa = (ra >> a_shift) * a_lds;
-    const int64_t ocb = rb * b_ldc, osb = (rb >> b_shift) * b_lds;
+    // the row this thread loads and decodes: threads 0..255 take A rows,
+    // 256..511 B rows (clamped; the extra rows are never stored)
+    const bool is_b = tid >= 256;
+    const int rid = tid & 255;
+    int64_t rr = is_b ? tile_n * kBN + rid : tile_m * kBM + rid;
+    const int64_t lim = is_b ? N : M;
+    rr = rr < lim ? rr : lim - 1;
+    const uint8_t* my_codes = is_b ? b_codes : a_codes;
+    const uint8_t* my_scales = is_b ? b_scales : a_scales;
+    const int64_t oc = rr * (is_b ? b_ldc : a_ldc);
+    const int64_t os = (rr >> (is_b ? b_shift : a_shift)) * (is_b ? b_lds : a_lds);
 
-    float16_t acc[4][4];
+    float16_t acc[4][2];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
     const int64_t nblk = K >> 4;
     const int64_t nsteps = (K + kKS - 1) / kKS;
-    const int wm = wave >> 1, wn = wave & 1;
+    const int wm = wave >> 2, wn = wave & 3;
     // fragment read offsets within a stage: row (32 t + lr) of the wave's
-    // 128-row slab, k = 16 i + 8 g
+    // 128-row A slab / 64-row B slab, k = 16 i + 8 g
     const int a_frag = (wm * 128 + lr) * kRowBytes + 16 * g;
-    const int b_frag = (wn * 128 + lr) * kRowBytes + 16 * g;
+    const int b_frag = (wn * 64 + lr) * kRowBytes + 16 * g;
 
     auto load = [&](int64_t step, Stage& st) {
-        const int64_t k0 = step * kKS;
-        load_row(a_codes, a_scales, oca, osa, k0, nblk, st.ca0, st.ca1, st.sa);
-        load_row(b_codes, b_scales, ocb, osb, k0, nblk, st.cb0, st.cb1, st.sb);
+        load_row(my_codes, my_scales, oc, os, step * kKS, nblk, st.ca0, st.ca1, st.sa);
     };
     auto decode = [&](const Stage& st, int stage) {
-        decode_row(st.ca0, st.ca1, st.sa, &lds[stage][0][tid * kRowBytes]);
-        decode_row(st.cb0, st.cb1, st.sb, &lds[stage][1][tid * kRowBytes]);
+        decode_row(st.ca0, st.ca1, st.sa, &lds[stage][is_b ? 1 : 0][rid * kRowBytes]);
     };
     auto compute = [&](int stage) {
         const uint8_t* As = lds[stage][0];
         const uint8_t* Bs = lds[stage][1];
-        half8_t af[2][4], bf[2][4];  // fragments of two sub-steps in flight
+        half8_t af[2][4], bf[2][2];  // fragments of two sub-steps in flight
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            af[0][t] = *reinterpret_cast<const half8_t*>(As + a_frag + t * 32 * kRowBytes);
-            bf[0][t] = *reinterpret_cast<const half8_t*>(Bs + b_frag + t * 32 * kRowBytes);
-        }
+        for (int t = 0; t < 4; ++t) af[0][t] = *reinterpret_cast<const half8_t*>(As + a_frag + t * 32 * kRowBytes);
+#pragma unroll
+        for (int t = 0; t < 2; ++t) bf[0][t] = *reinterpret_cast<const half8_t*>(Bs + b_frag + t * 32 * kRowBytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int cur = i & 1, nxt = cur ^ 1;
             if (i < 3) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t) {
+                for (int t = 0; t < 4; ++t)
                     af[nxt][t] = *reinterpret_cast<const half8_t*>(As + a_frag + t * 32 * kRowBytes + 32 * (i + 1));
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
                     bf[nxt][t] = *reinterpret_cast<const half8_t*>(Bs + b_frag + t * 32 * kRowBytes + 32 * (i + 1));
-                }
             }
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-                for (int tn = 0; tn < 4; ++tn)
+                for (int tn = 0; tn < 2; ++tn)
                     acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][tm], bf[cur][tn], acc[tm][tn], 0, 0, 0);
         }
     };
@@ -229,14 +232,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(
     const int64_t nfull = K / kKS;
     auto load_full = [&](int64_t step, Stage& st) {
         const int64_t k0 = step * kKS;
-        const uint4* pa = reinterpret_cast<const uint4*>(a_codes + oca + (k0 >> 1));
-        const uint4* pb = reinterpret_cast<const uint4*>(b_codes + ocb + (k0 >> 1));
-        st.ca0 = pa[0];
-        st.ca1 = pa[1];
-        st.cb0 = pb[0];
-        st.cb1 = pb[1];
-        st.sa = *reinterpret_cast<const uint32_t*>(a_scales + osa + (k0 >> 4));
-        st.sb = *reinterpret_cast<const uint32_t*>(b_scales + osb + (k0 >> 4));
+        const uint4* p = reinterpret_cast<const uint4*>(my_codes + oc + (k0 >> 1));
+        st.ca0 = p[0];
+        st.ca1 = p[1];
+        st.sa = *reinterpret_cast<const uint32_t*>(my_scales + os + (k0 >> 4));
     };
     Stage g0, g1;
     if (nfull > 0) {
@@ -252,13 +251,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(
         load_full(s + 2 < nfull ? s + 2 : nfull - 1, g0);
         compute(0);
         decode(g1, 1);
-        interleave_step(std::make_integer_sequence<int, 64>{});
+        interleave_step(std::make_integer_sequence<int, 32>{});
         __syncthreads();
         // odd step s+1: stage 1 holds s+1, g0 holds s+2, g1 is free
         load_full(s + 3 < nfull ? s + 3 : nfull - 1, g1);
         compute(1);
         decode(g0, 0);  // harmless on the last pass: stage 0 is not read again
-        interleave_step(std::make_integer_sequence<int, 64>{});
+        interleave_step(std::make_integer_sequence<int, 32>{});
         __syncthreads();
     }
     if (s < nfull) compute(0);  // odd number of full steps: the last one is in stage 0
@@ -273,14 +272,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(
     // Epilogue: each wave stages 32 output rows at a time through LDS (fp32,
     // alpha applied) and writes them back as 16-byte row segments.
     const float alpha = (1.0f / *a_senc) * (1.0f / *b_senc);
-    const int64_t m0 = tile_m * kBM + wm * 128, n0 = tile_n * kBN + wn * 128;
-    constexpr int kEpiStride = 132;  // floats per staged row (128 + 4 pad)
+    const int64_t m0 = tile_m * kBM + wm * 128, n0 = tile_n * kBN + wn * 64;
+    constexpr int kEpiStride = 68;   // floats per staged row (64 + 4 pad)
     __syncthreads();                 // every wave is done reading the operand stages
     float* stage_out = reinterpret_cast<float*>(&lds[0][0][0]) + wave * 32 * kEpiStride;
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
 #pragma unroll
-        for (int tn = 0; tn < 4; ++tn)
+        for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = (e >> 2) * 8 + g * 4 + (e & 3);
@@ -288,11 +287,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_nt(
             }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
         __builtin_amdgcn_wave_barrier();
-        // 32 rows x 128 columns = 32 x 32 float4; lane handles float4 (row, q)
+        // 32 rows x 64 columns = 32 x 16 float4; lane handles float4 (row, q)
 #pragma unroll
-        for (int it = 0; it < 16; ++it) {
+        for (int it = 0; it < 8; ++it) {
             const int idx = it * 64 + lane;
-            const int r = idx >> 5, q = idx & 31;
+            const int r = idx >> 4, q = idx & 15;
             const float4 v = *reinterpret_cast<const float4*>(stage_out + r * kEpiStride + 4 * q);
             const int64_t row = m0 + 32 * tm + r, col = n0 + 4 * q;
             if (row < M && col < N) {
@@ -353,11 +352,11 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
     const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     dim3 grid((unsigned)tiles), block(256);
     if (out_fp32)
-        hipLaunchKernelGGL(k_gemm_nt<true>, grid, block, 0, s, a.codes, a.ld_codes, a.scales,
+        hipLaunchKernelGGL(k_gemm_nt<true>, grid, dim3(512), 0, s, a.codes, a.ld_codes, a.scales,
                            a.ld_scales, a.scale_row_shift, a.s_enc, b.codes, b.ld_codes, b.scales,
                            b.ld_scales, b.scale_row_shift, b.s_enc, M, N, K, c, ldc);
     else
-        hipLaunchKernelGGL(k_gemm_nt<false>, grid, block, 0, s, a.codes, a.ld_codes, a.scales,
+        hipLaunchKernelGGL(k_gemm_nt<false>, grid, dim3(512), 0, s, a.codes, a.ld_codes, a.scales,
                            a.ld_scales, a.scale_row_shift, a.s_enc, b.codes, b.ld_codes, b.scales,
                            b.ld_scales, b.scale_row_shift, b.s_enc, M, N, K, c, ldc);
 }
