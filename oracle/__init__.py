@@ -48,9 +48,9 @@ def lib():
         i64 = ctypes.c_int64
         u64 = ctypes.c_uint64
         u32 = ctypes.c_uint32
-        L.orc_quantize.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int, u64, P, P, P, P, P]
+        L.orc_quantize.argtypes = [P, i64, i64, ctypes.c_int, ctypes.c_int, u64, u64, P, P, P, P, P]
         L.orc_quantize.restype = ctypes.c_int
-        L.orc_rht_quantize.argtypes = [P, i64, i64, u32, ctypes.c_int, u64, P, P, P, P, P]
+        L.orc_rht_quantize.argtypes = [P, i64, i64, u32, ctypes.c_int, u64, u64, P, P, P, P, P]
         L.orc_rht_quantize.restype = ctypes.c_int
         L.orc_rht_transform.argtypes = [P, i64, i64, u32, P]
         L.orc_rht_transform.restype = ctypes.c_int
@@ -182,8 +182,13 @@ class QTensor:
         self.block = block
 
 
-def quantize(x_u16, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None):
-    """NVFP4-quantise a row-major bf16 matrix given as uint16 bits."""
+def quantize(x_u16, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None, idx0=0):
+    """NVFP4-quantise a row-major bf16 matrix given as uint16 bits.
+
+    idx0 offsets the stochastic-rounding draw index: rows r0.. of a larger
+    tensor, quantised with its amax and idx0 = r0 * cols, give exactly those
+    rows of the whole tensor's result.
+    """
     x = _u16(x_u16)
     rows, cols = x.shape
     codes = np.zeros((rows, cols // 2), np.uint8)
@@ -192,15 +197,19 @@ def quantize(x_u16, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None):
     amax = np.zeros(1, np.float32)
     s_enc = np.zeros(1, np.float32)
     ain = None if amax_in is None else np.array([amax_in], np.float32)
-    rc = lib().orc_quantize(_ptr(x), rows, cols, block, rounding, seed, _ptr(ain), _ptr(codes),
+    rc = lib().orc_quantize(_ptr(x), rows, cols, block, rounding, seed, idx0, _ptr(ain), _ptr(codes),
                             _ptr(scales), _ptr(amax), _ptr(s_enc))
     if rc != 0:
         raise ValueError(f"orc_quantize: status {rc}")
     return QTensor(codes, scales, float(amax[0]), float(s_enc[0]), rows, cols, block)
 
 
-def rht_quantize(x_u16, sign_mask, rounding=RNE, seed=0, amax_in=None):
-    """Wgrad operand: RHT along tokens, transpose to channels x tokens, 1x16 quantise."""
+def rht_quantize(x_u16, sign_mask, rounding=RNE, seed=0, amax_in=None, idx0=0):
+    """Wgrad operand: RHT along tokens, transpose to channels x tokens, 1x16 quantise.
+
+    idx0 offsets the stochastic-rounding draw index (channels c0.. of a larger
+    tensor: idx0 = c0 * tokens, with that tensor's transformed amax).
+    """
     x = _u16(x_u16)
     tokens, channels = x.shape
     codes = np.zeros((channels, tokens // 2), np.uint8)
@@ -208,7 +217,7 @@ def rht_quantize(x_u16, sign_mask, rounding=RNE, seed=0, amax_in=None):
     amax = np.zeros(1, np.float32)
     s_enc = np.zeros(1, np.float32)
     ain = None if amax_in is None else np.array([amax_in], np.float32)
-    rc = lib().orc_rht_quantize(_ptr(x), tokens, channels, sign_mask, rounding, seed, _ptr(ain),
+    rc = lib().orc_rht_quantize(_ptr(x), tokens, channels, sign_mask, rounding, seed, idx0, _ptr(ain),
                                 _ptr(codes), _ptr(scales), _ptr(amax), _ptr(s_enc))
     if rc != 0:
         raise ValueError(f"orc_rht_quantize: status {rc}")
@@ -224,6 +233,31 @@ def rht_transform(x_u16, sign_mask):
     if rc != 0:
         raise ValueError(f"orc_rht_transform: status {rc}")
     return out
+
+
+def amax(x_u16, rows_per_chunk=4096):
+    """Tensor amax max |x| of a bf16 matrix (the input of the FP32 tensor
+    scale, Technische Zusammenfassung 2.A), a slice of rows at a time."""
+    x = np.atleast_2d(_u16(x_u16))
+    m = 0.0
+    for r0 in range(0, x.shape[0], rows_per_chunk):
+        v = bf16_bits_to_f64(x[r0:r0 + rows_per_chunk])
+        if v.size:
+            m = max(m, float(np.abs(v).max()))
+    return m
+
+
+def rht_amax(x_u16, sign_mask, channels_per_chunk=1024):
+    """max |RHT(x)| over the whole tokens x channels matrix, evaluated a slice
+    of channels at a time (the transform acts on each channel separately)."""
+    x = _u16(x_u16)
+    tokens, channels = x.shape
+    m = 0.0
+    for c0 in range(0, channels, channels_per_chunk):
+        t = rht_transform(np.ascontiguousarray(x[:, c0:c0 + channels_per_chunk]), sign_mask)
+        if t.size:
+            m = max(m, float(np.abs(t).max()))
+    return m
 
 
 # ---------------------------------------------------------------------------
@@ -321,11 +355,29 @@ def gemm_fp32_blocks(a: QTensor, b: QTensor):
     return c
 
 
-def bf16_gemm(a_u16, b_u16, nt=True):
-    """fp64 reference of a plain bf16 GEMM: a (M x K) times b^T (N x K) if nt."""
+def bf16_gemm(pass_, a_u16, b_u16, rows=None):
+    """fp64 GEMM of a linear layer kept in bf16 (Technische Zusammenfassung
+    2.B.1: some layers stay BF16; passes as in 2.B.2).  Plain definition of
+    each pass over the exact values of the bf16 operands:
+
+    FPROP: a = X (M x K), b = W (N x K):   Y  = X W^T     (M x N)
+    DGRAD: a = dY (M x N), b = W (N x K):  dX = dY W      (M x K)
+    WGRAD: a = dY (M x N), b = X (M x K):  dW = dY^T X    (N x K)
+    rows: optional index array of output rows to compute (sampled parity).
+    Returns float64.
+    """
     A = bf16_bits_to_f64(a_u16)
     B = bf16_bits_to_f64(b_u16)
-    return A @ B.T if nt else A @ B
+    if pass_ == FPROP:
+        A = A if rows is None else A[np.asarray(rows)]
+        return A @ B.T
+    if pass_ == DGRAD:
+        A = A if rows is None else A[np.asarray(rows)]
+        return A @ B
+    if pass_ == WGRAD:
+        At = A.T if rows is None else A.T[np.asarray(rows)]
+        return At @ B
+    raise ValueError(f"unknown pass {pass_}")
 
 
 def bf16_bits_to_f64(u16):

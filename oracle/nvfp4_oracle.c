@@ -278,10 +278,13 @@ static void put_code(uint8_t* row, int64_t col, uint8_t code)
  *   rounding      : RNE or SR ([P1] TZ 2.B.4).
  * codes: rows x cols/2 bytes, element (r, c) in byte r*cols/2 + c/2, even c
  * in the low nibble.  amax_in, if not NULL, replaces the computed amax.
+ * idx0 is added to every SR draw index (r*cols + c): a slice of rows of a
+ * larger tensor, quantised with that tensor's amax and idx0 = its first row
+ * times cols, gets exactly the codes of those rows in the whole tensor.
  */
 int orc_quantize(const uint16_t* x, int64_t rows, int64_t cols, int block, int rounding,
-                 uint64_t seed, const float* amax_in, uint8_t* codes, uint8_t* scales,
-                 float* amax_out, float* s_enc_out)
+                 uint64_t seed, uint64_t idx0, const float* amax_in, uint8_t* codes,
+                 uint8_t* scales, float* amax_out, float* s_enc_out)
 {
     if (rows < 0 || cols < 0 || cols % 16 != 0) return ORC_ERR_SHAPE;
     if (block == ORC_BLOCK_16X16 && rows % 16 != 0) return ORC_ERR_SHAPE;
@@ -341,7 +344,7 @@ int orc_quantize(const uint16_t* x, int64_t rows, int64_t cols, int block, int r
             float y = bf16_to_f32(x[r * cols + c]) * f;
             uint8_t code = (rounding == ORC_RNE)
                                ? orc_e2m1_encode_rne(y)
-                               : orc_e2m1_encode_sr(y, orc_sr_draw(seed, (uint64_t)(r * cols + c)));
+                               : orc_e2m1_encode_sr(y, orc_sr_draw(seed, idx0 + (uint64_t)(r * cols + c)));
             put_code(crow, c, code);
         }
     }
@@ -398,10 +401,12 @@ int orc_rht_transform(const uint16_t* x, int64_t tokens, int64_t channels, uint3
  * the weight-gradient GEMM).  The tensor amax is taken over the transformed
  * values (reading).  SR draws use the index c*tokens + t of the transposed
  * layout.  codes: channels x tokens/2; scales: channels x tokens/16.
+ * idx0 is added to every SR draw index, as in orc_quantize (for a slice of
+ * channels: its first channel times tokens).
  */
 int orc_rht_quantize(const uint16_t* x, int64_t tokens, int64_t channels, uint32_t sign_mask,
-                     int rounding, uint64_t seed, const float* amax_in, uint8_t* codes,
-                     uint8_t* scales, float* amax_out, float* s_enc_out)
+                     int rounding, uint64_t seed, uint64_t idx0, const float* amax_in,
+                     uint8_t* codes, uint8_t* scales, float* amax_out, float* s_enc_out)
 {
     if (tokens < 0 || channels < 0 || tokens % 16 != 0) return ORC_ERR_SHAPE;
     if (rounding != ORC_RNE && rounding != ORC_SR) return ORC_ERR_MODE;
@@ -443,7 +448,7 @@ int orc_rht_quantize(const uint16_t* x, int64_t tokens, int64_t channels, uint32
                 int64_t t = 16 * j + i;
                 uint8_t code = (rounding == ORC_RNE)
                                    ? orc_e2m1_encode_rne(y)
-                                   : orc_e2m1_encode_sr(y, orc_sr_draw(seed, (uint64_t)(c * tokens + t)));
+                                   : orc_e2m1_encode_sr(y, orc_sr_draw(seed, idx0 + (uint64_t)(c * tokens + t)));
                 put_code(codes + c * (tokens / 2), t, code);
             }
         }

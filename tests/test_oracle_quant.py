@@ -193,3 +193,57 @@ def test_nvfp4_error_below_mxfp4_style_scaling():
     codes = oracle.e2m1_encode_rne((blk / sc).astype(np.float32))
     mse_mx = np.mean((oracle.E2M1_VALUES[codes] * sc - blk) ** 2)
     assert mse_nv < mse_mx
+
+
+# --- slices of a larger tensor (sampled parity at full sizes) ---------------
+
+def test_amax_helpers_match_quantisers():
+    # the stand-alone maxima equal the ones the quantisers take themselves
+    rng = np.random.default_rng(21)
+    x = wl.lognormal_rows(rng, (48, 64))
+    x[5, 7] = wl.f32_to_bf16_bits(np.array([-123.0], np.float32))[0]   # largest is negative
+    assert oracle.amax(x) == oracle.quantize(x).amax == 123.0
+    assert oracle.amax(x, rows_per_chunk=7) == 123.0
+    mask = oracle.rht_sign_mask(4)
+    want = oracle.rht_quantize(x, mask).amax
+    assert oracle.rht_amax(x, mask) == want
+    assert oracle.rht_amax(x, mask, channels_per_chunk=5) == want
+    assert oracle.amax(np.zeros((0, 16), np.uint16)) == 0.0
+
+
+def test_row_slices_with_index_offset_match_whole_tensor():
+    # SR draws are indexed by the element's place in the whole tensor: a row
+    # slice quantised with idx0 = r0 * cols and the whole tensor's amax gives
+    # the same codes and scales as those rows of the whole result.
+    rng = np.random.default_rng(22)
+    rows, cols = 40, 96
+    x = wl.lognormal_rows(rng, (rows, cols))
+    full = oracle.quantize(x, rounding=oracle.SR, seed=77)
+    for r0, r1 in [(0, 3), (17, 18), (33, 40)]:
+        part = oracle.quantize(x[r0:r1], rounding=oracle.SR, seed=77, amax_in=full.amax,
+                               idx0=r0 * cols)
+        np.testing.assert_array_equal(part.codes, full.codes[r0:r1])
+        np.testing.assert_array_equal(part.scales, full.scales[r0:r1])
+        assert part.s_enc == full.s_enc
+    # without the offset the draws differ (the slice is not the tensor's start)
+    off = oracle.quantize(x[17:18], rounding=oracle.SR, seed=77, amax_in=full.amax)
+    assert not np.array_equal(off.codes, full.codes[17:18])
+    # 16x16 tiles: a column slice of whole tiles is independent of the rest
+    w = wl.normal(rng, (32, 96), 0.02)
+    fw = oracle.quantize(w, oracle.BLOCK_16X16)
+    pw = oracle.quantize(np.ascontiguousarray(w[:, 32:64]), oracle.BLOCK_16X16, amax_in=fw.amax)
+    np.testing.assert_array_equal(pw.codes, fw.codes[:, 16:32])
+    np.testing.assert_array_equal(pw.scales, fw.scales[:, 2:4])
+
+
+def test_channel_slices_with_index_offset_match_whole_rht_operand():
+    rng = np.random.default_rng(23)
+    tokens, channels = 64, 40
+    x = wl.lognormal_rows(rng, (tokens, channels))
+    mask = oracle.rht_sign_mask(9)
+    full = oracle.rht_quantize(x, mask, oracle.SR, 5)
+    for c0, c1 in [(0, 2), (13, 14), (37, 40)]:
+        part = oracle.rht_quantize(np.ascontiguousarray(x[:, c0:c1]), mask, oracle.SR, 5,
+                                   amax_in=full.amax, idx0=c0 * tokens)
+        np.testing.assert_array_equal(part.codes, full.codes[c0:c1])
+        np.testing.assert_array_equal(part.scales, full.scales[c0:c1])

@@ -166,3 +166,70 @@ def test_gemm_sampled_rows_match_full():
     full = oracle.gemm(oracle.FPROP, a, b)
     rows = np.array([0, 7, 39])
     np.testing.assert_array_equal(oracle.gemm(oracle.FPROP, a, b, rows=rows), full[rows])
+
+
+# --- bf16 GEMM of the layers kept in high precision (Technische
+# Zusammenfassung 2.B.1; passes of 2.B.2) ------------------------------------
+
+def test_bf16_bits_decode_closed_forms():
+    cases = {0x3F80: 1.0, 0xBF80: -1.0, 0x4049: 3.140625, 0x0001: 2.0 ** -133,
+             0x0080: 2.0 ** -126, 0x7F7F: (2 - 2.0 ** -7) * 2.0 ** 127, 0x0000: 0.0,
+             0xC2F7: -123.5}
+    bits = np.array(list(cases), dtype=np.uint16)
+    got = oracle.bf16_bits_to_f64(bits)
+    np.testing.assert_array_equal(got, np.array(list(cases.values())))
+    assert np.signbit(oracle.bf16_bits_to_f64(np.array([0x8000], dtype=np.uint16)))[0]
+
+
+def test_bf16_bits_decode_matches_torch():
+    # torch's own bfloat16 -> float64 conversion on every finite bit pattern
+    import torch
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    finite = ((bits >> 7) & 0xFF) != 0xFF
+    bits = bits[finite]
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    np.testing.assert_array_equal(oracle.bf16_bits_to_f64(bits), ref)
+
+
+def _bf16_value(u):
+    s, mag = ex.bf16_bits_to_fraction(int(u))
+    return -mag if s else mag
+
+
+@pytest.mark.parametrize("pass_", [oracle.FPROP, oracle.DGRAD, oracle.WGRAD])
+def test_bf16_gemm_passes_brute_force(pass_):
+    # Each pass written out with explicit indices over exact rationals: a
+    # transposed operand or a swapped pass would fail here.
+    rng = np.random.default_rng(10 + pass_)
+    M, N, K = 3, 5, 4
+    x = wl.normal(rng, (M, K), 1.0)
+    w = wl.normal(rng, (N, K), 0.02)
+    dy = wl.lognormal_rows(rng, (M, N))
+    X = [[_bf16_value(v) for v in r] for r in x]
+    W = [[_bf16_value(v) for v in r] for r in w]
+    DY = [[_bf16_value(v) for v in r] for r in dy]
+    if pass_ == oracle.FPROP:
+        got = oracle.bf16_gemm(pass_, x, w)
+        ref = [[sum(X[m][k] * W[n][k] for k in range(K)) for n in range(N)] for m in range(M)]
+    elif pass_ == oracle.DGRAD:
+        got = oracle.bf16_gemm(pass_, dy, w)
+        ref = [[sum(DY[m][n] * W[n][k] for n in range(N)) for k in range(K)] for m in range(M)]
+    else:
+        got = oracle.bf16_gemm(pass_, dy, x)
+        ref = [[sum(DY[m][n] * X[m][k] for m in range(M)) for k in range(K)] for n in range(N)]
+    ref = np.array([[float(v) for v in r] for r in ref])
+    assert got.shape == ref.shape
+    np.testing.assert_allclose(got, ref, rtol=1e-14, atol=0)
+
+
+@pytest.mark.parametrize("pass_", [oracle.FPROP, oracle.DGRAD, oracle.WGRAD])
+def test_bf16_gemm_sampled_rows_match_full(pass_):
+    rng = np.random.default_rng(11)
+    M, N, K = 24, 16, 40
+    x = wl.normal(rng, (M, K), 1.0)
+    w = wl.normal(rng, (N, K), 0.02)
+    dy = wl.normal(rng, (M, N), 1.0)
+    a, b = {oracle.FPROP: (x, w), oracle.DGRAD: (dy, w), oracle.WGRAD: (dy, x)}[pass_]
+    full = oracle.bf16_gemm(pass_, a, b)
+    rows = np.array([0, 3, full.shape[0] - 1])
+    np.testing.assert_array_equal(oracle.bf16_gemm(pass_, a, b, rows=rows), full[rows])
