@@ -23,6 +23,11 @@ times come from separate serialised passes with HIP events on the stream
 the library launches on.  The roofline entry is for the dominant kernel, the
 bf16-output GEMM (fprop and dgrad launches).  The CPU baseline is the
 oracle run on a token slice of the same step.
+
+--workload mlp times the 4-block MLP training step instead (tokens 16384,
+hidden 5120, FFN 20480; 8 linear layers, the last block's two in bf16; all
+fprops, then the backward pass in reverse layer order), value = its 24
+GEMMs' FLOPs / step time.  It is a separate line, not the default.
 """
 import argparse
 import hashlib
@@ -76,78 +81,6 @@ def make_inputs(dev):
     return data, out
 
 
-class Step:
-    """Buffers and launch sequence of one step (no allocation inside run()).
-
-    dgrad and wgrad only depend on the quantised dY, W and X, so wgrad's
-    operands are quantised and its GEMM runs on a second stream, concurrently
-    with dgrad: each GEMM's last, partial wave of workgroups is filled by the
-    other's (dgrad is 2.5 and wgrad 6.25 waves of 256 tiles on 256 CUs).
-    """
-
-    def __init__(self, q, torch, dev, x, w, dy):
-        self.q, self.torch = q, torch
-        self.x, self.w, self.dy = x, w, dy
-        self.gx = q.alloc_nvfp4(M, K, q.BLOCK_1X16)
-        self.gw = q.alloc_nvfp4(N, K, q.BLOCK_16X16, with_transpose=True)
-        self.gdy = q.alloc_nvfp4(M, N, q.BLOCK_1X16)
-        self.gdyt = q.alloc_nvfp4(N, M, q.BLOCK_1X16)
-        self.gxt = q.alloc_nvfp4(K, M, q.BLOCK_1X16)
-        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-        self.dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-        self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
-        self.mask = q.nvfp4_rht_sign_mask(SEED + 1000)
-        f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
-        self.ax, self.ax_rht, self.ady, self.ady_rht = f32(), f32(), f32(), f32()
-        self.side = torch.cuda.Stream(device=dev)  # default priority
-        self.ops = ["amax_X", "quant_X", "quant_W", "fprop", "amax_dY", "quant_dY", "dgrad",
-                    "rht_dY", "rht_X", "wgrad"]
-
-    def calls(self):
-        q = self.q
-        # X and dY are each quantised twice (1x16, and through the RHT for
-        # wgrad): one fused pass computes both tensor maxima of each.
-        return [
-            lambda: q.nvfp4_amax(self.x, self.mask, self.ax, self.ax_rht),
-            lambda: q.nvfp4_quantize(self.x, q.BLOCK_1X16, q.RNE, amax_in=self.ax, out=self.gx),
-            lambda: q.nvfp4_quantize(self.w, q.BLOCK_16X16, q.RNE, out=self.gw),
-            lambda: q.nvfp4_gemm(q.FPROP, self.gx, self.gw, out=self.y),
-            lambda: q.nvfp4_amax(self.dy, self.mask, self.ady, self.ady_rht),
-            lambda: q.nvfp4_quantize(self.dy, q.BLOCK_1X16, q.SR, SEED + 100, amax_in=self.ady,
-                                     out=self.gdy),
-            lambda: q.nvfp4_gemm(q.DGRAD, self.gdy, self.gw, out=self.dx),
-            lambda: q.nvfp4_rht_quantize(self.dy, self.mask, q.SR, SEED + 101,
-                                         amax_in=self.ady_rht, out=self.gdyt),
-            lambda: q.nvfp4_rht_quantize(self.x, self.mask, q.RNE, amax_in=self.ax_rht,
-                                         out=self.gxt),
-            lambda: q.nvfp4_gemm(q.WGRAD, self.gdyt, self.gxt, out=self.dw),
-        ]
-
-    def run(self):
-        """One step: wgrad's branch on the side stream, joined at the end."""
-        torch = self.torch
-        c = self.calls()
-        main = torch.cuda.current_stream()
-        for f in c[:6]:          # quantise X, W; fprop; amax and 1x16 SR of dY
-            f()
-        self.side.wait_stream(main)
-        c[6]()                   # dgrad on the main stream
-        with torch.cuda.stream(self.side):
-            c[7](); c[8](); c[9]()   # RHT operands and wgrad on the side stream
-        main.wait_stream(self.side)
-
-    def run_timed_ops(self):
-        """One step, serialised on one stream, with an event around every
-        operation (for per-operation times; events add small gaps)."""
-        torch = self.torch
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(self.ops) + 1)]
-        ev[0].record()
-        for i, f in enumerate(self.calls()):
-            f()
-            ev[i + 1].record()
-        return ev
-
-
 def quant_bytes():
     """Algorithmic HBM bytes of each quantisation operation: the fused amax
     passes read their tensor once; the encode passes read it and write codes
@@ -190,11 +123,42 @@ def cpu_baseline(data, tokens=M):
             "seconds": t}
 
 
+def build_layer_step(q, torch, dev):
+    """The 12B-layer step: one NVFP4 linear layer, numpy-drawn inputs."""
+    from quantize_precision_gemm_amd.step import NVFP4Linear, TrainingStep
+    data, t = make_inputs(dev)
+    layer = NVFP4Linear(q, torch, t["X"], t["W"], t["dY"], SEED)
+    return data, TrainingStep(torch, [layer], dev)
+
+
+def build_mlp_step(q, torch, dev):
+    """The 4-block MLP step: 8 linear layers (3 NVFP4 blocks, the last block
+    in bf16), each with its own inputs drawn on the GPU."""
+    from quantize_precision_gemm_amd import workloads as wl
+    from quantize_precision_gemm_amd.step import BF16Linear, NVFP4Linear, TrainingStep
+    t0 = time.time()
+    shapes = wl.mlp_layers()
+    layers = []
+    for i, sh in enumerate(shapes):
+        seed = wl.layer_seed(wl.MLP_SEED, i)
+        d = wl.layer_inputs_device(torch, dev, sh, seed)
+        cls = BF16Linear if i >= len(shapes) - 2 else NVFP4Linear
+        layers.append(cls(q, torch, d["X"], d["W"], d["dY"], seed))
+    torch.cuda.synchronize()
+    print(f"# MLP inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
+    return TrainingStep(torch, layers, dev)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 20 for the layer, 5 for the MLP step)")
+    ap.add_argument("--warmup", type=int, default=None,
+                    help="untimed warm-up steps (default 3 for the layer, 2 for the MLP step)")
+    ap.add_argument("--workload", choices=["layer", "mlp"], default="layer",
+                    help="layer: one 12B-style linear layer (the default bench line); "
+                         "mlp: the 4-block MLP training step at 16384 tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
@@ -202,6 +166,9 @@ def main():
               "(the layer shards by tokens; see the design notes). Run with --gpus 1.",
               file=sys.stderr)
         sys.exit(2)
+    mlp = args.workload == "mlp"
+    steps = args.steps if args.steps is not None else (5 if mlp else 20)
+    warmup = args.warmup if args.warmup is not None else (2 if mlp else 3)
 
     import torch
     import quantize_precision_gemm_amd as q
@@ -209,70 +176,101 @@ def main():
     q.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    data, t = make_inputs(dev)
-    step = Step(q, torch, dev, t["X"], t["W"], t["dY"])
+    if mlp:
+        data, step = None, build_mlp_step(q, torch, dev)
+    else:
+        data, step = build_layer_step(q, torch, dev)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step.run()
     torch.cuda.synchronize()
 
     # timed steps: nothing but the step itself between the two synchronisations
     t0 = time.perf_counter()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step.run()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
     # per-operation times: separate, serialised passes with events
-    per_op = {k: [] for k in step.ops}
-    evs = [step.run_timed_ops() for _ in range(max(5, args.steps // 2))]
-    torch.cuda.synchronize()
-    for ev in evs:
-        for i, k in enumerate(step.ops):
-            per_op[k].append(ev[i].elapsed_time(ev[i + 1]))
+    times = {}
+    for _ in range(max(3, steps // 2)):
+        ops, ev = step.run_timed_ops()
+        torch.cuda.synchronize()
+        for j, (i, name, _) in enumerate(ops):
+            times.setdefault((i, name), []).append(ev[j].elapsed_time(ev[j + 1]))
+    avg_op = {k: sum(v) / len(v) for k, v in times.items()}
+    by_name = {}
+    for (i, name), v in avg_op.items():
+        by_name.setdefault(name, []).append(v)
 
-    ms_step = wall * 1e3 / args.steps
-    gemm_flop = 2.0 * M * N * K
-    avg = {k: sum(v) / len(v) for k, v in per_op.items()}
-    qb = quant_bytes()
-    bf16_launches = per_op["fprop"] + per_op["dgrad"]
-    gemm_bf16_ms = sum(bf16_launches) / len(bf16_launches)
+    ms_step = wall * 1e3 / steps
+    layer0 = step.layers[0]
+    gemm_flop = 2.0 * layer0.M * layer0.N * layer0.K   # equal for every layer here
+    mean = lambda v: sum(v) / len(v)
+    nv_launches = [t for k in ("fprop", "dgrad") for t in
+                   sum((times[key] for key in times if key[1] == k), [])]
+    gemm_bf16_ms = mean(nv_launches)
     achieved = gemm_flop / (gemm_bf16_ms * 1e-3) / 1e12
 
     result = {
         "metric": "NVFP4 GEMM TFLOP/s (fprop/dgrad/wgrad) + quantize GB/s, 12B-layer shapes",
-        "value": round(3 * gemm_flop / (ms_step * 1e-3) / 1e12, 2),
+        "value": round(step.flops() / (ms_step * 1e-3) / 1e12, 2),
         "unit": "TFLOP/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
-        "config": {"workload": "12B-style MLP up-projection linear layer, one training step "
-                               "(fprop + dgrad + wgrad, all NVFP4 quantisations included)",
-                   "tokens_M": M, "in_K": K, "out_N": N, "operand_format": "nvfp4",
-                   "mfma": "f16 32x32x16, fp32 accumulate", "parallelism": "none (1 GPU)"},
-        "gemm_tflops": {p: round(gemm_flop / (avg[p] * 1e-3) / 1e12, 1)
-                        for p in ("fprop", "dgrad", "wgrad")},
-        "quantize_gbps": {k: round(qb[k] / (avg[k] * 1e-3) / 1e9, 1) for k in qb},
-        "quantize_frac_of_hbm_peak": {k: round(qb[k] / (avg[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3)
-                                      for k in qb},
-        "ms_per_op": {k: round(v, 4) for k, v in avg.items()},
-        "roofline": {"kernel": "k_gemm_nt<bf16 out> (fprop, dgrad launches)", "bound": "mfma",
-                     "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(achieved / PEAK_F16_TFLOPS, 4),
-                     "avg_launch_ms": round(gemm_bf16_ms, 4),
-                     "traffic": counter_traffic(gemm_bf16_ms)},
-        "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
+    gemm_names = [n for n in ("fprop", "dgrad", "wgrad", "bf16_fprop", "bf16_dgrad", "bf16_wgrad")
+                  if n in by_name]
+    result["gemm_tflops"] = {n: round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12, 1)
+                             for n in gemm_names}
+    if mlp:
+        result["config"] = {
+            "workload": "4-block MLP training step (per block an up- and a down-projection "
+                        "linear layer; fprop + dgrad + wgrad of all 8; blocks 1-3 NVFP4 with "
+                        "all quantisations, block 4 bf16)",
+            "tokens_M": wl_mlp("MLP_TOKENS"), "hidden": wl_mlp("MLP_HIDDEN"),
+            "ffn": wl_mlp("MLP_FFN"), "blocks": wl_mlp("MLP_BLOCKS"),
+            "activations": "Student-t(3), unit variance", "seed": wl_mlp("MLP_SEED"),
+            "operand_format": "nvfp4 (6 layers), bf16 (2 layers)",
+            "mfma": "f16 (nvfp4 decoded) and bf16 32x32x16, fp32 accumulate",
+            "parallelism": "none (1 GPU)"}
+        result["dtype"] = "f16+bf16"
+        result["ms_per_op_total"] = {n: round(sum(v), 4) for n, v in by_name.items()}
+    else:
+        result["config"] = {
+            "workload": "12B-style MLP up-projection linear layer, one training step "
+                        "(fprop + dgrad + wgrad, all NVFP4 quantisations included)",
+            "tokens_M": M, "in_K": K, "out_N": N, "operand_format": "nvfp4",
+            "mfma": "f16 32x32x16, fp32 accumulate", "parallelism": "none (1 GPU)"}
+        qb = quant_bytes()
+        avg = {n: mean(v) for n, v in by_name.items()}
+        result["quantize_gbps"] = {k: round(qb[k] / (avg[k] * 1e-3) / 1e9, 1) for k in qb}
+        result["quantize_frac_of_hbm_peak"] = {
+            k: round(qb[k] / (avg[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3) for k in qb}
+        result["ms_per_op"] = {k: round(v, 4) for k, v in avg.items()}
+    result["roofline"] = {
+        "kernel": "k_gemm_nt<Nvfp4Src, bf16 out> (fprop, dgrad launches)", "bound": "mfma",
+        "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
+        "frac": round(achieved / PEAK_F16_TFLOPS, 4), "avg_launch_ms": round(gemm_bf16_ms, 4),
+        "traffic": None if mlp else counter_traffic(gemm_bf16_ms)}
+    result["cpu_baseline"] = None
+    if not args.no_cpu_baseline and not mlp:
         print("# timing the CPU oracle on a token slice", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(data)
     print(json.dumps(result), flush=True)
+
+
+def wl_mlp(name):
+    from quantize_precision_gemm_amd import workloads as wl
+    return getattr(wl, name)
 
 
 if __name__ == "__main__":

@@ -211,6 +211,31 @@ uint32_t nvfp4_rht_sign_mask(uint64_t seed);
 int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
                int64_t ldc, int32_t c_dtype, void* stream);
 
+/*
+ * nvfp4_bf16_gemm -- the three GEMMs of a linear layer that stays in BF16
+ * (no quantisation); bf16 products accumulated in fp32.
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.B.1 (mixed precision: the most sensitive linear layers,
+ * the last blocks of the network among them, keep BF16) with the passes of
+ * 2.B.2.  M = tokens, K = input features, N = output features; every
+ * operand is a row-major bf16 matrix as the layer holds it, and the kernel
+ * reads W, X and dY in place (no transposed copies):
+ *   FPROP: a = X  (M x K, lda), b = W (N x K, ldb)
+ *          c[m, n] = sum_k x[m,k] * w[n,k]                     (M x N)
+ *   DGRAD: a = dY (M x N, lda), b = W (N x K, ldb)
+ *          c[m, k] = sum_n dy[m,n] * w[n,k]                    (M x K)
+ *   WGRAD: a = dY (M x N, lda), b = X (M x K, ldb)
+ *          c[n, k] = sum_m dy[m,n] * x[m,k]                    (N x K)
+ *   M, N, K   >= 0 and multiples of 8.
+ *   a, b      device bf16, 16-byte aligned; lda, ldb (elements) multiples
+ *             of 8 and at least the row length of the operand.
+ *   c, ldc, c_dtype  as for nvfp4_gemm (the output has no alpha: 1).
+ * Returns NVFP4_OK or a negative status; nothing is enqueued on failure.
+ */
+int nvfp4_bf16_gemm(int32_t pass, const void* a, int64_t lda, const void* b, int64_t ldb,
+                    int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, int32_t c_dtype,
+                    void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* nvfp4_status_string(int32_t status);
 

@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm",
-    "nvfp4_rht_sign_mask", "nvfp4_amax", "lib_path", "load_library",
+    "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "lib_path", "load_library",
 ]
 
 BLOCK_1X16 = 0
@@ -75,6 +75,8 @@ def load_library():
         L.nvfp4_gemm.restype = ctypes.c_int
         L.nvfp4_amax.argtypes = [P, i64, i64, i64, u32, P, P, P]
         L.nvfp4_amax.restype = ctypes.c_int
+        L.nvfp4_bf16_gemm.argtypes = [i32, P, i64, P, i64, i64, i64, i64, P, i64, i32, P]
+        L.nvfp4_bf16_gemm.restype = ctypes.c_int
         L.nvfp4_rht_sign_mask.argtypes = [u64]
         L.nvfp4_rht_sign_mask.restype = u32
         L.nvfp4_status_string.argtypes = [i32]
@@ -212,6 +214,39 @@ def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None):
     st = load_library().nvfp4_gemm(pass_, ctypes.byref(da), ctypes.byref(db), _ptr(out),
                                    out.stride(0), dt, _stream(stream))
     _check(st, "nvfp4_gemm")
+    return out
+
+
+def nvfp4_bf16_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None):
+    """GEMM of a linear layer kept in bf16 (see nvfp4_bf16_gemm in nvfp4.h).
+
+    FPROP: a = X (M x K), b = W (N x K) -> M x N
+    DGRAD: a = dY (M x N), b = W (N x K) -> M x K
+    WGRAD: a = dY (M x N), b = X (M x K) -> N x K
+    """
+    _check_bf16(a)
+    _check_bf16(b)
+    if pass_ == FPROP:
+        (M, K), N = a.shape, b.shape[0]
+        shape = (M, N)
+    elif pass_ == DGRAD:
+        (M, N), K = a.shape, b.shape[1]
+        shape = (M, K)
+    elif pass_ == WGRAD:
+        (M, N), K = a.shape, b.shape[1]
+        shape = (N, K)
+    else:
+        raise ValueError(f"unknown pass {pass_}")
+    if out is None:
+        out = torch.empty(shape, dtype=out_dtype, device=a.device)
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
+        raise TypeError("output must be float32 or bfloat16 with a contiguous last dimension")
+    dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    def ld(t):  # a matrix without columns has no meaningful row stride
+        return t.stride(0) if t.shape[1] > 0 else 0
+    st = load_library().nvfp4_bf16_gemm(pass_, _ptr(a), ld(a), _ptr(b), ld(b), M, N, K,
+                                        _ptr(out), ld(out), dt, _stream(stream))
+    _check(st, "nvfp4_bf16_gemm")
     return out
 
 

@@ -221,6 +221,38 @@ int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void*
     return launch_status();
 }
 
+int nvfp4_bf16_gemm(int32_t pass, const void* a, int64_t lda, const void* b, int64_t ldb,
+                    int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, int32_t c_dtype,
+                    void* stream)
+{
+    if (pass != NVFP4_FPROP && pass != NVFP4_DGRAD && pass != NVFP4_WGRAD) return NVFP4_ERR_MODE;
+    if (c_dtype != NVFP4_OUT_BF16 && c_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_MODE;
+    if (M < 0 || N < 0 || K < 0 || M % 8 || N % 8 || K % 8) return NVFP4_ERR_SHAPE;
+    // rows x columns of a, b and c for the pass
+    const int64_t a_cols = pass == NVFP4_FPROP ? K : N;
+    const int64_t b_cols = K;
+    const int64_t a_rows = M, b_rows = pass == NVFP4_WGRAD ? M : N;
+    const int64_t c_rows = pass == NVFP4_WGRAD ? N : M;
+    const int64_t c_cols = pass == NVFP4_FPROP ? N : K;
+    if ((a_rows > 0 && a_cols > 0 && !a) || (b_rows > 0 && b_cols > 0 && !b)) return NVFP4_ERR_NULL;
+    if (c_rows > 0 && c_cols > 0 && !c) return NVFP4_ERR_NULL;
+    if (!aligned(a, 16) || !aligned(b, 16) || lda % 8 || ldb % 8) return NVFP4_ERR_ALIGN;
+    if (!aligned(c, c_dtype == NVFP4_OUT_FP32 ? 16 : 8) || ldc % 4 != 0) return NVFP4_ERR_ALIGN;
+    if (lda < a_cols || ldb < b_cols || ldc < c_cols) return NVFP4_ERR_SHAPE;
+
+    const uint16_t* A = static_cast<const uint16_t*>(a);
+    const uint16_t* B = static_cast<const uint16_t*>(b);
+    const bool f32 = c_dtype == NVFP4_OUT_FP32;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (pass == NVFP4_FPROP)  // rows of X and of W, both K-contiguous
+        nvfp4::launch_bf16_gemm(A, lda, false, B, ldb, false, M, N, K, c, ldc, f32, s);
+    else if (pass == NVFP4_DGRAD)  // rows of dY (N-contiguous); W read as N x K, k-contiguous
+        nvfp4::launch_bf16_gemm(A, lda, false, B, ldb, true, M, K, N, c, ldc, f32, s);
+    else  // both operands contracted over tokens, their rows contiguous
+        nvfp4::launch_bf16_gemm(A, lda, true, B, ldb, true, N, K, M, c, ldc, f32, s);
+    return launch_status();
+}
+
 const char* nvfp4_status_string(int32_t status)
 {
     switch (status) {

@@ -1,0 +1,186 @@
+"""Training step of linear layers through the library: buffers and launch order.
+
+A linear layer y = x W^T (tokens M, inputs K, outputs N) runs three GEMMs per
+training step ("Pretraining Large Language Models with NVFP4", gist.science
+summary, Technische Zusammenfassung 2.B.2): fprop Y = X W^T, dgrad
+dX = dY W and wgrad dW = dY^T X.  In an NVFP4 layer every GEMM input is
+quantised first, by role (2.A, 2.B.2-2.B.4):
+
+  X   1x16 blocks, round-to-nearest-even       (fprop)
+  W   16x16 blocks, RNE, plus the transposed copy dgrad reads
+  dY  1x16 blocks, stochastic rounding         (dgrad)
+  dY, X  16-point random Hadamard transform along tokens, transposed, 1x16;
+         SR for dY, RNE for X, one sign vector for both   (wgrad)
+
+A layer kept in BF16 (2.B.1) runs the same three GEMMs on the bf16 tensors.
+
+Every operation is a library call; this module only allocates buffers (once,
+in the constructors) and orders the launches.  Nothing here computes.
+"""
+
+SR_SEED_DY = 100       # seed offsets of a layer's stochastic-rounding calls
+SR_SEED_DY_RHT = 101
+RHT_SEED = 1000        # offset of the seed the layer's RHT sign vector is drawn from
+
+
+class NVFP4Linear:
+    """One linear layer's training step in NVFP4.
+
+    x (M x K), w (N x K), dy (M x N): bf16 device tensors, row-major.
+    Outputs: y (M x N, bf16), dx (M x K, bf16), dw (N x K, fp32).
+    """
+
+    def __init__(self, q, torch, x, w, dy, seed):
+        self.q, self.torch = q, torch
+        self.x, self.w, self.dy = x, w, dy
+        M, K = x.shape
+        N = w.shape[0]
+        assert w.shape == (N, K) and dy.shape == (M, N)
+        self.M, self.K, self.N = M, K, N
+        dev = x.device
+        self.seed = seed
+        self.gx = q.alloc_nvfp4(M, K, q.BLOCK_1X16, device=dev)
+        self.gw = q.alloc_nvfp4(N, K, q.BLOCK_16X16, with_transpose=True, device=dev)
+        self.gdy = q.alloc_nvfp4(M, N, q.BLOCK_1X16, device=dev)
+        self.gdyt = q.alloc_nvfp4(N, M, q.BLOCK_1X16, device=dev)
+        self.gxt = q.alloc_nvfp4(K, M, q.BLOCK_1X16, device=dev)
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+        self.mask = q.nvfp4_rht_sign_mask(seed + RHT_SEED)
+        f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
+        self.ax, self.ax_rht, self.ady, self.ady_rht = f32(), f32(), f32(), f32()
+
+    def flops(self):
+        return 3 * 2.0 * self.M * self.N * self.K
+
+    # X and dY are each quantised twice (1x16, and through the RHT for
+    # wgrad): one fused pass computes both tensor maxima of each.
+    def forward_ops(self):
+        q = self.q
+        return [
+            ("amax_X", lambda: q.nvfp4_amax(self.x, self.mask, self.ax, self.ax_rht)),
+            ("quant_X", lambda: q.nvfp4_quantize(self.x, q.BLOCK_1X16, q.RNE, amax_in=self.ax,
+                                                 out=self.gx)),
+            ("quant_W", lambda: q.nvfp4_quantize(self.w, q.BLOCK_16X16, q.RNE, out=self.gw)),
+            ("fprop", lambda: q.nvfp4_gemm(q.FPROP, self.gx, self.gw, out=self.y)),
+        ]
+
+    def backward_quant_ops(self):
+        q = self.q
+        return [
+            ("amax_dY", lambda: q.nvfp4_amax(self.dy, self.mask, self.ady, self.ady_rht)),
+            ("quant_dY", lambda: q.nvfp4_quantize(self.dy, q.BLOCK_1X16, q.SR,
+                                                  self.seed + SR_SEED_DY, amax_in=self.ady,
+                                                  out=self.gdy)),
+        ]
+
+    def dgrad_ops(self):
+        q = self.q
+        return [("dgrad", lambda: q.nvfp4_gemm(q.DGRAD, self.gdy, self.gw, out=self.dx))]
+
+    def wgrad_ops(self):
+        q = self.q
+        return [
+            ("rht_dY", lambda: q.nvfp4_rht_quantize(self.dy, self.mask, q.SR,
+                                                    self.seed + SR_SEED_DY_RHT,
+                                                    amax_in=self.ady_rht, out=self.gdyt)),
+            ("rht_X", lambda: q.nvfp4_rht_quantize(self.x, self.mask, q.RNE,
+                                                   amax_in=self.ax_rht, out=self.gxt)),
+            ("wgrad", lambda: q.nvfp4_gemm(q.WGRAD, self.gdyt, self.gxt, out=self.dw)),
+        ]
+
+
+class BF16Linear:
+    """One linear layer's training step kept in bf16: the three GEMMs on the
+    layer's own tensors, fp32 accumulation; outputs as NVFP4Linear's."""
+
+    def __init__(self, q, torch, x, w, dy, seed=None):
+        self.q, self.torch = q, torch
+        self.x, self.w, self.dy = x, w, dy
+        M, K = x.shape
+        N = w.shape[0]
+        assert w.shape == (N, K) and dy.shape == (M, N)
+        self.M, self.K, self.N = M, K, N
+        dev = x.device
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+
+    def flops(self):
+        return 3 * 2.0 * self.M * self.N * self.K
+
+    def forward_ops(self):
+        q = self.q
+        return [("bf16_fprop", lambda: q.nvfp4_bf16_gemm(q.FPROP, self.x, self.w, out=self.y))]
+
+    def backward_quant_ops(self):
+        return []
+
+    def dgrad_ops(self):
+        q = self.q
+        return [("bf16_dgrad", lambda: q.nvfp4_bf16_gemm(q.DGRAD, self.dy, self.w, out=self.dx))]
+
+    def wgrad_ops(self):
+        q = self.q
+        return [("bf16_wgrad", lambda: q.nvfp4_bf16_gemm(q.WGRAD, self.dy, self.x, out=self.dw))]
+
+
+class TrainingStep:
+    """Fprop of every layer in order, then the backward pass in reverse order.
+
+    Per layer in the backward pass, dY is quantised on the main stream; then
+    dgrad runs on the main stream while the wgrad branch (RHT operands and the
+    wgrad GEMM) runs on a second stream.  Wgrad feeds nothing later in the
+    step, so it overlaps with dgrad and with the next layer's backward work:
+    each GEMM's last, partial wave of workgroups is filled by the other's.
+    The step ends with the main stream waiting for the side stream.
+    """
+
+    def __init__(self, torch, layers, device):
+        self.torch = torch
+        self.layers = list(layers)
+        self.side = torch.cuda.Stream(device=device)  # default priority
+
+    def flops(self):
+        return sum(l.flops() for l in self.layers)
+
+    def run(self):
+        torch = self.torch
+        main = torch.cuda.current_stream()
+        for layer in self.layers:
+            for _, f in layer.forward_ops():
+                f()
+        for layer in reversed(self.layers):
+            for _, f in layer.backward_quant_ops():
+                f()
+            self.side.wait_stream(main)
+            for _, f in layer.dgrad_ops():
+                f()
+            with torch.cuda.stream(self.side):
+                for _, f in layer.wgrad_ops():
+                    f()
+        main.wait_stream(self.side)
+
+    def serial_ops(self):
+        """(layer index, name, call) of the whole step in one serial order."""
+        ops = []
+        for i, layer in enumerate(self.layers):
+            ops += [(i, n, f) for n, f in layer.forward_ops()]
+        for i in reversed(range(len(self.layers))):
+            layer = self.layers[i]
+            for part in (layer.backward_quant_ops(), layer.dgrad_ops(), layer.wgrad_ops()):
+                ops += [(i, n, f) for n, f in part]
+        return ops
+
+    def run_timed_ops(self):
+        """One step serialised on the current stream with an event after every
+        operation; returns (ops, events), events[0] before the first op."""
+        torch = self.torch
+        ops = self.serial_ops()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)]
+        ev[0].record()
+        for j, (_, _, f) in enumerate(ops):
+            f()
+            ev[j + 1].record()
+        return ops, ev

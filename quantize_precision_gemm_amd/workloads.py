@@ -19,6 +19,15 @@ fp32, then to bf16 with round-to-nearest-even):
                        g ~ N(0,1) per element (log-normal row magnitudes,
                        sigma = 2), which puts some rows' block scales into the
                        E4M3 subnormal and zero range.
+
+The 4-block MLP training step (tokens 16384 = batch 4 x sequence 4096, hidden
+5120, FFN 20480; blocks of an up- and a down-projection; the last block kept
+in BF16) draws its much larger inputs on the GPU with torch's seeded
+generator instead, same distributions, activations Student-t(3):
+  Student-t(df), integer df : Z / sqrt((Z_1^2 + ... + Z_df^2) / df), all
+                              standard normals, scaled to unit variance
+Each linear layer gets its own inputs (layer seed = seed + 4096 * index);
+the activations of one layer are not the output of the previous one.
 """
 from dataclasses import dataclass
 
@@ -98,6 +107,54 @@ def layer_inputs(shapes: LayerShapes, seed=0, act_df=4, with_x=True, with_w=True
         out["W"] = normal(rng, (shapes.N, shapes.K), 0.02)
     if with_dy:
         out["dY"] = lognormal_rows(rng, (shapes.M, shapes.N))
+    return out
+
+
+MLP_TOKENS = 16384
+MLP_HIDDEN = 5120
+MLP_FFN = 20480
+MLP_BLOCKS = 4
+MLP_SEED = 1
+
+
+def mlp_layers(tokens=MLP_TOKENS, hidden=MLP_HIDDEN, ffn=MLP_FFN, blocks=MLP_BLOCKS):
+    """Shapes of the linear layers of the MLP stack, in order: per block an
+    up-projection (hidden -> ffn) and a down-projection (ffn -> hidden)."""
+    out = []
+    for _ in range(blocks):
+        out.append(LayerShapes(tokens, hidden, ffn))
+        out.append(LayerShapes(tokens, ffn, hidden))
+    return out
+
+
+def layer_seed(base_seed: int, index: int) -> int:
+    return base_seed + 4096 * index
+
+
+def layer_inputs_device(torch, device, shapes: LayerShapes, seed, act_df=3):
+    """X (M x K, Student-t(act_df) at unit variance), W (N x K, N(0, 0.02)) and
+    dY (M x N, log-normal row magnitudes) as bf16 tensors on `device`, drawn
+    in that order from torch's generator seeded with `seed`."""
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+
+    def randn(shape):
+        return torch.randn(shape, generator=g, device=device, dtype=torch.float32)
+
+    M, K, N = shapes.M, shapes.K, shapes.N
+    z = randn((M, K))
+    chi2 = torch.zeros_like(z)
+    for _ in range(act_df):
+        e = randn((M, K))
+        chi2.addcmul_(e, e)
+        del e
+    x = (z / torch.sqrt(chi2 / act_df)) * ((act_df - 2.0) / act_df) ** 0.5
+    del z, chi2
+    out = {"X": x.to(torch.bfloat16)}
+    del x
+    out["W"] = (randn((N, K)) * 0.02).to(torch.bfloat16)
+    row = torch.exp(2.0 * randn((M, 1))) * 1e-3
+    out["dY"] = (row * randn((M, N))).to(torch.bfloat16)
     return out
 
 

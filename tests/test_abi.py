@@ -137,3 +137,21 @@ def test_amax_validation(lib):
     assert lib.nvfp4_amax(None, 16, 16, 16, 1, out, None, None) == -1     # null input
     assert lib.nvfp4_amax(FAKE + 8, 16, 16, 16, 1, out, None, None) == -3  # misaligned input
     assert lib.nvfp4_amax(FAKE, 16, 16, 8, 1, out, None, None) == -2      # ld < cols
+
+
+def test_bf16_gemm_validation(lib):
+    f = lib.nvfp4_bf16_gemm
+    # pass, a, lda, b, ldb, M, N, K, c, ldc, dtype
+    assert f(3, FAKE, 64, FAKE, 64, 16, 16, 64, FAKE, 64, 0, None) == -4      # unknown pass
+    assert f(0, FAKE, 64, FAKE, 64, 16, 16, 64, FAKE, 64, 2, None) == -4      # unknown dtype
+    assert f(0, FAKE, 64, FAKE, 64, 12, 16, 64, FAKE, 64, 0, None) == -2      # M % 8
+    assert f(0, FAKE, 64, FAKE, 64, 16, 16, 60, FAKE, 64, 0, None) == -2      # K % 8
+    assert f(0, FAKE, 64, FAKE, 64, -8, 16, 64, FAKE, 64, 0, None) == -2      # negative
+    assert f(0, None, 64, FAKE, 64, 16, 16, 64, FAKE, 64, 0, None) == -1      # null a
+    assert f(0, FAKE, 64, FAKE, 64, 16, 16, 64, None, 64, 0, None) == -1      # null c
+    assert f(0, FAKE + 8, 64, FAKE, 64, 16, 16, 64, FAKE, 64, 0, None) == -3  # misaligned a
+    assert f(0, FAKE, 60, FAKE, 64, 16, 16, 56, FAKE, 64, 0, None) == -3      # lda % 8
+    assert f(0, FAKE, 64, FAKE, 64, 16, 16, 64, FAKE + 8, 64, 1, None) == -3  # fp32 c alignment
+    assert f(0, FAKE, 56, FAKE, 64, 16, 16, 64, FAKE, 64, 0, None) == -2      # lda < K
+    assert f(1, FAKE, 8, FAKE, 64, 16, 16, 64, FAKE, 64, 0, None) == -2       # dgrad: lda < N
+    assert f(2, FAKE, 16, FAKE, 64, 16, 16, 64, FAKE, 8, 0, None) == -2       # wgrad: ldc < K

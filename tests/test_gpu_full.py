@@ -27,12 +27,11 @@ def full():
 
     dev = torch.device("cuda:0")
     print("generating full-size inputs", flush=True)
-    data, t = bench.make_inputs(dev)
-    step = bench.Step(q, torch, dev, t["X"], t["W"], t["dY"])
+    data, train = bench.build_layer_step(q, torch, dev)
     print("running one bench step", flush=True)
-    step.run()
+    train.run()
     torch.cuda.synchronize()
-    return torch, oracle, q, bench, data, step
+    return torch, oracle, q, bench, data, train.layers[0]
 
 
 def _rows(n, k=40, seed=0):
