@@ -235,7 +235,7 @@ def rht_transform(x_u16, sign_mask):
     return out
 
 
-def amax(x_u16, rows_per_chunk=4096):
+def amax(x_u16, rows_per_chunk=1024):
     """Tensor amax max |x| of a bf16 matrix (the input of the FP32 tensor
     scale, Technische Zusammenfassung 2.A), a slice of rows at a time."""
     x = np.atleast_2d(_u16(x_u16))
