@@ -160,6 +160,9 @@ def main():
                     help="layer: one 12B-style linear layer (the default bench line); "
                          "mlp: the 4-block MLP training step at 16384 tokens")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain elementwise copy of 1 GiB (bf16 negation, 3 launches): "
+                         "the reference that scales hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -176,6 +179,16 @@ def main():
     q.load_library()
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.calibrate_copy:
+        n = 1 << 29                      # bf16 elements: 1 GiB read, 1 GiB written
+        src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"calibration": "torch.neg bf16", "bytes_read_per_launch": 2 * n,
+                          "bytes_written_per_launch": 2 * n, "launches": 3}), flush=True)
+        return
     if mlp:
         data, step = None, build_mlp_step(q, torch, dev)
     else:
@@ -185,12 +198,15 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    # timed steps: nothing but the step itself between the two synchronisations
+    # timed steps: the step itself, with timing events around the launches of
+    # the roofline kernel (the bf16-output NVFP4 GEMM: fprop and dgrad) only
+    marks = {"fprop": [], "dgrad": []}
     t0 = time.perf_counter()
     for _ in range(steps):
-        step.run()
+        step.run(marks)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    live = [s.elapsed_time(e) for k in marks for s, e in marks[k]]
 
     # per-operation times: separate, serialised passes with events
     times = {}
@@ -208,9 +224,7 @@ def main():
     layer0 = step.layers[0]
     gemm_flop = 2.0 * layer0.M * layer0.N * layer0.K   # equal for every layer here
     mean = lambda v: sum(v) / len(v)
-    nv_launches = [t for k in ("fprop", "dgrad") for t in
-                   sum((times[key] for key in times if key[1] == k), [])]
-    gemm_bf16_ms = mean(nv_launches)
+    gemm_bf16_ms = mean(live)
     achieved = gemm_flop / (gemm_bf16_ms * 1e-3) / 1e12
 
     result = {
@@ -260,6 +274,7 @@ def main():
         "kernel": "k_gemm_nt<Nvfp4Src, bf16 out> (fprop, dgrad launches)", "bound": "mfma",
         "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_F16_TFLOPS, 4), "avg_launch_ms": round(gemm_bf16_ms, 4),
+        "launches": len(live), "timing": "HIP events around each launch in the timed steps",
         "traffic": None if mlp else counter_traffic(gemm_bf16_ms)}
     result["cpu_baseline"] = None
     if not args.no_cpu_baseline and not mlp:

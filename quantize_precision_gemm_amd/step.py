@@ -145,21 +145,35 @@ class TrainingStep:
     def flops(self):
         return sum(l.flops() for l in self.layers)
 
-    def run(self):
+    def run(self, marks=None):
+        """One step.  marks: optional {op name: list}; every launch of a named
+        operation is bracketed by two timing events on the stream it is
+        launched on, appended to the list as (start, end)."""
         torch = self.torch
         main = torch.cuda.current_stream()
+
+        def call(name, f):
+            if marks is None or name not in marks:
+                f()
+                return
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            f()
+            e.record()
+            marks[name].append((s, e))
+
         for layer in self.layers:
-            for _, f in layer.forward_ops():
-                f()
+            for n, f in layer.forward_ops():
+                call(n, f)
         for layer in reversed(self.layers):
-            for _, f in layer.backward_quant_ops():
-                f()
+            for n, f in layer.backward_quant_ops():
+                call(n, f)
             self.side.wait_stream(main)
-            for _, f in layer.dgrad_ops():
-                f()
+            for n, f in layer.dgrad_ops():
+                call(n, f)
             with torch.cuda.stream(self.side):
-                for _, f in layer.wgrad_ops():
-                    f()
+                for n, f in layer.wgrad_ops():
+                    call(n, f)
         main.wait_stream(self.side)
 
     def serial_ops(self):
