@@ -220,6 +220,25 @@ def main():
     for (i, name), v in avg_op.items():
         by_name.setdefault(name, []).append(v)
 
+    # the second NVFP4 GEMM datapath (FP8 MFMA per 16-element block),
+    # serialised, on the same quantised operands: measured beside the first
+    datapaths = None
+    if not mlp:
+        L = step.layers[0]
+        runs = [("fprop", q.FPROP, L.gx, L.gw, L.y), ("dgrad", q.DGRAD, L.gdy, L.gw, L.dx),
+                ("wgrad", q.WGRAD, L.gdyt, L.gxt, L.dw)]
+        fp8 = {}
+        for name, p_, a_, b_, o_ in runs:
+            q.nvfp4_gemm(p_, a_, b_, out=o_, fp8_blocks=True)
+            s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s_.record()
+            for _ in range(3):
+                q.nvfp4_gemm(p_, a_, b_, out=o_, fp8_blocks=True)
+            e_.record()
+            torch.cuda.synchronize()
+            fp8[name] = 2.0 * L.M * L.N * L.K / (s_.elapsed_time(e_) / 3 * 1e-3) / 1e12
+        datapaths = fp8
+
     ms_step = wall * 1e3 / steps
     layer0 = step.layers[0]
     gemm_flop = 2.0 * layer0.M * layer0.N * layer0.K   # equal for every layer here
@@ -245,6 +264,10 @@ def main():
                   if n in by_name]
     result["gemm_tflops"] = {n: round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12, 1)
                              for n in gemm_names}
+    if datapaths is not None:
+        result["gemm_datapaths_tflops"] = {
+            "fp16_decode (nvfp4_gemm)": {n: result["gemm_tflops"][n] for n in datapaths},
+            "fp8_blocks (nvfp4_gemm_fp8blk)": {n: round(v, 1) for n, v in datapaths.items()}}
     if mlp:
         result["config"] = {
             "workload": "4-block MLP training step (per block an up- and a down-projection "

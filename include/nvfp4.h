@@ -212,6 +212,21 @@ int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void*
                int64_t ldc, int32_t c_dtype, void* stream);
 
 /*
+ * nvfp4_gemm_fp8blk -- the same GEMM as nvfp4_gemm (same arguments, passes,
+ * validation and result within the same tolerance) by the second datapath:
+ * each NVFP4 block of 16 products is contracted by an FP8 matrix-core
+ * instruction (E2M1 values are exact in E4M3), and the two block scales
+ * multiply the exact fp32 partial before it is accumulated.  Only the
+ * accumulation across blocks rounds, in block order.
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.A (16-element blocks with an E4M3 scale each) and 2.B.2
+ * (the three passes).  Slower than nvfp4_gemm on gfx950 (the per-block
+ * scaling is vector-ALU work); provided so both datapaths can be measured.
+ */
+int nvfp4_gemm_fp8blk(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                      int64_t ldc, int32_t c_dtype, void* stream);
+
+/*
  * nvfp4_bf16_gemm -- the three GEMMs of a linear layer that stays in BF16
  * (no quantisation); bf16 products accumulated in fp32.
  * Defines: "Pretraining Large Language Models with NVFP4", Technische

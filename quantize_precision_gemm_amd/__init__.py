@@ -20,7 +20,7 @@ import torch
 __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm",
-    "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "lib_path", "load_library",
+    "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_gemm_fp8blk", "lib_path", "load_library",
 ]
 
 BLOCK_1X16 = 0
@@ -73,6 +73,8 @@ def load_library():
         L.nvfp4_rht_quantize.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [i32, D, D, P, i64, i32, P]
         L.nvfp4_gemm.restype = ctypes.c_int
+        L.nvfp4_gemm_fp8blk.argtypes = [i32, D, D, P, i64, i32, P]
+        L.nvfp4_gemm_fp8blk.restype = ctypes.c_int
         L.nvfp4_amax.argtypes = [P, i64, i64, i64, u32, P, P, P]
         L.nvfp4_amax.restype = ctypes.c_int
         L.nvfp4_bf16_gemm.argtypes = [i32, P, i64, P, i64, i64, i64, i64, P, i64, i32, P]
@@ -201,8 +203,10 @@ def nvfp4_rht_quantize(x, sign_mask, rounding=RNE, seed=0, amax_in=None, out=Non
     return out
 
 
-def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None):
-    """NVFP4 GEMM for FPROP / DGRAD / WGRAD (see nvfp4_gemm in nvfp4.h)."""
+def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None, fp8_blocks=False):
+    """NVFP4 GEMM for FPROP / DGRAD / WGRAD (see nvfp4_gemm in nvfp4.h).
+
+    fp8_blocks=True runs the second datapath (nvfp4_gemm_fp8blk)."""
     M = a.rows
     N = b.cols if pass_ == DGRAD else b.rows
     if out is None:
@@ -211,9 +215,10 @@ def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None):
     if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
         raise TypeError("output must be float32 or bfloat16 with a contiguous last dimension")
     da, db = a.descriptor(), b.descriptor()
-    st = load_library().nvfp4_gemm(pass_, ctypes.byref(da), ctypes.byref(db), _ptr(out),
-                                   out.stride(0), dt, _stream(stream))
-    _check(st, "nvfp4_gemm")
+    fn = load_library().nvfp4_gemm_fp8blk if fp8_blocks else load_library().nvfp4_gemm
+    st = fn(pass_, ctypes.byref(da), ctypes.byref(db), _ptr(out), out.stride(0), dt,
+            _stream(stream))
+    _check(st, "nvfp4_gemm_fp8blk" if fp8_blocks else "nvfp4_gemm")
     return out
 
 

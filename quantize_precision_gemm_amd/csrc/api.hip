@@ -181,8 +181,13 @@ uint32_t nvfp4_rht_sign_mask(uint64_t seed)
     return c[0] & 0xFFFFu;
 }
 
-int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
-               int64_t ldc, int32_t c_dtype, void* stream)
+}  // extern "C"
+
+namespace {
+
+// Validation and operand set-up shared by the two NVFP4 GEMM datapaths.
+int gemm_nvfp4(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t ldc,
+               int32_t c_dtype, void* stream, bool fp8_blocks)
 {
     if (pass != NVFP4_FPROP && pass != NVFP4_DGRAD && pass != NVFP4_WGRAD) return NVFP4_ERR_MODE;
     if (c_dtype != NVFP4_OUT_BF16 && c_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_MODE;
@@ -216,9 +221,29 @@ int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void*
         N = b->rows;
     }
     if (ldc < N) return NVFP4_ERR_SHAPE;
-    nvfp4::launch_gemm_nt(A, B, M, N, K, c, ldc, c_dtype == NVFP4_OUT_FP32,
-                          static_cast<hipStream_t>(stream));
+    const bool f32 = c_dtype == NVFP4_OUT_FP32;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (fp8_blocks && K > 0)
+        nvfp4::launch_gemm_fp8blk(A, B, M, N, K, c, ldc, f32, s);
+    else  // (an empty contraction is the same zero fill for both)
+        nvfp4::launch_gemm_nt(A, B, M, N, K, c, ldc, f32, s);
     return launch_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+               int64_t ldc, int32_t c_dtype, void* stream)
+{
+    return gemm_nvfp4(pass, a, b, c, ldc, c_dtype, stream, false);
+}
+
+int nvfp4_gemm_fp8blk(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                      int64_t ldc, int32_t c_dtype, void* stream)
+{
+    return gemm_nvfp4(pass, a, b, c, ldc, c_dtype, stream, true);
 }
 
 int nvfp4_bf16_gemm(int32_t pass, const void* a, int64_t lda, const void* b, int64_t ldb,

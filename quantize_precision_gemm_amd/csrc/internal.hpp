@@ -50,6 +50,11 @@ void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64
 void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
                     int64_t K, void* c, int64_t ldc, bool out_fp32, hipStream_t s);
 
+// The same product by the other datapath: FP8 MFMA per 16-element block,
+// block scales applied to the fp32 partials (K > 0).
+void launch_gemm_fp8blk(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
+                        int64_t K, void* c, int64_t ldc, bool out_fp32, hipStream_t s);
+
 // C[m, n] = sum_k A[m, k] B[n, k] over bf16 operands; a_t / b_t: the operand
 // is stored K x rows (element (r, k) at k * ld + r) instead of rows x K.
 // M, N, K are multiples of 8.

@@ -108,7 +108,10 @@ def test_rht_validation(lib):
     assert lib.nvfp4_rht_quantize(FAKE, 32, 16, 16, 1, 0, 0, None, ctypes.byref(d), None) == -2
 
 
-def test_gemm_validation(lib):
+@pytest.mark.parametrize("fn", ["nvfp4_gemm", "nvfp4_gemm_fp8blk"])
+def test_gemm_validation(lib, fn):
+    gemm = getattr(lib, fn)
+
     def op(rows, cols, block=0, **kw):
         base = dict(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, rows=rows, cols=cols,
                     ld_codes=max(16, ((cols + 31) // 32) * 16), ld_scales=max(4, cols // 16),
@@ -117,16 +120,16 @@ def test_gemm_validation(lib):
         return _desc(**base)
 
     a, w = op(32, 64), op(48, 64, 1)
-    assert lib.nvfp4_gemm(7, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 0, None) == -4
-    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 3, None) == -4
-    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(op(48, 32, 1)), FAKE, 64, 0, None) == -5
-    assert lib.nvfp4_gemm(0, ctypes.byref(w), ctypes.byref(a), FAKE, 64, 0, None) == -5
-    assert lib.nvfp4_gemm(1, ctypes.byref(op(32, 48)), ctypes.byref(w), FAKE, 64, 0, None) == -1
-    assert lib.nvfp4_gemm(2, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 0, None) == -5
-    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE + 2, 64, 0, None) == -3
-    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 66, 0, None) == -3
-    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 16, 0, None) == -2
-    assert lib.nvfp4_gemm(0, ctypes.byref(a), ctypes.byref(op(40, 64, 1)), FAKE, 64, 0, None) == -2
+    assert gemm(7, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 0, None) == -4
+    assert gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 3, None) == -4
+    assert gemm(0, ctypes.byref(a), ctypes.byref(op(48, 32, 1)), FAKE, 64, 0, None) == -5
+    assert gemm(0, ctypes.byref(w), ctypes.byref(a), FAKE, 64, 0, None) == -5
+    assert gemm(1, ctypes.byref(op(32, 48)), ctypes.byref(w), FAKE, 64, 0, None) == -1
+    assert gemm(2, ctypes.byref(a), ctypes.byref(w), FAKE, 64, 0, None) == -5
+    assert gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE + 2, 64, 0, None) == -3
+    assert gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 66, 0, None) == -3
+    assert gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 16, 0, None) == -2
+    assert gemm(0, ctypes.byref(a), ctypes.byref(op(40, 64, 1)), FAKE, 64, 0, None) == -2
 
 
 def test_amax_validation(lib):

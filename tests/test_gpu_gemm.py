@@ -1,7 +1,10 @@
 """GPU parity of the NVFP4 GEMM (fprop, dgrad, wgrad) against the fp64 oracle.
 
 Bar: relative Frobenius error <= 1e-5 on the kernel's fp32 output; the bf16
-output is bit-equal to round-to-nearest-even of that fp32 output.
+output is bit-equal to round-to-nearest-even of that fp32 output.  Both
+datapaths are checked: nvfp4_gemm (fp16 decode) and nvfp4_gemm_fp8blk (FP8
+MFMA per block).  The latter sums exact block partials in block order, which
+is what the oracle's fp32 block GEMM does, so it must match that bit for bit.
 Passes: "Pretraining Large Language Models with NVFP4" (gist.science
 summary), Technische Zusammenfassung 2.B.2 (Fprop, Dgrad, Wgrad).
 """
@@ -27,15 +30,18 @@ def env():
 
 
 def _check_both_dtypes(torch, q, pass_, ga, gb, want):
-    y32 = q.nvfp4_gemm(pass_, ga, gb, torch.float32)
-    y16 = q.nvfp4_gemm(pass_, ga, gb, torch.bfloat16)
-    torch.cuda.synchronize()
-    g32 = y32.cpu().numpy()
-    err = rel_fro(g32, want)
-    assert err <= TOL, f"relative Frobenius error {err:.3e}"
-    b16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
-    np.testing.assert_array_equal(b16, bf16_rne_bits(g32))
-    return g32
+    out = None
+    for fp8 in (False, True):
+        y32 = q.nvfp4_gemm(pass_, ga, gb, torch.float32, fp8_blocks=fp8)
+        y16 = q.nvfp4_gemm(pass_, ga, gb, torch.bfloat16, fp8_blocks=fp8)
+        torch.cuda.synchronize()
+        g32 = y32.cpu().numpy()
+        err = rel_fro(g32, want)
+        assert err <= TOL, f"{'fp8 blocks' if fp8 else 'fp16 decode'}: relative Frobenius error {err:.3e}"
+        b16 = y16.view(torch.int16).cpu().numpy().view(np.uint16)
+        np.testing.assert_array_equal(b16, bf16_rne_bits(g32))
+        out = g32 if out is None else out
+    return out
 
 
 # (M, K, N): several 256-tiles, ragged M/N, K tails (K % 128 != 0, K % 32 == 16)
@@ -128,3 +134,45 @@ def test_empty_contraction_and_determinism(env):
     y2 = q.nvfp4_gemm(q.FPROP, gx, gw, torch.float32)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+@pytest.mark.parametrize("shape", [(16, 16, 16), (300, 336, 272), (257, 1040, 528), (64, 4112, 96)])
+@pytest.mark.parametrize("pass_name", ["fprop", "dgrad", "wgrad"])
+def test_fp8blk_matches_block_oracle_bitwise(env, pass_name, shape):
+    torch, oracle, q, wl, dev = env
+    M, K, N = shape
+    rng = np.random.default_rng(11 * M + K + N)
+    print(f"fp8blk {pass_name} {shape}", flush=True)
+    if pass_name == "fprop":
+        x = wl.student_t_unit_var(rng, (M, K), 4)
+        w = wl.normal(rng, (N, K), 0.02)
+        ga = q.nvfp4_quantize(to_dev(x, dev))
+        gb = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, q.RNE, with_transpose=True)
+        oa, ob = oracle.quantize(x), oracle.quantize(w, oracle.BLOCK_16X16)
+        pass_ = q.FPROP
+    elif pass_name == "dgrad":
+        dy = wl.lognormal_rows(rng, (M, N))
+        w = wl.normal(rng, (N, K), 0.02)
+        ga = q.nvfp4_quantize(to_dev(dy, dev), q.BLOCK_1X16, q.SR, 3)
+        gb = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, q.RNE, with_transpose=True)
+        # the block GEMM takes both operands rows x K: W^T quantised 16x16
+        oa = oracle.quantize(dy, oracle.BLOCK_1X16, oracle.SR, 3)
+        ob = oracle.quantize(np.ascontiguousarray(w.T), oracle.BLOCK_16X16)
+        pass_ = q.DGRAD
+    else:
+        Mt = ((M + 15) // 16) * 16
+        dy = wl.lognormal_rows(rng, (Mt, N))
+        x = wl.student_t_unit_var(rng, (Mt, K), 4)
+        mask = q.nvfp4_rht_sign_mask(Mt)
+        ga = q.nvfp4_rht_quantize(to_dev(dy, dev), mask, q.SR, 5)
+        gb = q.nvfp4_rht_quantize(to_dev(x, dev), mask, q.RNE)
+        oa = oracle.rht_quantize(dy, mask, oracle.SR, 5)
+        ob = oracle.rht_quantize(x, mask, oracle.RNE)
+        pass_ = q.WGRAD
+    y = q.nvfp4_gemm(pass_, ga, gb, torch.float32, fp8_blocks=True)
+    torch.cuda.synchronize()
+    want = oracle.gemm_fp32_blocks(oa, ob)
+    got = y.cpu().numpy()
+    assert got.shape == want.shape
+    bad = np.argwhere(got.view(np.uint32) != want.view(np.uint32))
+    assert len(bad) == 0, f"{len(bad)} outputs differ, first {bad[0]}: {got[tuple(bad[0])]} vs {want[tuple(bad[0])]}"
