@@ -29,8 +29,9 @@
 // 8x8 block in registers for layout T.  Each wave then runs 4x2 MFMA
 // 32x32x16 tiles (a 128x64 slab, 128 fp32 accumulators) over the stage.  Two
 // LDS stages alternate: while the MFMAs consume one, the next step's data
-// (loaded from global memory one step earlier) is written into the other,
-// and the global loads two steps ahead are in flight.  Two waves per SIMD
+// (loaded from global memory one step earlier) is written into the other;
+// NVFP4 rows are small enough for two register stages, so their global loads
+// run two steps ahead, bf16 rows one.  Two waves per SIMD
 // let one wave's MFMAs cover the other's waits.  The epilogue stages 32
 // output rows per wave through LDS and stores 16-byte row segments.
 //
@@ -385,11 +386,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nt(OpArgs A, OpArgs B, int64_t 
         __syncthreads();
         for (; s + 2 <= nfull; s += 2) {
             src.load_full((s + 1) * kKS, g0);
+            // keep the loads ahead of the MFMAs: with one register stage
+            // they have only this step to land
+            __builtin_amdgcn_sched_barrier(0);
             compute(0);
             put(g0, 1);
             interleave_step(std::make_integer_sequence<int, 32>{});
             __syncthreads();
             src.load_full((s + 2 < nfull ? s + 2 : nfull - 1) * kKS, g0);
+            __builtin_amdgcn_sched_barrier(0);
             compute(1);
             put(g0, 0);  // harmless on the last pass: stage 0 is not read again
             interleave_step(std::make_integer_sequence<int, 32>{});

@@ -81,18 +81,29 @@ __device__ __forceinline__ uint32_t absmax8(const uint4& q)
     return max(max(bf16_absmax2(q.x), bf16_absmax2(q.y)), max(bf16_absmax2(q.z), bf16_absmax2(q.w)));
 }
 
+// Streaming reads run best with a few resident workgroups per CU that each
+// walk the tensor (grid-stride) with several loads in flight, rather than
+// one short-lived workgroup per chunk.
+constexpr int kFlatLoads = 4;      // 16-byte loads in flight per thread
+constexpr int kFlatGrid = 1024;    // workgroups of the flat amax pass
+constexpr int kAmaxGrid = 512;     // workgroups of the RHT amax passes
 __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, int64_t nvec,
                                                    uint32_t* __restrict__ amax_bits)
 {
-    // each workgroup reads 4 x 256 consecutive vectors, each thread 4 of them
-    const int64_t base = (int64_t)blockIdx.x * 1024 + threadIdx.x;
+    constexpr int kL = kFlatLoads;
     uint32_t m = 0u;
-    if (base + 768 < nvec) {
-        const uint4 q0 = x[base], q1 = x[base + 256], q2 = x[base + 512], q3 = x[base + 768];
-        m = max(max(absmax8(q0), absmax8(q1)), max(absmax8(q2), absmax8(q3)));
-    } else {
+    const int64_t stride = (int64_t)gridDim.x * 256 * kL;
+    int64_t base = (int64_t)blockIdx.x * 256 * kL + threadIdx.x;
+    for (; base + 256 * (kL - 1) < nvec; base += stride) {
+        uint4 q[kL];
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < kL; ++j) q[j] = x[base + 256 * j];
+#pragma unroll
+        for (int j = 0; j < kL; ++j) m = max(m, absmax8(q[j]));
+    }
+    if (base < nvec) {
+#pragma unroll
+        for (int j = 0; j < kL; ++j)
             if (base + 256 * j < nvec) m = max(m, absmax8(x[base + 256 * j]));
     }
     m = wave_max_u32(m);
@@ -296,13 +307,17 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
 }
 
 // ---------------------------------------------------------------------------
-// RHT + transpose + 1x16 quantiser (weight-gradient operands).
-// A workgroup covers 256 tokens x 128 channels; thread t takes channels
-// 8*(t%16) .. +7 of the tile (one 16-byte load per token row) and the
-// 16-token chunk t/16.
+// RHT + transpose + 1x16 quantiser (weight-gradient operands), and the amax
+// passes over the transform.  A thread loads 8 channels (one 16-byte load per
+// token row) of one 16-token chunk and runs their 8 butterflies.  The amax
+// passes, which write nothing, give a workgroup 64 tokens x 512 channels so
+// that every row is read in 1 KB runs, and walk the tiles grid-stride; the
+// quantiser covers 256 tokens x 128 channels so that each channel's codes
+// leave as 128 contiguous bytes.
 // ---------------------------------------------------------------------------
 
 constexpr int kRhtTok = 256, kRhtCh = 128;
+constexpr int kAmTok = 64, kAmCh = 512;   // amax passes: 1 KB of every row per workgroup
 
 __device__ __forceinline__ void load_rht_raw(const uint16_t* __restrict__ x, int64_t ld,
                                              int64_t tok0, int64_t ch0, uint4 (&raw)[16])
@@ -325,10 +340,12 @@ __global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x
                                                   int64_t channels, int64_t ld, uint32_t mask,
                                                   uint32_t* __restrict__ amax_bits)
 {
-    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
-    const int64_t ch0 = (int64_t)blockIdx.x * kRhtCh + cg * 8;
-    const int64_t tok0 = (int64_t)blockIdx.y * kRhtTok + j * 16;
+    const int cg = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int64_t bch = (channels + kAmCh - 1) / kAmCh, btok = (tokens + kAmTok - 1) / kAmTok;
     uint32_t m = 0u;
+    for (int64_t bt = blockIdx.x; bt < bch * btok; bt += gridDim.x) {
+    const int64_t ch0 = (bt % bch) * kAmCh + cg * 8;
+    const int64_t tok0 = (bt / bch) * kAmTok + j * 16;
     if (ch0 < channels && tok0 < tokens) {
         uint4 raw[16];
         load_rht_raw(x, ld, tok0, ch0, raw);
@@ -341,7 +358,8 @@ __global__ __launch_bounds__(256) void k_rht_amax(const uint16_t* __restrict__ x
             mu = __builtin_fmaxf(mu, absmax16(v));
         }
         // rounding is monotonic: the max of the scaled values is the scaled max
-        m = __float_as_uint(mu * 0.25f);
+        m = max(m, __float_as_uint(mu * 0.25f));
+    }
     }
     m = wave_max_u32(m);
     __shared__ uint32_t red[4];
@@ -359,10 +377,12 @@ __global__ __launch_bounds__(256) void k_amax_dual(const uint16_t* __restrict__ 
                                                    uint32_t* __restrict__ amax_bits,
                                                    uint32_t* __restrict__ amax_rht_bits)
 {
-    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
-    const int64_t ch0 = (int64_t)blockIdx.x * kRhtCh + cg * 8;
-    const int64_t tok0 = (int64_t)blockIdx.y * kRhtTok + j * 16;
+    const int cg = threadIdx.x & 63, j = threadIdx.x >> 6;
+    const int64_t bch = (channels + kAmCh - 1) / kAmCh, btok = (tokens + kAmTok - 1) / kAmTok;
     uint32_t m = 0u, mr = 0u;
+    for (int64_t bt = blockIdx.x; bt < bch * btok; bt += gridDim.x) {
+    const int64_t ch0 = (bt % bch) * kAmCh + cg * 8;
+    const int64_t tok0 = (bt / bch) * kAmTok + j * 16;
     if (ch0 < channels && tok0 < tokens) {
         uint4 raw[16];
         load_rht_raw(x, ld, tok0, ch0, raw);
@@ -377,7 +397,8 @@ __global__ __launch_bounds__(256) void k_amax_dual(const uint16_t* __restrict__ 
             mu = __builtin_fmaxf(mu, absmax16(v));
         }
         // rounding is monotonic: the max of the scaled values is the scaled max
-        mr = __float_as_uint(mu * 0.25f);
+        mr = max(mr, __float_as_uint(mu * 0.25f));
+    }
     }
     m = wave_max_u32(m);
     mr = wave_max_u32(mr);
@@ -467,7 +488,7 @@ void launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld,
     const int64_t nvec = rows * (cols >> 3);
     if (nvec == 0) return;
     if (ld == cols) {
-        hipLaunchKernelGGL(k_amax_flat, dim3(grid_for(nvec, 1024, INT32_MAX)), dim3(256), 0, s,
+        hipLaunchKernelGGL(k_amax_flat, dim3(grid_for(nvec, 256 * kFlatLoads, kFlatGrid)), dim3(256), 0, s,
                            reinterpret_cast<const uint4*>(x), nvec, bits);
     } else {
         hipLaunchKernelGGL(k_amax_rows, dim3(grid_for(nvec, 256, 4096)), dim3(256), 0, s, x, rows,
@@ -511,7 +532,7 @@ void launch_rht_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_
     uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
     hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, bits);
     if (tokens == 0 || channels == 0) return;
-    dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
+    dim3 g(grid_for(((channels + kAmCh - 1) / kAmCh) * ((tokens + kAmTok - 1) / kAmTok), 1, kAmaxGrid));
     hipLaunchKernelGGL(k_rht_amax, g, dim3(256), 0, s, x, tokens, channels, ld, mask, bits);
 }
 
@@ -522,7 +543,7 @@ void launch_amax_dual(const uint16_t* x, int64_t tokens, int64_t channels, int64
     uint32_t* b1 = reinterpret_cast<uint32_t*>(amax_rht);
     hipLaunchKernelGGL(k_zero_u32x2, dim3(1), dim3(1), 0, s, b0, b1);
     if (tokens == 0 || channels == 0) return;
-    dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
+    dim3 g(grid_for(((channels + kAmCh - 1) / kAmCh) * ((tokens + kAmTok - 1) / kAmTok), 1, kAmaxGrid));
     hipLaunchKernelGGL(k_amax_dual, g, dim3(256), 0, s, x, tokens, channels, ld, mask, b0, b1);
 }
 
