@@ -29,9 +29,10 @@
 // 8x8 block in registers for layout T.  Each wave then runs 4x2 MFMA
 // 32x32x16 tiles (a 128x64 slab, 128 fp32 accumulators) over the stage.  Two
 // LDS stages alternate: while the MFMAs consume one, the next step's data
-// (loaded from global memory one step earlier) is written into the other;
-// NVFP4 rows are small enough for two register stages, so their global loads
-// run two steps ahead, bf16 rows one.  Two waves per SIMD
+// (loaded from global memory earlier) is written into the other.  NVFP4 rows
+// are small (9 registers), so three register stages keep their global loads
+// three steps ahead of the MFMAs; bf16 rows (32 registers) get one stage and
+// load one step ahead.  Two waves per SIMD
 // let one wave's MFMAs cover the other's waits.  The epilogue stages 32
 // output rows per wave through LDS and stores 16-byte row segments.
 //
@@ -72,7 +73,7 @@ struct Nvfp4Src {
         uint32_t s;
     };
     typedef half8_t frag_t;
-    static constexpr bool kDeep = true;  // rows are small: two register stages
+    static constexpr bool kDeep = true;  // rows are small: three register stages
     const uint8_t* codes;
     const uint8_t* scales;
     int64_t nblk;
@@ -354,27 +355,44 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nt(OpArgs A, OpArgs B, int64_t 
     int64_t s = 0;
     Row g0, g1;
     if constexpr (Src::kDeep) {
-        // global loads run two steps ahead of the MFMAs (two register stages)
+        // global loads run three steps ahead of the MFMAs (three register
+        // stages); step t's row data lives in register stage t % 3 and its
+        // decoded tile in LDS stage t % 2
+        Row g2;
         if (nfull > 0) {
             src.load_full(0, g0);
-            put(g0, 0);
             // unconditional (clamped) loads keep the wait counts exact
-            src.load_full(nfull > 1 ? kKS : 0, g1);
+            src.load_full((nfull > 1 ? 1 : 0) * kKS, g1);
+            src.load_full((nfull > 2 ? 2 : nfull - 1) * kKS, g2);
+            put(g0, 0);
         }
         __syncthreads();
-        for (; s + 2 <= nfull; s += 2) {
-            // even step s: LDS stage 0 holds s, g1 holds s+1, g0 is free
-            src.load_full((s + 2 < nfull ? s + 2 : nfull - 1) * kKS, g0);
-            compute(0);
-            put(g1, 1);
+        auto step = [&](auto c3, int64_t t) {
+            constexpr int r = decltype(c3)::value;
+            const int st = (int)(t & 1);
+            Row& done = r == 0 ? g0 : (r == 1 ? g1 : g2);        // step t, already in LDS
+            Row& next = r == 0 ? g1 : (r == 1 ? g2 : g0);        // step t + 1
+            src.load_full((t + 3 < nfull ? t + 3 : nfull - 1) * kKS, done);
+            compute(st);
+            put(next, st ^ 1);  // past the last full step: harmless, never read
             interleave_step(std::make_integer_sequence<int, 32>{});
             __syncthreads();
-            // odd step s+1: stage 1 holds s+1, g0 holds s+2, g1 is free
-            src.load_full((s + 3 < nfull ? s + 3 : nfull - 1) * kKS, g1);
-            compute(1);
-            put(g0, 0);  // harmless on the last pass: stage 0 is not read again
-            interleave_step(std::make_integer_sequence<int, 32>{});
+        };
+        using I0 = std::integral_constant<int, 0>;
+        using I1 = std::integral_constant<int, 1>;
+        using I2 = std::integral_constant<int, 2>;
+        for (; s + 3 <= nfull; s += 3) {
+            step(I0{}, s);
+            step(I1{}, s + 1);
+            step(I2{}, s + 2);
+        }
+        if (s < nfull) step(I0{}, s++);
+        if (s < nfull) step(I1{}, s++);
+        if (nfull < nsteps) {  // partial last step into LDS stage nfull % 2
+            src.load_tail(nfull * kKS, g0);
+            put(g0, (int)(nfull & 1));
             __syncthreads();
+            compute((int)(nfull & 1));
         }
     } else {
         // one register stage: the loads of step s+1 are issued before the
@@ -401,13 +419,15 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nt(OpArgs A, OpArgs B, int64_t 
             __syncthreads();
         }
     }
-    if (s < nfull) compute(0);  // odd number of full steps: the last one is in stage 0
-    if (nfull < nsteps) {       // partial last step
-        src.load_tail(nfull * kKS, g1);
-        __syncthreads();
-        put(g1, 1);
-        __syncthreads();
-        compute(1);
+    if constexpr (!Src::kDeep) {
+        if (s < nfull) compute(0);  // odd number of full steps: the last one is in stage 0
+        if (nfull < nsteps) {       // partial last step
+            src.load_tail(nfull * kKS, g1);
+            __syncthreads();
+            put(g1, 1);
+            __syncthreads();
+            compute(1);
+        }
     }
 
     // Epilogue: each wave stages 32 output rows at a time through LDS (fp32,
