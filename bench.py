@@ -294,7 +294,7 @@ def main():
             k: round(qb[k] / (avg[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3) for k in qb}
         result["ms_per_op"] = {k: round(v, 4) for k, v in avg.items()}
     result["roofline"] = {
-        "kernel": "k_gemm_nt<Nvfp4Src, bf16 out> (fprop, dgrad launches)", "bound": "mfma",
+        "kernel": "k_gemm_nv<bf16 out> (fprop, dgrad launches)", "bound": "mfma",
         "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
         "frac": round(achieved / PEAK_F16_TFLOPS, 4), "avg_launch_ms": round(gemm_bf16_ms, 4),
         "launches": len(live), "timing": "HIP events around each launch in the timed steps",

@@ -6,39 +6,43 @@
 // linear layer); format 2.A (E2M1 codes, E4M3 scale per 16 elements, FP32
 // tensor scale); 2.B.1 (a few layers keep BF16).
 //
-// The pages' GEMM runs on Blackwell FP4 tensor cores; gfx950's block-scaled
-// FP4 MFMA takes power-of-two scales per 32 elements, which cannot express an
-// E4M3 scale per 16 elements.  Here every element is decoded to the exact
-// fp16 value q * S_b (E2M1 times E4M3 needs at most 6 significant bits and
-// lies in [2^-10, 2688], inside fp16's normal range): the hardware converts
-// a byte of two codes to an fp16 pair, and one packed fp16 multiply applies
-// the block scale.  The fp16 MFMA then accumulates exact products in fp32,
-// and the epilogue multiplies by alpha = (1/s_enc_a) (1/s_enc_b).
+// Both kernels compute C[m, n] = alpha sum_k A[m, k] B[n, k] with a
+// workgroup of 8 waves (two per SIMD) per 256x256 output tile, in K steps of
+// 64, and 4x2 MFMA 32x32x16 tiles per wave (a 128x64 slab, 128 fp32
+// accumulators).  Two LDS stages alternate: while the MFMAs consume one, the
+// next step is written into the other.  Workgroups are renumbered so that
+// each XCD gets a contiguous range of tiles, walked in groups of 8 tile rows
+// so that concurrently running tiles share operand panels.  The epilogue
+// stages 32 output rows per wave through LDS and stores 16-byte row segments.
 //
-// The kernel computes C[m, n] = alpha sum_k A[m, k] B[n, k].  NVFP4 operands
-// are always "rows x K" with K contiguous (the dgrad weight operand is the
-// transposed 16x16-block copy written by the quantiser).  A bf16 operand is
-// either "rows x K" (layout N) or "K x rows" (layout T, rows contiguous), so
-// the three bf16 passes read X, W and dY where they lie.
+// NVFP4 (k_gemm_nv).  The pages' GEMM runs on Blackwell FP4 tensor cores;
+// gfx950's block-scaled FP4 MFMA takes power-of-two scales per 32 elements,
+// which cannot express an E4M3 scale per 16 elements.  Here every element is
+// decoded to the exact fp16 value q * S_b (E2M1 times E4M3 needs at most 6
+// significant bits and lies in [2^-10, 2688], inside fp16's normal range):
+// the hardware converts a byte of two codes to an fp16 pair, and one packed
+// fp16 multiply applies the block scale.  The fp16 MFMA accumulates exact
+// products in fp32, and the epilogue multiplies by
+// alpha = (1/s_enc_a) (1/s_enc_b).  The A tile (shared by 4 waves) is
+// decoded once per workgroup into fp16 LDS rows; the B tile (shared by 2
+// waves) stays raw in LDS -- 48 bytes per row instead of 144 -- and each
+// wave decodes its own B fragments after reading them, trading a little
+// VALU work for a third less LDS traffic, the resource that bounds this
+// loop.  Each thread loads half an A row and half a B row per step; the
+// loads run three steps ahead of the MFMAs in three register stages.
+// NVFP4 operands are "rows x K" with K contiguous (the dgrad weight operand
+// is the transposed 16x16-block copy written by the quantiser).
 //
-// A workgroup of 8 waves (two per SIMD) computes a 256x256 tile in K steps
-// of 64.  Per step threads 0-255 bring the A tile and threads 256-511 the B
-// tile into a 16-bit LDS stage (256 rows of 64 values): an NVFP4 thread
-// decodes one row's 32 code bytes and 4 scales, so each element is decoded
-// once per workgroup; a bf16 thread moves 8 16-byte pieces, transposing an
-// 8x8 block in registers for layout T.  Each wave then runs 4x2 MFMA
-// 32x32x16 tiles (a 128x64 slab, 128 fp32 accumulators) over the stage.  Two
-// LDS stages alternate: while the MFMAs consume one, the next step's data
-// (loaded from global memory earlier) is written into the other.  NVFP4 rows
-// are small (9 registers), so three register stages keep their global loads
-// three steps ahead of the MFMAs; bf16 rows (32 registers) get one stage and
-// load one step ahead.  Two waves per SIMD
-// let one wave's MFMAs cover the other's waits.  The epilogue stages 32
-// output rows per wave through LDS and stores 16-byte row segments.
+// bf16 (k_gemm_bf16).  A bf16 operand is either "rows x K" (layout N) or
+// "K x rows" (layout T, rows contiguous), so the three bf16 passes read X,
+// W and dY where they lie.  Per step each thread moves 8 pieces of 16 bytes
+// into the 16-bit LDS tile, transposing an 8x8 block in registers for layout
+// T; its loads run one step ahead.
 //
 // Lane layout of v_mfma_f32_32x32x16_{f16,bf16}: lane l supplies row (A) or
-// column (B) l % 32 and the 8 consecutive k 8*(l/32) .. +7 of the 16-wide
-// step; accumulator j of lane l is row (j/4)*8 + (l/32)*4 + j%4, column l % 32.
+// column (B) l % 32 and 8 consecutive k (the "half" l / 32 of the 16-wide
+// step); accumulator j of lane l is row (j/4)*8 + (l/32)*4 + j%4, column l % 32.
+#include <type_traits>
 #include <utility>
 
 #include "internal.hpp"
@@ -52,9 +56,10 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 
 constexpr int kBM = 256, kBN = 256, kKS = 64;  // workgroup tile and K step
 constexpr int kRowBytes = 144;                 // LDS row: 64 16-bit values (128 B) + 16 B pad
-constexpr int kOpBytes = 256 * kRowBytes;      // one operand, one stage
+constexpr int kOpBytes = 256 * kRowBytes;      // one 16-bit operand tile, one stage
+constexpr int kEpiStride = 68;                 // floats per staged output row (64 + 4 pad)
 
-// Kernel arguments of one operand; fields a source does not use stay zero.
+// Kernel arguments of one operand; fields a kernel does not use stay zero.
 struct OpArgs {
     const void* data;       // NVFP4 codes, or bf16 values
     int64_t ld;             // bytes (codes) or elements (bf16) between consecutive rows in memory
@@ -65,86 +70,301 @@ struct OpArgs {
     int trans;              // bf16: 1 = stored K x rows (layout T), 0 = rows x K (layout N)
 };
 
-// --- NVFP4 operand: one thread per tile row --------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return (uint16_t)(u >> 16);
+}
 
-struct Nvfp4Src {
-    struct Row {  // one row's K step: 32 code bytes (64 k) and 4 scale bytes
-        uint4 c0, c1;
-        uint32_t s;
-    };
-    typedef half8_t frag_t;
-    static constexpr bool kDeep = true;  // rows are small: three register stages
-    const uint8_t* codes;
-    const uint8_t* scales;
-    int64_t nblk;
-    int rid;
+// This workgroup's output tile.  Workgroups are dealt round-robin to the 8
+// XCDs; renumbering gives each XCD a contiguous range, walked in groups of 8
+// tile rows, column by column.
+__device__ __forceinline__ void tile_of(int64_t M, int64_t N, int64_t& tile_m, int64_t& tile_n)
+{
+    const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+    const int64_t T = tiles_m * tiles_n;
+    const int64_t hw = blockIdx.x;
+    const int64_t L = (T % 8 == 0) ? (hw % 8) * (T / 8) + hw / 8 : hw;
+    const int64_t GM = 8;
+    const int64_t group = L / (GM * tiles_n);
+    const int64_t first_m = group * GM;
+    const int64_t gsz = (tiles_m - first_m < GM) ? (tiles_m - first_m) : GM;
+    const int64_t in_group = L - group * GM * tiles_n;
+    tile_m = first_m + in_group % gsz;
+    tile_n = in_group / gsz;
+}
 
-    // rid: this thread's row within the tile, r0: the tile's first row,
-    // lim: rows of the operand (rows past it re-read the last row; they are
-    // never stored)
-    __device__ __forceinline__ Nvfp4Src(const OpArgs& o, int rid_, int64_t r0, int64_t lim,
-                                        int64_t K)
-    {
-        rid = rid_;
-        int64_t r = r0 + rid;
-        r = r < lim ? r : lim - 1;
-        codes = static_cast<const uint8_t*>(o.data) + r * o.ld;
-        scales = o.scales + (r >> o.scale_shift) * o.ld_scales;
-        nblk = K >> 4;
-    }
-    __device__ __forceinline__ void load_full(int64_t k0, Row& w) const
-    {
-        const uint4* p = reinterpret_cast<const uint4*>(codes + (k0 >> 1));
-        w.c0 = p[0];
-        w.c1 = p[1];
-        w.s = *reinterpret_cast<const uint32_t*>(scales + (k0 >> 4));
-    }
-    // partial last step: missing blocks get zero codes and zero scales
-    __device__ __forceinline__ void load_tail(int64_t k0, Row& w) const
-    {
-        const int64_t b0 = k0 >> 4;
-        const uint4* p = reinterpret_cast<const uint4*>(codes + (k0 >> 1));
-        w.c0 = (b0 < nblk) ? p[0] : make_uint4(0, 0, 0, 0);
-        w.c1 = (b0 + 2 < nblk) ? p[1] : make_uint4(0, 0, 0, 0);
-        w.s = 0u;
+// Epilogue: each wave stages 32 output rows at a time through its part of
+// `lds` (fp32, alpha applied; every wave must be done with the operand
+// stages) and writes them back as 16-byte row segments.
+template <bool kOutF32>
+__device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float alpha,
+                                           uint8_t* lds, int64_t m0, int64_t n0, int64_t M,
+                                           int64_t N, void* __restrict__ c, int64_t ldc)
+{
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 5, lr = lane & 31;
+    float* stage_out = reinterpret_cast<float*>(lds) + wave * 32 * kEpiStride;
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-            if (b0 + j < nblk) w.s |= (uint32_t)scales[b0 + j] << (8 * j);
-    }
-    // decode 64 codes (4 blocks) to exact fp16 q * S into the row's 128 LDS bytes
-    __device__ __forceinline__ void store(const Row& w, uint8_t* __restrict__ op) const
-    {
-        uint8_t* dst = op + rid * kRowBytes;
-        const half2_t sa = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.s, 1.0f, false);
-        const half2_t sb = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.s, 1.0f, true);
-        const half2_t ss[4] = {__builtin_shufflevector(sa, sa, 0, 0), __builtin_shufflevector(sa, sa, 1, 1),
-                               __builtin_shufflevector(sb, sb, 0, 0), __builtin_shufflevector(sb, sb, 1, 1)};
-        const uint32_t c[8] = {w.c0.x, w.c0.y, w.c0.z, w.c0.w, w.c1.x, w.c1.y, w.c1.z, w.c1.w};
+    for (int tm = 0; tm < 4; ++tm) {
 #pragma unroll
-        for (int d = 0; d < 8; ++d) {  // dword d: elements 8d .. 8d+7, block d / 2
-            const half2_t S = ss[d >> 1];
-            half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[d], 1.0f, 0) * S;
-            half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[d], 1.0f, 1) * S;
-            half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[d], 1.0f, 2) * S;
-            half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(c[d], 1.0f, 3) * S;
-            uint4 v;
-            v.x = __builtin_bit_cast(uint32_t, p0);
-            v.y = __builtin_bit_cast(uint32_t, p1);
-            v.z = __builtin_bit_cast(uint32_t, p2);
-            v.w = __builtin_bit_cast(uint32_t, p3);
-            *reinterpret_cast<uint4*>(dst + 16 * d) = v;
+        for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+                const int r = (e >> 2) * 8 + g * 4 + (e & 3);
+                stage_out[r * kEpiStride + 32 * tn + lr] = acc[tm][tn][e] * alpha;
+            }
+        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
+        __builtin_amdgcn_wave_barrier();
+        // 32 rows x 64 columns = 32 x 16 float4; lane handles float4 (row, q)
+#pragma unroll
+        for (int it = 0; it < 8; ++it) {
+            const int idx = it * 64 + lane;
+            const int r = idx >> 4, q = idx & 15;
+            const float4 v = *reinterpret_cast<const float4*>(stage_out + r * kEpiStride + 4 * q);
+            const int64_t row = m0 + 32 * tm + r, col = n0 + 4 * q;
+            if (row < M && col < N) {
+                if constexpr (kOutF32) {
+                    float* dst = static_cast<float*>(c) + row * ldc + col;
+                    if (col + 4 <= N) {
+                        *reinterpret_cast<float4*>(dst) = v;
+                    } else {
+                        dst[0] = v.x;
+                        if (col + 1 < N) dst[1] = v.y;
+                        if (col + 2 < N) dst[2] = v.z;
+                    }
+                } else {
+                    uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
+                    const uint16_t b0 = f32_to_bf16_rne(v.x), b1 = f32_to_bf16_rne(v.y);
+                    const uint16_t b2 = f32_to_bf16_rne(v.z), b3 = f32_to_bf16_rne(v.w);
+                    if (col + 4 <= N) {
+                        *reinterpret_cast<uint2*>(dst) =
+                            make_uint2(b0 | ((uint32_t)b1 << 16), b2 | ((uint32_t)b3 << 16));
+                    } else {
+                        dst[0] = b0;
+                        if (col + 1 < N) dst[1] = b1;
+                        if (col + 2 < N) dst[2] = b2;
+                    }
+                }
+            }
         }
+        __builtin_amdgcn_wave_barrier();
     }
-    __device__ __forceinline__ static float16_t mfma(const frag_t& a, const frag_t& b, const float16_t& c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
-    }
+}
+
+__device__ __forceinline__ void zero_acc(float16_t (&acc)[4][2])
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+}
+
+// 8 E2M1 codes (one dword, low nibble first) times the fp16 block scale S
+// (broadcast pair): the exact fp16 values, in code order.
+__device__ __forceinline__ half8_t decode8(uint32_t w, half2_t S)
+{
+    const half2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 0) * S;
+    const half2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 1) * S;
+    const half2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 2) * S;
+    const half2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(w, 1.0f, 3) * S;
+    return __builtin_shufflevector(__builtin_shufflevector(p0, p1, 0, 1, 2, 3),
+                                   __builtin_shufflevector(p2, p3, 0, 1, 2, 3), 0, 1, 2, 3, 4, 5,
+                                   6, 7);
+}
+
+// ---------------------------------------------------------------------------
+// NVFP4 x NVFP4
+//
+// LDS stage: A as fp16 rows (256 x 144 B), B as raw codes (256 x 48 B: 32
+// code bytes + pad, so that 16-byte reads of 8 consecutive rows hit distinct
+// banks) and B scales (256 x 4 B).  Thread t handles half h = t % 2 of tile
+// row t / 2 of both operands: 16 code bytes (32 k, blocks 2h and 2h+1) and 2
+// scale bytes each.
+//
+// Within a step the MFMA sub-steps take the k in a permuted order (the
+// contraction does not depend on it): lane half g of sub-step i covers
+// k = 32 g + 8 i .. +7.  A lane's B fragments for the whole step are then 16
+// contiguous code bytes -- one 16-byte LDS read -- and sub-step i uses block
+// 2g + i/2; the A fragments are read from the matching fp16 offsets.
+// ---------------------------------------------------------------------------
+
+constexpr int kBRow = 48;
+constexpr int kAOp = kOpBytes;
+constexpr int kBOp = 256 * kBRow;
+constexpr int kStage = kAOp + kBOp + 256 * 4;
+
+struct NvRow {     // one thread's share of a K step
+    uint4 ca, cb;  // 16 code bytes of its A and B half rows
+    uint32_t s;    // A scales in bytes 0-1, B scales in bytes 2-3
 };
 
-// --- bf16 operand ----------------------------------------------------------
+}  // namespace
+
+template <bool kOutF32>
+__global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t M, int64_t N,
+                                                    int64_t K, void* __restrict__ c, int64_t ldc)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, lr = lane & 31;
+    int64_t tile_m, tile_n;
+    tile_of(M, N, tile_m, tile_n);
+
+    // half h of tile row `row` (rows past the operand re-read its last row;
+    // they are never stored)
+    const int row = tid >> 1, h = tid & 1;
+    int64_t ra = tile_m * kBM + row, rb = tile_n * kBN + row;
+    ra = ra < M ? ra : M - 1;
+    rb = rb < N ? rb : N - 1;
+    const uint8_t* pa = static_cast<const uint8_t*>(A.data) + ra * A.ld + 16 * h;
+    const uint8_t* pb = static_cast<const uint8_t*>(B.data) + rb * B.ld + 16 * h;
+    const uint8_t* psa = A.scales + (ra >> A.scale_shift) * A.ld_scales + 2 * h;
+    const uint8_t* psb = B.scales + (rb >> B.scale_shift) * B.ld_scales + 2 * h;
+    const int64_t nblk = K >> 4;
+
+    auto load_full = [&](int64_t k0, NvRow& w) {
+        w.ca = *reinterpret_cast<const uint4*>(pa + (k0 >> 1));
+        w.cb = *reinterpret_cast<const uint4*>(pb + (k0 >> 1));
+        const uint32_t sa = *reinterpret_cast<const uint16_t*>(psa + (k0 >> 4));
+        const uint32_t sb = *reinterpret_cast<const uint16_t*>(psb + (k0 >> 4));
+        w.s = sa | (sb << 16);
+    };
+    // partial last step: blocks past K get zero scales, so their codes decode
+    // to zero (the 16 code bytes of a half row with one valid block still lie
+    // inside the row, whose length is rounded up to 32 codes)
+    auto load_tail = [&](int64_t k0, NvRow& w) {
+        const int64_t b0 = (k0 >> 4) + 2 * h;
+        w.ca = b0 < nblk ? *reinterpret_cast<const uint4*>(pa + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
+        w.cb = b0 < nblk ? *reinterpret_cast<const uint4*>(pb + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
+        uint32_t s = 0u;
+        for (int j = 0; j < 2; ++j)
+            if (b0 + j < nblk)
+                s |= ((uint32_t)psa[(k0 >> 4) + j] << (8 * j)) |
+                     ((uint32_t)psb[(k0 >> 4) + j] << (16 + 8 * j));
+        w.s = s;
+    };
+    // A half row decoded to fp16 q * S in natural k order; B half row stored raw
+    auto put = [&](const NvRow& w, int st) {
+        uint8_t* base = lds + st * kStage;
+        const half2_t pair = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.s, 1.0f, false);
+        const half2_t S0 = __builtin_shufflevector(pair, pair, 0, 0);
+        const half2_t S1 = __builtin_shufflevector(pair, pair, 1, 1);
+        const uint32_t cw[4] = {w.ca.x, w.ca.y, w.ca.z, w.ca.w};
+#pragma unroll
+        for (int d = 0; d < 4; ++d)  // dword d: k 32h + 8d .. +7, block 2h + d/2
+            *reinterpret_cast<half8_t*>(base + row * kRowBytes + 64 * h + 16 * d) =
+                decode8(cw[d], d < 2 ? S0 : S1);
+        *reinterpret_cast<uint4*>(base + kAOp + row * kBRow + 16 * h) = w.cb;
+        *reinterpret_cast<uint16_t*>(base + kAOp + kBOp + row * 4 + 2 * h) = (uint16_t)(w.s >> 16);
+    };
+
+    float16_t acc[4][2];
+    zero_acc(acc);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int a_frag = (wm * 128 + lr) * kRowBytes + 64 * g;  // + 32 tm rows, + 16 i bytes
+    const int b_row = wn * 64 + lr;                           // + 32 tn
+
+    auto compute = [&](int st) {
+        const uint8_t* As = lds + st * kStage;
+        const uint8_t* Bs = As + kAOp;
+        const uint8_t* Bsc = Bs + kBOp;
+        uint4 bc[2];
+        half2_t bpair[2];
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn) {
+            bc[tn] = *reinterpret_cast<const uint4*>(Bs + (b_row + 32 * tn) * kBRow + 16 * g);
+            // this lane's blocks 2g and 2g+1, moved to the low half
+            const uint32_t sw = *reinterpret_cast<const uint32_t*>(Bsc + (b_row + 32 * tn) * 4) >> (16 * g);
+            bpair[tn] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sw, 1.0f, false);
+        }
+        half8_t af[2][4];  // A fragments of two sub-steps in flight
+#pragma unroll
+        for (int t = 0; t < 4; ++t) af[0][t] = *reinterpret_cast<const half8_t*>(As + a_frag + t * 32 * kRowBytes);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int cur = i & 1, nxt = cur ^ 1;
+            if (i < 3) {
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                    af[nxt][t] = *reinterpret_cast<const half8_t*>(As + a_frag + t * 32 * kRowBytes + 16 * (i + 1));
+            }
+            half8_t bf[2];
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) {
+                const half2_t S = (i < 2) ? __builtin_shufflevector(bpair[tn], bpair[tn], 0, 0)
+                                          : __builtin_shufflevector(bpair[tn], bpair[tn], 1, 1);
+                const uint32_t w = i == 0 ? bc[tn].x : i == 1 ? bc[tn].y : i == 2 ? bc[tn].z : bc[tn].w;
+                bf[tn] = decode8(w, S);
+            }
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][tm], bf[tn], acc[tm][tn], 0, 0, 0);
+        }
+    };
+
+    // Step t's rows live in register stage t % 3 and its tile in LDS stage
+    // t % 2.  Loads are unconditional (clamped to the last full step) so the
+    // compiler's wait counts stay exact.
+    const int64_t nsteps = (K + kKS - 1) / kKS;
+    const int64_t nfull = K / kKS;
+    int64_t s = 0;
+    NvRow g0, g1, g2;
+    if (nfull > 0) {
+        load_full(0, g0);
+        load_full((nfull > 1 ? 1 : 0) * kKS, g1);
+        load_full((nfull > 2 ? 2 : nfull - 1) * kKS, g2);
+        put(g0, 0);
+    }
+    __syncthreads();
+    auto step = [&](auto c3, int64_t t) {
+        constexpr int r = decltype(c3)::value;
+        const int st = (int)(t & 1);
+        NvRow& done = r == 0 ? g0 : (r == 1 ? g1 : g2);  // step t, already in LDS
+        NvRow& next = r == 0 ? g1 : (r == 1 ? g2 : g0);  // step t + 1
+        load_full((t + 3 < nfull ? t + 3 : nfull - 1) * kKS, done);
+        compute(st);
+        put(next, st ^ 1);  // past the last full step: harmless, never read
+        __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (; s + 3 <= nfull; s += 3) {
+        step(I0{}, s);
+        step(I1{}, s + 1);
+        step(I2{}, s + 2);
+    }
+    if (s < nfull) step(I0{}, s++);
+    if (s < nfull) step(I1{}, s++);
+    if (nfull < nsteps) {  // partial last step, into LDS stage nfull % 2
+        load_tail(nfull * kKS, g0);
+        put(g0, (int)(nfull & 1));
+        __syncthreads();
+        compute((int)(nfull & 1));
+    }
+
+    const float alpha = (1.0f / *A.s_enc) * (1.0f / *B.s_enc);
+    __syncthreads();  // every wave is done reading the operand stages
+    store_tile<kOutF32>(acc, alpha, lds, tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c,
+                        ldc);
+}
+
+namespace {
+
+// ---------------------------------------------------------------------------
+// bf16 operands
 //
-// Thread rid moves 8 pieces of 16 bytes (8 values) per step; kg = rid % 8
-// names the 8-wide k group of the step it covers and c = rid / 8 the rows.
+// Thread rid (0..255 of its operand) moves 8 pieces of 16 bytes (8 values)
+// per step; kg = rid % 8 names the 8-wide k group of the step it covers and
+// c = rid / 8 the rows.
 // Layout N (rows x K): piece j is row c + 32 j, k group kg -- a wave's load
 //   covers 8 full 128-byte row segments.
 // Layout T (K x rows): piece j is k row 8 kg + j, rows 8c .. 8c+7 -- again 8
@@ -156,13 +376,12 @@ struct Nvfp4Src {
 // kMode: 0 = both operands N, 1 = both T, 2 = per operand (OpArgs::trans);
 // in mode 2 both layouts' arithmetic runs and a select keeps one, so the two
 // halves of the workgroup run the same instructions.
+// ---------------------------------------------------------------------------
 template <int kMode>
 struct Bf16Src {
     struct Row {
         uint4 v[8];
     };
-    typedef bf16x8_t frag_t;
-    static constexpr bool kDeep = false;  // 32 registers per stage: one stage
     const uint16_t* base;  // piece 0 of step 0
     int64_t ld, K, kstride, jstride;
     int kg, c, cmax;
@@ -170,6 +389,8 @@ struct Bf16Src {
 
     __device__ __forceinline__ bool trans() const { return kMode == 2 ? t_ : kMode == 1; }
 
+    // rid: this thread's index within its operand, r0: the tile's first row,
+    // lim: rows of the operand
     __device__ __forceinline__ Bf16Src(const OpArgs& o, int rid, int64_t r0, int64_t lim, int64_t K_)
     {
         t_ = o.trans != 0;
@@ -235,24 +456,12 @@ struct Bf16Src {
             *reinterpret_cast<uint4*>(op + (rbase + rstep * i) * kRowBytes + 16 * kg) = t;
         }
     }
-    __device__ __forceinline__ static float16_t mfma(const frag_t& a, const frag_t& b, const float16_t& c)
-    {
-        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-    }
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
-{
-    uint32_t u = __float_as_uint(f);
-    u += 0x7FFFu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
-}
-
-// Instruction-schedule hint for one K step (32 MFMAs per wave): the first
-// half of the MFMAs is interleaved with the LDS fragment reads only; the
-// second half also carries the next step's LDS writes and the VALU work
-// feeding them (the NVFP4 decode, the bf16 transpose), which gives the
-// global loads behind them as much time as possible to land.
+// Instruction-schedule hint for one bf16 K step (32 MFMAs per wave): the
+// first half of the MFMAs is interleaved with the LDS fragment reads only;
+// the second half also carries the next step's LDS writes and the transposes
+// feeding them.
 template <int kM>
 __device__ __forceinline__ void interleave_slot()
 {
@@ -277,31 +486,17 @@ __device__ __forceinline__ void interleave_step(std::integer_sequence<int, kMs..
 }  // namespace
 
 template <class Src, bool kOutF32>
-__global__ __launch_bounds__(512, 1) void k_gemm_nt(OpArgs A, OpArgs B, int64_t M, int64_t N,
-                                                    int64_t K, void* __restrict__ c, int64_t ldc)
+__global__ __launch_bounds__(512, 1) void k_gemm_bf16(OpArgs A, OpArgs B, int64_t M, int64_t N,
+                                                      int64_t K, void* __restrict__ c, int64_t ldc)
 {
     typedef typename Src::Row Row;
-    typedef typename Src::frag_t frag_t;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kOpBytes];  // [stage][A/B]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, lr = lane & 31;
-
-    // Tile order: workgroups are dealt round-robin to the 8 XCDs; renumber so
-    // that each XCD gets a contiguous range, then walk groups of 8 tile rows
-    // column by column so that concurrently running tiles share operand panels.
-    const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
-    const int64_t T = tiles_m * tiles_n;
-    const int64_t hw = blockIdx.x;
-    const int64_t L = (T % 8 == 0) ? (hw % 8) * (T / 8) + hw / 8 : hw;
-    const int64_t GM = 8;
-    const int64_t group = L / (GM * tiles_n);
-    const int64_t first_m = group * GM;
-    const int64_t gsz = (tiles_m - first_m < GM) ? (tiles_m - first_m) : GM;
-    const int64_t in_group = L - group * GM * tiles_n;
-    const int64_t tile_m = first_m + in_group % gsz;
-    const int64_t tile_n = in_group / gsz;
+    int64_t tile_m, tile_n;
+    tile_of(M, N, tile_m, tile_n);
 
     // threads 0..255 bring the A tile into LDS, 256..511 the B tile
     const bool is_b = tid >= 256;
@@ -310,13 +505,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nt(OpArgs A, OpArgs B, int64_t 
     auto put = [&](const Row& w, int stage) { src.store(w, lds[stage][is_b ? 1 : 0]); };
 
     float16_t acc[4][2];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
+    zero_acc(acc);
     const int wm = wave >> 2, wn = wave & 3;
     // fragment read offsets within a stage: row (32 t + lr) of the wave's
     // 128-row A slab / 64-row B slab, k = 16 i + 8 g
@@ -326,163 +515,68 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nt(OpArgs A, OpArgs B, int64_t 
     auto compute = [&](int stage) {
         const uint8_t* As = lds[stage][0];
         const uint8_t* Bs = lds[stage][1];
-        frag_t af[2][4], bf[2][2];  // fragments of two sub-steps in flight
+        bf16x8_t af[2][4], bf[2][2];  // fragments of two sub-steps in flight
 #pragma unroll
-        for (int t = 0; t < 4; ++t) af[0][t] = *reinterpret_cast<const frag_t*>(As + a_frag + t * 32 * kRowBytes);
+        for (int t = 0; t < 4; ++t) af[0][t] = *reinterpret_cast<const bf16x8_t*>(As + a_frag + t * 32 * kRowBytes);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) bf[0][t] = *reinterpret_cast<const frag_t*>(Bs + b_frag + t * 32 * kRowBytes);
+        for (int t = 0; t < 2; ++t) bf[0][t] = *reinterpret_cast<const bf16x8_t*>(Bs + b_frag + t * 32 * kRowBytes);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int cur = i & 1, nxt = cur ^ 1;
             if (i < 3) {
 #pragma unroll
                 for (int t = 0; t < 4; ++t)
-                    af[nxt][t] = *reinterpret_cast<const frag_t*>(As + a_frag + t * 32 * kRowBytes + 32 * (i + 1));
+                    af[nxt][t] = *reinterpret_cast<const bf16x8_t*>(As + a_frag + t * 32 * kRowBytes + 32 * (i + 1));
 #pragma unroll
                 for (int t = 0; t < 2; ++t)
-                    bf[nxt][t] = *reinterpret_cast<const frag_t*>(Bs + b_frag + t * 32 * kRowBytes + 32 * (i + 1));
+                    bf[nxt][t] = *reinterpret_cast<const bf16x8_t*>(Bs + b_frag + t * 32 * kRowBytes + 32 * (i + 1));
             }
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
-                for (int tn = 0; tn < 2; ++tn) acc[tm][tn] = Src::mfma(af[cur][tm], bf[cur][tn], acc[tm][tn]);
+                for (int tn = 0; tn < 2; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][tm], bf[cur][tn], acc[tm][tn], 0, 0, 0);
         }
     };
 
-    // Main loop over full K steps (the partial last step is handled after it).
+    // One register stage: the loads of step s+1 are issued before the MFMAs
+    // of step s (a scheduling barrier keeps them there) and written to LDS
+    // after them.
     const int64_t nsteps = (K + kKS - 1) / kKS;
     const int64_t nfull = K / kKS;
     int64_t s = 0;
-    Row g0, g1;
-    if constexpr (Src::kDeep) {
-        // global loads run three steps ahead of the MFMAs (three register
-        // stages); step t's row data lives in register stage t % 3 and its
-        // decoded tile in LDS stage t % 2
-        Row g2;
-        if (nfull > 0) {
-            src.load_full(0, g0);
-            // unconditional (clamped) loads keep the wait counts exact
-            src.load_full((nfull > 1 ? 1 : 0) * kKS, g1);
-            src.load_full((nfull > 2 ? 2 : nfull - 1) * kKS, g2);
-            put(g0, 0);
-        }
-        __syncthreads();
-        auto step = [&](auto c3, int64_t t) {
-            constexpr int r = decltype(c3)::value;
-            const int st = (int)(t & 1);
-            Row& done = r == 0 ? g0 : (r == 1 ? g1 : g2);        // step t, already in LDS
-            Row& next = r == 0 ? g1 : (r == 1 ? g2 : g0);        // step t + 1
-            src.load_full((t + 3 < nfull ? t + 3 : nfull - 1) * kKS, done);
-            compute(st);
-            put(next, st ^ 1);  // past the last full step: harmless, never read
-            interleave_step(std::make_integer_sequence<int, 32>{});
-            __syncthreads();
-        };
-        using I0 = std::integral_constant<int, 0>;
-        using I1 = std::integral_constant<int, 1>;
-        using I2 = std::integral_constant<int, 2>;
-        for (; s + 3 <= nfull; s += 3) {
-            step(I0{}, s);
-            step(I1{}, s + 1);
-            step(I2{}, s + 2);
-        }
-        if (s < nfull) step(I0{}, s++);
-        if (s < nfull) step(I1{}, s++);
-        if (nfull < nsteps) {  // partial last step into LDS stage nfull % 2
-            src.load_tail(nfull * kKS, g0);
-            put(g0, (int)(nfull & 1));
-            __syncthreads();
-            compute((int)(nfull & 1));
-        }
-    } else {
-        // one register stage: the loads of step s+1 are issued before the
-        // MFMAs of step s and written to LDS after them
-        if (nfull > 0) {
-            src.load_full(0, g0);
-            put(g0, 0);
-        }
-        __syncthreads();
-        for (; s + 2 <= nfull; s += 2) {
-            src.load_full((s + 1) * kKS, g0);
-            // keep the loads ahead of the MFMAs: with one register stage
-            // they have only this step to land
-            __builtin_amdgcn_sched_barrier(0);
-            compute(0);
-            put(g0, 1);
-            interleave_step(std::make_integer_sequence<int, 32>{});
-            __syncthreads();
-            src.load_full((s + 2 < nfull ? s + 2 : nfull - 1) * kKS, g0);
-            __builtin_amdgcn_sched_barrier(0);
-            compute(1);
-            put(g0, 0);  // harmless on the last pass: stage 0 is not read again
-            interleave_step(std::make_integer_sequence<int, 32>{});
-            __syncthreads();
-        }
+    Row g0;
+    if (nfull > 0) {
+        src.load_full(0, g0);
+        put(g0, 0);
     }
-    if constexpr (!Src::kDeep) {
-        if (s < nfull) compute(0);  // odd number of full steps: the last one is in stage 0
-        if (nfull < nsteps) {       // partial last step
-            src.load_tail(nfull * kKS, g1);
-            __syncthreads();
-            put(g1, 1);
-            __syncthreads();
-            compute(1);
-        }
+    __syncthreads();
+    for (; s + 2 <= nfull; s += 2) {
+        src.load_full((s + 1) * kKS, g0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(0);
+        put(g0, 1);
+        interleave_step(std::make_integer_sequence<int, 32>{});
+        __syncthreads();
+        src.load_full((s + 2 < nfull ? s + 2 : nfull - 1) * kKS, g0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(1);
+        put(g0, 0);  // harmless on the last pass: stage 0 is not read again
+        interleave_step(std::make_integer_sequence<int, 32>{});
+        __syncthreads();
+    }
+    if (s < nfull) compute(0);  // odd number of full steps: the last one is in stage 0
+    if (nfull < nsteps) {       // partial last step
+        src.load_tail(nfull * kKS, g0);
+        __syncthreads();
+        put(g0, 1);
+        __syncthreads();
+        compute(1);
     }
 
-    // Epilogue: each wave stages 32 output rows at a time through LDS (fp32,
-    // alpha applied) and writes them back as 16-byte row segments.
-    float alpha = 1.0f;
-    if (A.s_enc) alpha = (1.0f / *A.s_enc) * (1.0f / *B.s_enc);
-    const int64_t m0 = tile_m * kBM + wm * 128, n0 = tile_n * kBN + wn * 64;
-    constexpr int kEpiStride = 68;   // floats per staged row (64 + 4 pad)
-    __syncthreads();                 // every wave is done reading the operand stages
-    float* stage_out = reinterpret_cast<float*>(&lds[0][0][0]) + wave * 32 * kEpiStride;
-#pragma unroll
-    for (int tm = 0; tm < 4; ++tm) {
-#pragma unroll
-        for (int tn = 0; tn < 2; ++tn)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-                const int r = (e >> 2) * 8 + g * 4 + (e & 3);
-                stage_out[r * kEpiStride + 32 * tn + lr] = acc[tm][tn][e] * alpha;
-            }
-        __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
-        __builtin_amdgcn_wave_barrier();
-        // 32 rows x 64 columns = 32 x 16 float4; lane handles float4 (row, q)
-#pragma unroll
-        for (int it = 0; it < 8; ++it) {
-            const int idx = it * 64 + lane;
-            const int r = idx >> 4, q = idx & 15;
-            const float4 v = *reinterpret_cast<const float4*>(stage_out + r * kEpiStride + 4 * q);
-            const int64_t row = m0 + 32 * tm + r, col = n0 + 4 * q;
-            if (row < M && col < N) {
-                if constexpr (kOutF32) {
-                    float* dst = static_cast<float*>(c) + row * ldc + col;
-                    if (col + 4 <= N) {
-                        *reinterpret_cast<float4*>(dst) = v;
-                    } else {
-                        dst[0] = v.x;
-                        if (col + 1 < N) dst[1] = v.y;
-                        if (col + 2 < N) dst[2] = v.z;
-                    }
-                } else {
-                    uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
-                    const uint16_t b0 = f32_to_bf16_rne(v.x), b1 = f32_to_bf16_rne(v.y);
-                    const uint16_t b2 = f32_to_bf16_rne(v.z), b3 = f32_to_bf16_rne(v.w);
-                    if (col + 4 <= N) {
-                        *reinterpret_cast<uint2*>(dst) =
-                            make_uint2(b0 | ((uint32_t)b1 << 16), b2 | ((uint32_t)b3 << 16));
-                    } else {
-                        dst[0] = b0;
-                        if (col + 1 < N) dst[1] = b1;
-                        if (col + 2 < N) dst[2] = b2;
-                    }
-                }
-            }
-        }
-        __builtin_amdgcn_wave_barrier();
-    }
+    __syncthreads();  // every wave is done reading the operand stages
+    store_tile<kOutF32>(acc, 1.0f, &lds[0][0][0], tile_m * kBM + wm * 128, tile_n * kBN + wn * 64,
+                        M, N, c, ldc);
 }
 
 // Output of a GEMM with an empty contraction: alpha * 0.
@@ -499,47 +593,58 @@ __global__ __launch_bounds__(256) void k_fill_zero(void* __restrict__ c, int64_t
         static_cast<uint16_t*>(c)[r * ldc + col] = 0;
 }
 
-template <class Src>
-static void launch(const OpArgs& a, const OpArgs& b, int64_t M, int64_t N, int64_t K, void* c,
-                   int64_t ldc, bool out_fp32, hipStream_t s)
+static void launch_fill_zero(int64_t M, int64_t N, void* c, int64_t ldc, bool out_fp32,
+                             hipStream_t s)
 {
-    if (M == 0 || N == 0) return;
-    if (K == 0) {
-        dim3 g((unsigned)((M * N + 255) / 256));
-        if (out_fp32)
-            hipLaunchKernelGGL(k_fill_zero<true>, g, dim3(256), 0, s, c, ldc, M, N);
-        else
-            hipLaunchKernelGGL(k_fill_zero<false>, g, dim3(256), 0, s, c, ldc, M, N);
-        return;
-    }
-    const int64_t tiles = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
-    const dim3 grid((unsigned)tiles), block(512);
+    const dim3 g((unsigned)((M * N + 255) / 256));
     if (out_fp32)
-        hipLaunchKernelGGL((k_gemm_nt<Src, true>), grid, block, 0, s, a, b, M, N, K, c, ldc);
+        hipLaunchKernelGGL(k_fill_zero<true>, g, dim3(256), 0, s, c, ldc, M, N);
     else
-        hipLaunchKernelGGL((k_gemm_nt<Src, false>), grid, block, 0, s, a, b, M, N, K, c, ldc);
+        hipLaunchKernelGGL(k_fill_zero<false>, g, dim3(256), 0, s, c, ldc, M, N);
+}
+
+static dim3 tile_grid(int64_t M, int64_t N)
+{
+    return dim3((unsigned)(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN)));
 }
 
 void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N, int64_t K,
                     void* c, int64_t ldc, bool out_fp32, hipStream_t s)
 {
+    if (M == 0 || N == 0) return;
+    if (K == 0) return launch_fill_zero(M, N, c, ldc, out_fp32, s);
     const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc, 0};
     const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc, 0};
-    launch<Nvfp4Src>(A, B, M, N, K, c, ldc, out_fp32, s);
+    if (out_fp32)
+        hipLaunchKernelGGL(k_gemm_nv<true>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
+    else
+        hipLaunchKernelGGL(k_gemm_nv<false>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
+}
+
+template <class Src>
+static void launch_bf16(const OpArgs& a, const OpArgs& b, int64_t M, int64_t N, int64_t K, void* c,
+                        int64_t ldc, bool out_fp32, hipStream_t s)
+{
+    if (out_fp32)
+        hipLaunchKernelGGL((k_gemm_bf16<Src, true>), tile_grid(M, N), dim3(512), 0, s, a, b, M, N, K, c, ldc);
+    else
+        hipLaunchKernelGGL((k_gemm_bf16<Src, false>), tile_grid(M, N), dim3(512), 0, s, a, b, M, N, K, c, ldc);
 }
 
 void launch_bf16_gemm(const uint16_t* a, int64_t lda, bool a_t, const uint16_t* b, int64_t ldb,
                       bool b_t, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc,
                       bool out_fp32, hipStream_t s)
 {
+    if (M == 0 || N == 0) return;
+    if (K == 0) return launch_fill_zero(M, N, c, ldc, out_fp32, s);
     const OpArgs A{a, lda, nullptr, 0, 0, nullptr, a_t ? 1 : 0};
     const OpArgs B{b, ldb, nullptr, 0, 0, nullptr, b_t ? 1 : 0};
     if (a_t != b_t)
-        launch<Bf16Src<2>>(A, B, M, N, K, c, ldc, out_fp32, s);
+        launch_bf16<Bf16Src<2>>(A, B, M, N, K, c, ldc, out_fp32, s);
     else if (a_t)
-        launch<Bf16Src<1>>(A, B, M, N, K, c, ldc, out_fp32, s);
+        launch_bf16<Bf16Src<1>>(A, B, M, N, K, c, ldc, out_fp32, s);
     else
-        launch<Bf16Src<0>>(A, B, M, N, K, c, ldc, out_fp32, s);
+        launch_bf16<Bf16Src<0>>(A, B, M, N, K, c, ldc, out_fp32, s);
 }
 
 }  // namespace nvfp4
