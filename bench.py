@@ -57,7 +57,7 @@ def gemm_source_hash():
 def counter_traffic(avg_launch_ms):
     """HBM bytes per launch of the bf16 GEMM from the committed rocprofv3 PMC
     summary, if it was taken on the current kernel source; else None."""
-    path = os.path.join(ROOT, "profiles", "gemm_nt_bf16_12b_layer_pmc.md")
+    path = os.path.join(ROOT, "profiles", "gemm_nv_bf16_12b_layer_pmc.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
