@@ -56,13 +56,16 @@ class NVFP4Linear:
 
     # X and dY are each quantised twice (1x16, and through the RHT for
     # wgrad): one fused pass computes both tensor maxima of each.
+    def weight_ops(self):
+        q = self.q
+        return [("quant_W", lambda: q.nvfp4_quantize(self.w, q.BLOCK_16X16, q.RNE, out=self.gw))]
+
     def forward_ops(self):
         q = self.q
         return [
             ("amax_X", lambda: q.nvfp4_amax(self.x, self.mask, self.ax, self.ax_rht)),
             ("quant_X", lambda: q.nvfp4_quantize(self.x, q.BLOCK_1X16, q.RNE, amax_in=self.ax,
                                                  out=self.gx)),
-            ("quant_W", lambda: q.nvfp4_quantize(self.w, q.BLOCK_16X16, q.RNE, out=self.gw)),
             ("fprop", lambda: q.nvfp4_gemm(q.FPROP, self.gx, self.gw, out=self.y)),
         ]
 
@@ -110,6 +113,9 @@ class BF16Linear:
     def flops(self):
         return 3 * 2.0 * self.M * self.N * self.K
 
+    def weight_ops(self):
+        return []
+
     def forward_ops(self):
         q = self.q
         return [("bf16_fprop", lambda: q.nvfp4_bf16_gemm(q.FPROP, self.x, self.w, out=self.y))]
@@ -129,12 +135,16 @@ class BF16Linear:
 class TrainingStep:
     """Fprop of every layer in order, then the backward pass in reverse order.
 
-    Per layer in the backward pass, dY is quantised on the main stream; then
-    dgrad runs on the main stream while the wgrad branch (RHT operands and the
-    wgrad GEMM) runs on a second stream.  Wgrad feeds nothing later in the
-    step, so it overlaps with dgrad and with the next layer's backward work:
-    each GEMM's last, partial wave of workgroups is filled by the other's.
-    The step ends with the main stream waiting for the side stream.
+    The weights do not depend on anything else in the step: their
+    quantisation runs on a second stream from the start, beside the
+    activations' amax and quantisation on the main stream, and each layer's
+    fprop waits for its own weight.  Per layer in the backward pass, dY is
+    quantised on the main stream; then dgrad runs on the main stream while
+    the wgrad branch (RHT operands and the wgrad GEMM) runs on the second
+    stream.  Wgrad feeds nothing later in the step, so it overlaps with dgrad
+    and with the next layer's backward work: each GEMM's last, partial wave
+    of workgroups is filled by the other's.  The step ends with the main
+    stream waiting for the second one.
     """
 
     def __init__(self, torch, layers, device):
@@ -162,9 +172,21 @@ class TrainingStep:
             e.record()
             marks[name].append((s, e))
 
-        for layer in self.layers:
-            for n, f in layer.forward_ops():
+        self.side.wait_stream(main)
+        ready = []
+        with torch.cuda.stream(self.side):
+            for layer in self.layers:
+                for n, f in layer.weight_ops():
+                    call(n, f)
+                ev = torch.cuda.Event()
+                ev.record()
+                ready.append(ev)
+        for layer, ev in zip(self.layers, ready):
+            ops = layer.forward_ops()
+            for n, f in ops[:-1]:
                 call(n, f)
+            main.wait_event(ev)
+            call(*ops[-1])  # the layer's fprop
         for layer in reversed(self.layers):
             for n, f in layer.backward_quant_ops():
                 call(n, f)
@@ -180,7 +202,8 @@ class TrainingStep:
         """(layer index, name, call) of the whole step in one serial order."""
         ops = []
         for i, layer in enumerate(self.layers):
-            ops += [(i, n, f) for n, f in layer.forward_ops()]
+            fw = layer.forward_ops()
+            ops += [(i, n, f) for n, f in fw[:-1] + layer.weight_ops() + fw[-1:]]
         for i in reversed(range(len(self.layers))):
             layer = self.layers[i]
             for part in (layer.backward_quant_ops(), layer.dgrad_ops(), layer.wgrad_ops()):
