@@ -69,14 +69,15 @@ class NVFP4Linear:
             ("fprop", lambda: q.nvfp4_gemm(q.FPROP, self.gx, self.gw, out=self.y)),
         ]
 
+    def backward_amax_ops(self):
+        q = self.q
+        return [("amax_dY", lambda: q.nvfp4_amax(self.dy, self.mask, self.ady, self.ady_rht))]
+
     def backward_quant_ops(self):
         q = self.q
-        return [
-            ("amax_dY", lambda: q.nvfp4_amax(self.dy, self.mask, self.ady, self.ady_rht)),
-            ("quant_dY", lambda: q.nvfp4_quantize(self.dy, q.BLOCK_1X16, q.SR,
-                                                  self.seed + SR_SEED_DY, amax_in=self.ady,
-                                                  out=self.gdy)),
-        ]
+        return [("quant_dY", lambda: q.nvfp4_quantize(self.dy, q.BLOCK_1X16, q.SR,
+                                                      self.seed + SR_SEED_DY, amax_in=self.ady,
+                                                      out=self.gdy))]
 
     def dgrad_ops(self):
         q = self.q
@@ -120,6 +121,9 @@ class BF16Linear:
         q = self.q
         return [("bf16_fprop", lambda: q.nvfp4_bf16_gemm(q.FPROP, self.x, self.w, out=self.y))]
 
+    def backward_amax_ops(self):
+        return []
+
     def backward_quant_ops(self):
         return []
 
@@ -138,9 +142,10 @@ class TrainingStep:
     The weights do not depend on anything else in the step: their
     quantisation runs on a second stream from the start, beside the
     activations' amax and quantisation on the main stream, and each layer's
-    fprop waits for its own weight.  Per layer in the backward pass, dY is
-    quantised on the main stream; then dgrad runs on the main stream while
-    the wgrad branch (RHT operands and the wgrad GEMM) runs on the second
+    fprop waits for its own weight.  Per layer in the backward pass, the
+    fused amax pass over dY runs on the main stream; then the main stream
+    quantises dY (SR) and runs dgrad while the wgrad branch (RHT operands,
+    which need only the maxima, and the wgrad GEMM) runs on the second
     stream.  Wgrad feeds nothing later in the step, so it overlaps with dgrad
     and with the next layer's backward work: each GEMM's last, partial wave
     of workgroups is filled by the other's.  The step ends with the main
@@ -188,10 +193,10 @@ class TrainingStep:
             main.wait_event(ev)
             call(*ops[-1])  # the layer's fprop
         for layer in reversed(self.layers):
-            for n, f in layer.backward_quant_ops():
+            for n, f in layer.backward_amax_ops():
                 call(n, f)
             self.side.wait_stream(main)
-            for n, f in layer.dgrad_ops():
+            for n, f in layer.backward_quant_ops() + layer.dgrad_ops():
                 call(n, f)
             with torch.cuda.stream(self.side):
                 for n, f in layer.wgrad_ops():
@@ -206,7 +211,8 @@ class TrainingStep:
             ops += [(i, n, f) for n, f in fw[:-1] + layer.weight_ops() + fw[-1:]]
         for i in reversed(range(len(self.layers))):
             layer = self.layers[i]
-            for part in (layer.backward_quant_ops(), layer.dgrad_ops(), layer.wgrad_ops()):
+            for part in (layer.backward_amax_ops(), layer.backward_quant_ops(), layer.dgrad_ops(),
+                         layer.wgrad_ops()):
                 ops += [(i, n, f) for n, f in part]
         return ops
 
