@@ -176,3 +176,40 @@ def test_fp8blk_matches_block_oracle_bitwise(env, pass_name, shape):
     assert got.shape == want.shape
     bad = np.argwhere(got.view(np.uint32) != want.view(np.uint32))
     assert len(bad) == 0, f"{len(bad)} outputs differ, first {bad[0]}: {got[tuple(bad[0])]} vs {want[tuple(bad[0])]}"
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+def test_padded_leading_dimensions(env, fp8):
+    # Codes and scales with rows wider than needed, and an output with a wider
+    # row: the quantisers and both GEMM datapaths honour every leading
+    # dimension, and nothing past the logical columns of the output is written.
+    torch, oracle, q, wl, dev = env
+    rng = np.random.default_rng(17)
+    M, K, N = 272, 336, 208
+    x = wl.student_t_unit_var(rng, (M, K), 4)
+    w = wl.normal(rng, (N, K), 0.02)
+    print(f"padded ld fp8={fp8}", flush=True)
+
+    def padded(rows, cols, block, with_t):
+        t = q.alloc_nvfp4(rows, cols, block, with_t, dev)
+        srows = rows if block == q.BLOCK_1X16 else rows // 16
+        t.codes = torch.empty((rows, t.codes.shape[1] + 48), dtype=torch.uint8, device=dev)
+        t.scales = torch.empty((srows, t.scales.shape[1] + 8), dtype=torch.uint8, device=dev)
+        return t
+
+    gx = q.nvfp4_quantize(to_dev(x, dev), out=padded(M, K, q.BLOCK_1X16, False))
+    gw = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, q.RNE,
+                          out=padded(N, K, q.BLOCK_16X16, True))
+    assert gx.codes.stride(0) > K // 2 and gw.codes.stride(0) > K // 2
+    want = oracle.gemm(oracle.FPROP, oracle.quantize(x), oracle.quantize(w, oracle.BLOCK_16X16))
+    outs = {}
+    for dt in (torch.float32, torch.bfloat16):
+        buf = torch.full((M, N + 24), -3.0, dtype=dt, device=dev)
+        q.nvfp4_gemm(q.FPROP, gx, gw, out=buf[:, :N], fp8_blocks=fp8)
+        torch.cuda.synchronize()
+        assert (buf[:, N:] == -3.0).all().item()
+        outs[dt] = buf[:, :N].contiguous()
+    g32 = outs[torch.float32].cpu().numpy()
+    assert rel_fro(g32, want) <= TOL
+    b16 = outs[torch.bfloat16].view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(b16, bf16_rne_bits(g32))
