@@ -84,12 +84,15 @@ def make_inputs(dev):
 def quant_bytes():
     """Algorithmic HBM bytes of each quantisation operation: the fused amax
     passes read their tensor once; the encode passes read it and write codes
-    and scales; W is quantised with its own amax pass and a transposed copy."""
+    and scales (the dual passes both operands' codes and scales); W is
+    quantised with its own amax pass and a transposed copy."""
     e_x, e_w, e_dy = M * K, N * K, M * N
     enc = lambda e: 2 * e + e // 2 + e // 16                  # read bf16, write codes, scales
+    enc2 = lambda e: 2 * e + 2 * (e // 2 + e // 16)          # one read, both operands written
     return {"amax_X": 2 * e_x, "quant_X": enc(e_x),
             "quant_W": 2 * e_w + 2 * e_w + 2 * (e_w // 2 + e_w // 256),
-            "amax_dY": 2 * e_dy, "quant_dY": enc(e_dy), "rht_dY": enc(e_dy), "rht_X": enc(e_x)}
+            "amax_dY": 2 * e_dy, "quant_dY": enc(e_dy), "rht_dY": enc(e_dy), "rht_X": enc(e_x),
+            "dual_dY": enc2(e_dy), "dual_X": enc2(e_x)}
 
 
 def cpu_baseline(data, tokens=M):
@@ -123,15 +126,24 @@ def cpu_baseline(data, tokens=M):
             "seconds": t}
 
 
-def build_layer_step(q, torch, dev):
+def build_layer_step(q, torch, dev, fused_quant=False):
     """The 12B-layer step: one NVFP4 linear layer, numpy-drawn inputs."""
     from quantize_precision_gemm_amd.step import NVFP4Linear, TrainingStep
     data, t = make_inputs(dev)
-    layer = NVFP4Linear(q, torch, t["X"], t["W"], t["dY"], SEED)
+    layer = NVFP4Linear(q, torch, t["X"], t["W"], t["dY"], SEED, fused_quant)
     return data, TrainingStep(torch, [layer], dev)
 
 
-def build_mlp_step(q, torch, dev):
+def with_schedule(q, torch, dev, step, fused_quant):
+    """The same step over the same tensors, with the NVFP4 layers' quantisers
+    fused (nvfp4_quantize_dual) or separate."""
+    from quantize_precision_gemm_amd.step import NVFP4Linear, TrainingStep
+    layers = [NVFP4Linear(q, torch, l.x, l.w, l.dy, l.seed, fused_quant)
+              if isinstance(l, NVFP4Linear) else l for l in step.layers]
+    return TrainingStep(torch, layers, dev)
+
+
+def build_mlp_step(q, torch, dev, fused_quant=False):
     """The 4-block MLP step: 8 linear layers (3 NVFP4 blocks, the last block
     in bf16), each with its own inputs drawn on the GPU."""
     from quantize_precision_gemm_amd import workloads as wl
@@ -143,7 +155,8 @@ def build_mlp_step(q, torch, dev):
         seed = wl.layer_seed(wl.MLP_SEED, i)
         d = wl.layer_inputs_device(torch, dev, sh, seed)
         cls = BF16Linear if i >= len(shapes) - 2 else NVFP4Linear
-        layers.append(cls(q, torch, d["X"], d["W"], d["dY"], seed))
+        layers.append(NVFP4Linear(q, torch, d["X"], d["W"], d["dY"], seed, fused_quant)
+                      if cls is NVFP4Linear else cls(q, torch, d["X"], d["W"], d["dY"], seed))
     torch.cuda.synchronize()
     print(f"# MLP inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
     return TrainingStep(torch, layers, dev)
@@ -159,6 +172,10 @@ def main():
     ap.add_argument("--workload", choices=["layer", "mlp"], default="layer",
                     help="layer: one 12B-style linear layer (the default bench line); "
                          "mlp: the 4-block MLP training step at 16384 tokens")
+    ap.add_argument("--fused-quant", action="store_true",
+                    help="time the step with the dual quantisers (one encode pass per tensor "
+                         "for both operands) instead of separate ones; the other schedule is "
+                         "timed beside it either way")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (bf16 negation, 3 launches): "
@@ -190,9 +207,9 @@ def main():
                           "bytes_written_per_launch": 2 * n, "launches": 3}), flush=True)
         return
     if mlp:
-        data, step = None, build_mlp_step(q, torch, dev)
+        data, step = None, build_mlp_step(q, torch, dev, args.fused_quant)
     else:
-        data, step = build_layer_step(q, torch, dev)
+        data, step = build_layer_step(q, torch, dev, args.fused_quant)
 
     for _ in range(warmup):
         step.run()
@@ -208,6 +225,17 @@ def main():
     wall = time.perf_counter() - t0
     live = [s.elapsed_time(e) for k in marks for s, e in marks[k]]
 
+    # the other quantiser schedule over the same tensors, timed the same way
+    alt = with_schedule(q, torch, dev, step, not args.fused_quant)
+    for _ in range(warmup):
+        alt.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        alt.run()
+    torch.cuda.synchronize()
+    alt_ms = (time.perf_counter() - t0) * 1e3 / steps
+
     # per-operation times: separate, serialised passes with events
     times = {}
     for _ in range(max(3, steps // 2)):
@@ -215,6 +243,12 @@ def main():
         torch.cuda.synchronize()
         for j, (i, name, _) in enumerate(ops):
             times.setdefault((i, name), []).append(ev[j].elapsed_time(ev[j + 1]))
+        if not mlp:  # the other schedule's quantisers, for their bandwidth
+            ops, ev = alt.run_timed_ops()
+            torch.cuda.synchronize()
+            for j, (i, name, _) in enumerate(ops):
+                if name.startswith(("dual_", "quant_X", "quant_dY", "rht_")):
+                    times.setdefault((i, name), []).append(ev[j].elapsed_time(ev[j + 1]))
     avg_op = {k: sum(v) / len(v) for k, v in times.items()}
     by_name = {}
     for (i, name), v in avg_op.items():
@@ -260,6 +294,10 @@ def main():
         "dtype": "f16",
         "data": "synthetic",
     }
+    names = ("separate quantisers", "dual quantisers (nvfp4_quantize_dual)")
+    result["schedules_ms_per_step"] = {
+        names[int(args.fused_quant)]: round(ms_step, 4),
+        names[int(not args.fused_quant)]: round(alt_ms, 4)}
     gemm_names = [n for n in ("fprop", "dgrad", "wgrad", "bf16_fprop", "bf16_dgrad", "bf16_wgrad")
                   if n in by_name]
     result["gemm_tflops"] = {n: round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12, 1)

@@ -160,6 +160,40 @@ int nvfp4_rht_quantize(const void* x, int64_t tokens, int64_t channels, int64_t 
                        const float* amax_in, nvfp4_tensor* out, void* stream);
 
 /*
+ * nvfp4_quantize_dual -- both NVFP4 operands of one tensor from a single read:
+ * the 1x16 quantisation along the channels (the fprop operand X or the dgrad
+ * operand dY) and the RHT-transposed 1x16 quantisation along the tokens (the
+ * wgrad operand).
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.B.2 (the same activation and gradient enter fprop/dgrad
+ * untransformed and wgrad after the 16x16 random Hadamard transform) and
+ * 2.B.4 (SR for gradients, RNE otherwise; one rounding mode for both results,
+ * since both come from the same tensor).
+ * The results are bit-identical to
+ *   nvfp4_quantize(x, tokens, channels, ld_x, NVFP4_BLOCK_1X16, rounding,
+ *                  seed, amax_in, out)
+ *   nvfp4_rht_quantize(x, tokens, channels, ld_x, sign_mask, rounding,
+ *                      seed_rht, amax_rht_in, out_rht)
+ * and cost one read of x instead of two.
+ *   x          device bf16, tokens x ld_x elements (row = token); 16-byte
+ *              aligned, ld_x >= channels and a multiple of 8.
+ *   tokens     >= 0, a multiple of 16.   channels >= 0, a multiple of 16.
+ *   sign_mask  as for nvfp4_rht_quantize.
+ *   seed       Philox key of the SR draws of out (indexed as in
+ *              nvfp4_quantize); seed_rht the key of out_rht's draws.
+ *   amax_in, amax_rht_in  both NULL (one nvfp4_amax-style pass computes both
+ *              maxima) or both device floats holding max |x| and max |RHT(x)|.
+ *   out        1x16 descriptor of the tokens x channels result (no codes_t).
+ *   out_rht    1x16 descriptor of the channels x tokens result (no codes_t);
+ *              a different descriptor from out, with non-overlapping buffers.
+ * Returns NVFP4_OK or a negative status; nothing is launched on error.
+ */
+int nvfp4_quantize_dual(const void* x, int64_t tokens, int64_t channels, int64_t ld_x,
+                        uint32_t sign_mask, int32_t rounding, uint64_t seed, uint64_t seed_rht,
+                        const float* amax_in, const float* amax_rht_in, nvfp4_tensor* out,
+                        nvfp4_tensor* out_rht, void* stream);
+
+/*
  * nvfp4_amax -- tensor amax of a bf16 matrix and, optionally, of its 16-point
  * random Hadamard transform along the rows, in one pass over the data.
  * Defines: "Pretraining Large Language Models with NVFP4", Technische

@@ -19,7 +19,7 @@ import torch
 
 __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
-    "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_gemm",
+    "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_gemm",
     "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_gemm_fp8blk", "lib_path", "load_library",
 ]
 
@@ -71,6 +71,8 @@ def load_library():
         L.nvfp4_quantize.restype = ctypes.c_int
         L.nvfp4_rht_quantize.argtypes = [P, i64, i64, i64, u32, i32, u64, P, D, P]
         L.nvfp4_rht_quantize.restype = ctypes.c_int
+        L.nvfp4_quantize_dual.argtypes = [P, i64, i64, i64, u32, i32, u64, u64, P, P, D, D, P]
+        L.nvfp4_quantize_dual.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [i32, D, D, P, i64, i32, P]
         L.nvfp4_gemm.restype = ctypes.c_int
         L.nvfp4_gemm_fp8blk.argtypes = [i32, D, D, P, i64, i32, P]
@@ -201,6 +203,30 @@ def nvfp4_rht_quantize(x, sign_mask, rounding=RNE, seed=0, amax_in=None, out=Non
     _check(st, "nvfp4_rht_quantize")
     out.rows, out.cols, out.block = d.rows, d.cols, d.block
     return out
+
+
+def nvfp4_quantize_dual(x, sign_mask, rounding=RNE, seed=0, seed_rht=0, amax_in=None,
+                        amax_rht_in=None, out=None, out_rht=None, stream=None):
+    """Both operands of one tensor from one read (see nvfp4_quantize_dual).
+
+    Returns (the 1x16 tokens x channels operand, the RHT-transposed
+    channels x tokens operand)."""
+    _check_bf16(x)
+    tokens, channels = x.shape
+    if out is None:
+        out = alloc_nvfp4(tokens, channels, BLOCK_1X16, False, x.device)
+    if out_rht is None:
+        out_rht = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device)
+    d, dr = out.descriptor(), out_rht.descriptor()
+    ld_x = x.stride(0) if channels > 0 else 0  # no row stride without columns
+    st = load_library().nvfp4_quantize_dual(_ptr(x), tokens, channels, ld_x, sign_mask,
+                                            rounding, seed, seed_rht, _ptr(amax_in),
+                                            _ptr(amax_rht_in), ctypes.byref(d),
+                                            ctypes.byref(dr), _stream(stream))
+    _check(st, "nvfp4_quantize_dual")
+    out.rows, out.cols, out.block = d.rows, d.cols, d.block
+    out_rht.rows, out_rht.cols, out_rht.block = dr.rows, dr.cols, dr.block
+    return out, out_rht
 
 
 def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None, fp8_blocks=False):

@@ -138,6 +138,49 @@ int nvfp4_rht_quantize(const void* x, int64_t tokens, int64_t channels, int64_t 
     return launch_status();
 }
 
+int nvfp4_quantize_dual(const void* x, int64_t tokens, int64_t channels, int64_t ld_x,
+                        uint32_t sign_mask, int32_t rounding, uint64_t seed, uint64_t seed_rht,
+                        const float* amax_in, const float* amax_rht_in, nvfp4_tensor* out,
+                        nvfp4_tensor* out_rht, void* stream)
+{
+    if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_MODE;
+    if ((amax_in == nullptr) != (amax_rht_in == nullptr)) return NVFP4_ERR_NULL;
+    if (tokens < 0 || channels < 0 || tokens % 16 != 0 || channels % 16 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!x && tokens > 0 && channels > 0) return NVFP4_ERR_NULL;
+    if (ld_x < channels) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld_x % 8 != 0) return NVFP4_ERR_ALIGN;
+    if (!aligned(amax_in, 4) || !aligned(amax_rht_in, 4)) return NVFP4_ERR_ALIGN;
+    if (!out || !out_rht) return NVFP4_ERR_NULL;
+    if (out == out_rht) return NVFP4_ERR_MODE;
+    if (out->codes_t || out->scales_t || out_rht->codes_t || out_rht->scales_t)
+        return NVFP4_ERR_MODE;
+    int st = check_out(out, tokens, channels, NVFP4_BLOCK_1X16);
+    if (st != NVFP4_OK) return st;
+    st = check_out(out_rht, channels, tokens, NVFP4_BLOCK_1X16);
+    if (st != NVFP4_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint32_t mask = sign_mask & 0xFFFFu;
+    const float* amax_src = amax_in;
+    const float* amax_rht_src = amax_rht_in;
+    if (!amax_src) {
+        nvfp4::launch_amax_dual(xb, tokens, channels, ld_x, mask, out->amax, out_rht->amax, s);
+        amax_src = out->amax;
+        amax_rht_src = out_rht->amax;
+    }
+    nvfp4::launch_dual_quant(xb, tokens, channels, ld_x, mask, rounding, seed, seed_rht, amax_src,
+                             amax_rht_src, qout_of(out), qout_of(out_rht), s);
+    out->rows = tokens;
+    out->cols = channels;
+    out->block = NVFP4_BLOCK_1X16;
+    out_rht->rows = channels;
+    out_rht->cols = tokens;
+    out_rht->block = NVFP4_BLOCK_1X16;
+    return launch_status();
+}
+
 int nvfp4_amax(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t sign_mask,
                float* amax, float* amax_rht, void* stream)
 {

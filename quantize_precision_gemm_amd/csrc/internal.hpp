@@ -45,6 +45,13 @@ void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64
                       uint32_t mask, int rounding, uint64_t seed, const float* amax_src,
                       const QOut& o, hipStream_t s);
 
+// One read of x: o gets the 1x16 quantisation along the channels, o_rht the
+// RHT-transposed one (same codes as launch_quant and launch_rht_quant).
+void launch_dual_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
+                       uint32_t mask, int rounding, uint64_t seed, uint64_t seed_rht,
+                       const float* amax_src, const float* amax_rht_src, const QOut& o,
+                       const QOut& o_rht, hipStream_t s);
+
 // C[m, n] = (1/s_enc_a) (1/s_enc_b) sum_k a^[m, k] b^[n, k]; out_fp32 selects
 // fp32 or bf16 (round to nearest even) output.
 void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,

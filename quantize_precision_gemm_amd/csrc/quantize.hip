@@ -470,6 +470,119 @@ __global__ __launch_bounds__(256) void k_rht_quant(
 }
 
 // ---------------------------------------------------------------------------
+// Dual quantiser: one read of a tokens x channels matrix yields both its 1x16
+// quantisation along the channels (the fprop or dgrad operand) and the
+// RHT-transposed 1x16 quantisation along the tokens (the wgrad operand), with
+// the same codes as k_quant_1x16 and k_rht_quant.  Tile and thread map are
+// k_rht_quant's; a row block's 16 channels are the 8 + 8 held by lanes 2q and
+// 2q + 1 of one wave, so its amax is one lane shuffle.
+// ---------------------------------------------------------------------------
+
+// 8 values times f -> 4 packed bytes (RNE)
+__device__ __forceinline__ uint32_t encode8_rne(const float (&v)[8], float f)
+{
+    uint32_t w = 0u;
+    w = e2m1_rne_pk<0>(w, v[0] * f, v[1] * f);
+    w = e2m1_rne_pk<1>(w, v[2] * f, v[3] * f);
+    w = e2m1_rne_pk<2>(w, v[4] * f, v[5] * f);
+    w = e2m1_rne_pk<3>(w, v[6] * f, v[7] * f);
+    return w;
+}
+
+// 8 values times f, stochastically rounded with the draws of elements
+// 8*g8 .. 8*g8+7 (one Philox block) -> 4 packed bytes
+__device__ __forceinline__ uint32_t encode8_sr(const float (&v)[8], float f, uint64_t seed,
+                                               uint64_t g8)
+{
+    const Draws8 d = sr_draws8(seed, g8);
+    uint32_t w = 0u;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w |= e2m1_sr(v[i] * f, d.get(i)) << (4 * i);
+    return w;
+}
+
+template <bool kSR>
+__global__ __launch_bounds__(256) void k_dual_quant(
+    const uint16_t* __restrict__ x, int64_t tokens, int64_t channels, int64_t ld, uint32_t mask,
+    const float* __restrict__ amax_src, const float* __restrict__ amax_rht_src, uint64_t seed,
+    uint64_t seed_rht, QOut o, QOut o_rht)
+{
+    __shared__ uint2 scodes[kRhtCh][17];    // transposed codes [channel][chunk], padded
+    __shared__ uint8_t sscale[kRhtCh][16];  // [channel][chunk]
+
+    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int64_t chb = (int64_t)blockIdx.x * kRhtCh, tokb = (int64_t)blockIdx.y * kRhtTok;
+    const int64_t ch0 = chb + cg * 8;
+    const int64_t tok0 = tokb + j * 16;
+    const float amax = *amax_src, amax_r = *amax_rht_src;
+    const float s_enc = tensor_scale(amax), s_enc_r = tensor_scale(amax_r);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        *o.amax = amax;
+        *o.s_enc = s_enc;
+        *o_rht.amax = amax_r;
+        *o_rht.s_enc = s_enc_r;
+    }
+    // channels is a multiple of 16, so both lanes of a row block are valid
+    // or neither is, and the shuffle partner is always active.
+    if (ch0 < channels && tok0 < tokens) {
+        uint4 raw[16];
+        load_rht_raw(x, ld, tok0, ch0, raw);
+
+        // row-wise blocks: token tok0 + i, channels ch0 .. ch0 + 7 of this lane
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int64_t tok = tok0 + i;
+            const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                v[2 * k] = bf16_lo(w[k]);
+                v[2 * k + 1] = bf16_hi(w[k]);
+            }
+            uint32_t mb = absmax8(raw[i]) << 16;  // fp32 bits of the lane's max |x|
+            mb = max(mb, (uint32_t)__shfl_xor((int)mb, 1, 64));
+            const uint32_t sb = block_scale(__uint_as_float(mb), s_enc);
+            const float f = block_factor(sb, s_enc);
+            uint32_t pk;
+            if constexpr (kSR)
+                pk = encode8_sr(v, f, seed, (uint64_t)(tok * channels + ch0) >> 3);
+            else
+                pk = encode8_rne(v, f);
+            *reinterpret_cast<uint32_t*>(o.codes + tok * o.ld_codes + (ch0 >> 1)) = pk;
+            if ((cg & 1) == 0) o.scales[tok * o.ld_scales + (ch0 >> 4)] = (uint8_t)sb;
+        }
+
+        // transformed blocks: channel ch0 + c, tokens tok0 .. tok0 + 15
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float v[16];
+            unpack_channel(raw, c, v);
+            rht16(v, mask);
+            const uint32_t sb = block_scale(absmax16(v), s_enc_r);
+            const float f = block_factor(sb, s_enc_r);
+            uint2 pk;
+            if constexpr (kSR)
+                pk = encode16_sr(v, f, seed_rht, (uint64_t)((ch0 + c) * tokens + tok0) >> 3);
+            else
+                pk = encode16_rne(v, f);
+            scodes[cg * 8 + c][j] = pk;
+            sscale[cg * 8 + c][j] = (uint8_t)sb;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int idx = it * 256 + threadIdx.x;
+        const int row = idx >> 4, q = idx & 15;
+        const int64_t ch = chb + row, tk = tokb + q * 16;
+        if (ch < channels && tk < tokens) {
+            *reinterpret_cast<uint2*>(o_rht.codes + ch * o_rht.ld_codes + (tk >> 1)) = scodes[row][q];
+            o_rht.scales[ch * o_rht.ld_scales + (tk >> 4)] = sscale[row][q];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
@@ -564,6 +677,26 @@ void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64
         hipLaunchKernelGGL(k_rht_quant<false>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
                            amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax,
                            o.s_enc);
+}
+
+void launch_dual_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld,
+                       uint32_t mask, int rounding, uint64_t seed, uint64_t seed_rht,
+                       const float* amax_src, const float* amax_rht_src, const QOut& o,
+                       const QOut& o_rht, hipStream_t s)
+{
+    if (tokens == 0 || channels == 0) {
+        hipLaunchKernelGGL(k_publish, dim3(1), dim3(1), 0, s, amax_src, o.amax, o.s_enc);
+        hipLaunchKernelGGL(k_publish, dim3(1), dim3(1), 0, s, amax_rht_src, o_rht.amax,
+                           o_rht.s_enc);
+        return;
+    }
+    dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
+    if (rounding == 1)
+        hipLaunchKernelGGL(k_dual_quant<true>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
+                           amax_src, amax_rht_src, seed, seed_rht, o, o_rht);
+    else
+        hipLaunchKernelGGL(k_dual_quant<false>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
+                           amax_src, amax_rht_src, seed, seed_rht, o, o_rht);
 }
 
 }  // namespace nvfp4

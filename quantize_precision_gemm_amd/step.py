@@ -30,8 +30,9 @@ class NVFP4Linear:
     Outputs: y (M x N, bf16), dx (M x K, bf16), dw (N x K, fp32).
     """
 
-    def __init__(self, q, torch, x, w, dy, seed):
+    def __init__(self, q, torch, x, w, dy, seed, fused_quant=False):
         self.q, self.torch = q, torch
+        self.fused_quant = fused_quant
         self.x, self.w, self.dy = x, w, dy
         M, K = x.shape
         N = w.shape[0]
@@ -55,26 +56,44 @@ class NVFP4Linear:
         return 3 * 2.0 * self.M * self.N * self.K
 
     # X and dY are each quantised twice (1x16, and through the RHT for
-    # wgrad): one fused pass computes both tensor maxima of each.
+    # wgrad): one fused pass computes both tensor maxima of each.  With
+    # fused_quant one encode pass also emits both operands of each tensor
+    # (nvfp4_quantize_dual), so X and dY are read twice per step instead of
+    # three times; the RHT encodes then run before fprop and dgrad instead of
+    # beside them on the second stream.
     def weight_ops(self):
         q = self.q
         return [("quant_W", lambda: q.nvfp4_quantize(self.w, q.BLOCK_16X16, q.RNE, out=self.gw))]
 
     def forward_ops(self):
         q = self.q
+        if self.fused_quant:
+            quant = ("dual_X", lambda: q.nvfp4_quantize_dual(
+                self.x, self.mask, q.RNE, amax_in=self.ax, amax_rht_in=self.ax_rht,
+                out=self.gx, out_rht=self.gxt))
+        else:
+            quant = ("quant_X", lambda: q.nvfp4_quantize(self.x, q.BLOCK_1X16, q.RNE,
+                                                         amax_in=self.ax, out=self.gx))
         return [
             ("amax_X", lambda: q.nvfp4_amax(self.x, self.mask, self.ax, self.ax_rht)),
-            ("quant_X", lambda: q.nvfp4_quantize(self.x, q.BLOCK_1X16, q.RNE, amax_in=self.ax,
-                                                 out=self.gx)),
+            quant,
             ("fprop", lambda: q.nvfp4_gemm(q.FPROP, self.gx, self.gw, out=self.y)),
         ]
 
-    def backward_amax_ops(self):
+    def backward_shared_ops(self):
+        """The backward work both branches (dgrad, wgrad) wait for."""
         q = self.q
-        return [("amax_dY", lambda: q.nvfp4_amax(self.dy, self.mask, self.ady, self.ady_rht))]
+        ops = [("amax_dY", lambda: q.nvfp4_amax(self.dy, self.mask, self.ady, self.ady_rht))]
+        if self.fused_quant:
+            ops.append(("dual_dY", lambda: q.nvfp4_quantize_dual(
+                self.dy, self.mask, q.SR, self.seed + SR_SEED_DY, self.seed + SR_SEED_DY_RHT,
+                amax_in=self.ady, amax_rht_in=self.ady_rht, out=self.gdy, out_rht=self.gdyt)))
+        return ops
 
     def backward_quant_ops(self):
         q = self.q
+        if self.fused_quant:
+            return []
         return [("quant_dY", lambda: q.nvfp4_quantize(self.dy, q.BLOCK_1X16, q.SR,
                                                       self.seed + SR_SEED_DY, amax_in=self.ady,
                                                       out=self.gdy))]
@@ -85,13 +104,16 @@ class NVFP4Linear:
 
     def wgrad_ops(self):
         q = self.q
+        wgrad = ("wgrad", lambda: q.nvfp4_gemm(q.WGRAD, self.gdyt, self.gxt, out=self.dw))
+        if self.fused_quant:
+            return [wgrad]
         return [
             ("rht_dY", lambda: q.nvfp4_rht_quantize(self.dy, self.mask, q.SR,
                                                     self.seed + SR_SEED_DY_RHT,
                                                     amax_in=self.ady_rht, out=self.gdyt)),
             ("rht_X", lambda: q.nvfp4_rht_quantize(self.x, self.mask, q.RNE,
                                                    amax_in=self.ax_rht, out=self.gxt)),
-            ("wgrad", lambda: q.nvfp4_gemm(q.WGRAD, self.gdyt, self.gxt, out=self.dw)),
+            wgrad,
         ]
 
 
@@ -121,7 +143,7 @@ class BF16Linear:
         q = self.q
         return [("bf16_fprop", lambda: q.nvfp4_bf16_gemm(q.FPROP, self.x, self.w, out=self.y))]
 
-    def backward_amax_ops(self):
+    def backward_shared_ops(self):
         return []
 
     def backward_quant_ops(self):
@@ -143,10 +165,11 @@ class TrainingStep:
     quantisation runs on a second stream from the start, beside the
     activations' amax and quantisation on the main stream, and each layer's
     fprop waits for its own weight.  Per layer in the backward pass, the
-    fused amax pass over dY runs on the main stream; then the main stream
-    quantises dY (SR) and runs dgrad while the wgrad branch (RHT operands,
-    which need only the maxima, and the wgrad GEMM) runs on the second
-    stream.  Wgrad feeds nothing later in the step, so it overlaps with dgrad
+    work both branches wait for runs on the main stream (the amax pass over
+    dY, plus the dual encode when the layer fuses its quantisers); then the
+    main stream quantises dY (SR, unless already done) and runs dgrad while
+    the wgrad branch (RHT operands, which need only the maxima, unless
+    already encoded, and the wgrad GEMM) runs on the second stream.  Wgrad feeds nothing later in the step, so it overlaps with dgrad
     and with the next layer's backward work: each GEMM's last, partial wave
     of workgroups is filled by the other's.  The step ends with the main
     stream waiting for the second one.
@@ -193,7 +216,7 @@ class TrainingStep:
             main.wait_event(ev)
             call(*ops[-1])  # the layer's fprop
         for layer in reversed(self.layers):
-            for n, f in layer.backward_amax_ops():
+            for n, f in layer.backward_shared_ops():
                 call(n, f)
             self.side.wait_stream(main)
             for n, f in layer.backward_quant_ops() + layer.dgrad_ops():
@@ -211,7 +234,7 @@ class TrainingStep:
             ops += [(i, n, f) for n, f in fw[:-1] + layer.weight_ops() + fw[-1:]]
         for i in reversed(range(len(self.layers))):
             layer = self.layers[i]
-            for part in (layer.backward_amax_ops(), layer.backward_quant_ops(), layer.dgrad_ops(),
+            for part in (layer.backward_shared_ops(), layer.backward_quant_ops(), layer.dgrad_ops(),
                          layer.wgrad_ops()):
                 ops += [(i, n, f) for n, f in part]
         return ops

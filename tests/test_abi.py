@@ -108,6 +108,31 @@ def test_rht_validation(lib):
     assert lib.nvfp4_rht_quantize(FAKE, 32, 16, 16, 1, 0, 0, None, ctypes.byref(d), None) == -2
 
 
+@pytest.mark.parametrize("case,status", [
+    # (tokens, channels, ld_x, rounding, amax, amax_rht, same descriptor, out_rht.ld_codes)
+    ((32, 24, 32, 0, None, None, False, 16), -2),    # channels not a multiple of 16
+    ((24, 32, 32, 0, None, None, False, 16), -2),    # tokens not a multiple of 16
+    ((32, 32, 32, 2, None, None, False, 16), -4),    # unknown rounding
+    ((32, 32, 32, 0, FAKE, None, False, 16), -1),    # only one of the two maxima
+    ((32, 32, 32, 0, None, FAKE, False, 16), -1),
+    ((32, 32, 32, 0, FAKE + 2, FAKE, False, 16), -3),  # misaligned amax
+    ((32, 32, 16, 0, None, None, False, 16), -2),    # ld_x < channels
+    ((32, 32, 36, 0, None, None, False, 16), -3),    # ld_x not a multiple of 8
+    ((32, 32, 32, 0, None, None, True, 16), -4),     # one descriptor for both results
+    ((32, 32, 32, 0, None, None, False, 0), -2),     # transposed result's rows too short
+])
+def test_dual_validation(lib, case, status):
+    tokens, channels, ld, rnd, am, amr, same, ldr = case
+    d = _desc(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, ld_codes=16, ld_scales=4)
+    dr = _desc(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, ld_codes=ldr, ld_scales=4)
+    st = lib.nvfp4_quantize_dual(FAKE, tokens, channels, ld, 1, rnd, 0, 0, am, amr,
+                                 ctypes.byref(d), ctypes.byref(d if same else dr), None)
+    assert st == status
+    d.codes_t = FAKE  # no transposed copies on either result
+    assert lib.nvfp4_quantize_dual(FAKE, 32, 32, 32, 1, 0, 0, 0, None, None, ctypes.byref(d),
+                                   ctypes.byref(dr), None) == -4
+
+
 @pytest.mark.parametrize("fn", ["nvfp4_gemm", "nvfp4_gemm_fp8blk"])
 def test_gemm_validation(lib, fn):
     gemm = getattr(lib, fn)
