@@ -27,6 +27,10 @@ _LIB_PATH = os.path.join(_HERE, "liboracle.so")
 
 BLOCK_1X16 = 0
 BLOCK_16X16 = 1
+BLOCK_MX32 = 2     # MXFP4: 32-element blocks, UE8M0 scales, no tensor scale
+MX_ROWS = 0        # MXFP4 layouts: blocks along the rows of x
+MX_COLS = 1        # the transposed matrix, blocks along the columns of x
+MX_COLS_RHT = 2    # as MX_COLS after the 16-point RHT of each 16-row chunk
 RNE = 0
 SR = 1
 
@@ -81,6 +85,10 @@ def lib():
         L.orc_gemm_fp32.argtypes = [P, P, ctypes.c_int, ctypes.c_float, P, P, ctypes.c_int,
                                     ctypes.c_float, i64, i64, i64, P]
         L.orc_gemm_fp32.restype = ctypes.c_int
+        L.orc_mx_quantize.argtypes = [P, i64, i64, ctypes.c_int, u32, ctypes.c_int, u64, P, P]
+        L.orc_mx_quantize.restype = ctypes.c_int
+        L.orc_mx_exponent.argtypes = [ctypes.c_float]
+        L.orc_mx_exponent.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -224,6 +232,34 @@ def rht_quantize(x_u16, sign_mask, rounding=RNE, seed=0, amax_in=None, idx0=0):
     return QTensor(codes, scales, float(amax[0]), float(s_enc[0]), channels, tokens, BLOCK_1X16)
 
 
+def mx_exponent(amax_b):
+    """Shared exponent of an MXFP4 block with max |x| = amax_b."""
+    return int(lib().orc_mx_exponent(amax_b))
+
+
+def mx_quantize(x_u16, mode=MX_ROWS, sign_mask=0, rounding=RNE, seed=0):
+    """MXFP4 quantisation (the format NVFP4 is compared with, Technische
+    Zusammenfassung 2.A): E2M1 codes, one UE8M0 scale per 32 elements.
+
+    mode MX_ROWS: blocks along the rows of x, result rows x cols;
+    MX_COLS: the transposed matrix (blocks along the columns of x), result
+    cols x rows; MX_COLS_RHT: MX_COLS after the 16-point RHT of every
+    16-row chunk of each column (2.B.2).  SR draws are indexed in the
+    result's layout.  Returns a QTensor with block BLOCK_MX32 (amax and
+    s_enc are None: MXFP4 has no tensor scale).
+    """
+    x = _u16(x_u16)
+    rows, cols = x.shape
+    orows, ocols = (rows, cols) if mode == MX_ROWS else (cols, rows)
+    codes = np.zeros((orows, ocols // 2), np.uint8)
+    scales = np.zeros((orows, ocols // 32), np.uint8)
+    rc = lib().orc_mx_quantize(_ptr(x), rows, cols, mode, sign_mask, rounding, seed, _ptr(codes),
+                               _ptr(scales))
+    if rc != 0:
+        raise ValueError(f"orc_mx_quantize: status {rc}")
+    return QTensor(codes, scales, None, None, orows, ocols, BLOCK_MX32)
+
+
 def rht_transform(x_u16, sign_mask):
     """fp32 channels x tokens transform of a tokens x channels bf16 matrix."""
     x = _u16(x_u16)
@@ -311,6 +347,22 @@ def dequantize_qs(q: QTensor):
     else:
         S = np.repeat(np.repeat(S, 16, axis=0), 16, axis=1)
     return vals * S
+
+
+def mx_dequantize(q: QTensor):
+    """x^ = q * 2^(scale - 127) (fp64) of an MXFP4 tensor."""
+    codes = unpack_codes(q.codes, q.cols)
+    S = np.ldexp(1.0, q.scales.astype(np.int64) - 127)
+    return E2M1_VALUES[codes] * np.repeat(S, 32, axis=1)
+
+
+def mx_gemm(a: QTensor, b: QTensor, rows=None):
+    """fp64 GEMM of dequantised MXFP4 operands, both rows x K:
+    C[m, n] = sum_k a^[m, k] b^[n, k].  rows: optional output rows."""
+    A = mx_dequantize(a)
+    if rows is not None:
+        A = A[np.asarray(rows)]
+    return A @ mx_dequantize(b).T
 
 
 def dequantize(q: QTensor):

@@ -456,6 +456,102 @@ int orc_rht_quantize(const uint16_t* x, int64_t tokens, int64_t channels, uint32
 }
 
 /* ------------------------------------------------------------------------ */
+/* MXFP4, the format NVFP4 is compared with ([P1] TZ 2.A).                  */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * [P1] TZ 2.A sets NVFP4 against MXFP4: E2M1 elements in blocks of 32 that
+ * share a power-of-two scale stored as UE8M0, with no tensor-level scale.
+ * The pages stop there.  Reading (the OCP Microscaling Formats
+ * specification, v1.0, which defines MXFP4): the shared exponent of a block
+ * is floor(log2(amax_b)) - 2, where 2 is the exponent of E2M1's largest
+ * value 6 = 1.5 * 2^2, clamped to the UE8M0 range [-127, 127]; an all-zero
+ * block takes -127.  The scale byte is the exponent + 127.  Inputs are
+ * finite.
+ */
+int orc_mx_exponent(float amax_b)
+{
+    if (!(amax_b > 0.0f)) return -127;
+    int ex;
+    (void)frexpf(amax_b, &ex);  /* amax_b = m * 2^ex, m in [0.5, 1) */
+    int e = (ex - 1) - 2;       /* floor(log2(amax_b)) - 2 */
+    if (e < -127) e = -127;
+    if (e > 127) e = 127;
+    return e;
+}
+
+/*
+ * The 32 values of MX block b of output row r (fp32), for the three
+ * layouts of orc_mx_quantize.
+ */
+static void mx_block_values(const uint16_t* x, int64_t rows, int64_t cols, int mode,
+                            uint32_t sign_mask, int64_t r, int64_t b, float* v)
+{
+    if (mode == 0) {
+        for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(x[r * cols + 32 * b + i]);
+        return;
+    }
+    /* modes 1, 2: output row r is input column r; block b is input rows 32b.. */
+    for (int i = 0; i < 32; ++i) v[i] = bf16_to_f32(x[(32 * b + i) * cols + r]);
+    if (mode == 2) {
+        float w[16];
+        for (int h = 0; h < 2; ++h) {
+            orc_rht16(v + 16 * h, sign_mask, w);
+            for (int i = 0; i < 16; ++i) v[16 * h + i] = w[i];
+        }
+    }
+    (void)rows;
+}
+
+/*
+ * MXFP4 quantisation of a row-major bf16 matrix x (rows x cols).
+ *   mode 0: blocks of 32 along each row; output rows x cols.
+ *   mode 1: the transposed matrix, blocks of 32 along each column of x;
+ *           output cols x rows.
+ *   mode 2: as mode 1 after the 16-point random Hadamard transform of every
+ *           aligned 16-row chunk of each column (orc_rht16, sign_mask) --
+ *           the wgrad operand of the recipe, [P1] TZ 2.B.2.
+ * Each element: y = v * 2^-e (fp32; exact unless it underflows, where every
+ * rounding gives a zero of the same sign), coded onto the E2M1 grid by RNE
+ * (saturating) or by SR with the draw of its index r * out_cols + c in the
+ * output layout ([P1] TZ 2.B.4), exactly as for NVFP4.
+ * codes: out_rows x out_cols/2; scales: out_rows x out_cols/32 (UE8M0).
+ */
+int orc_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int mode, uint32_t sign_mask,
+                    int rounding, uint64_t seed, uint8_t* codes, uint8_t* scales)
+{
+    if (rows < 0 || cols < 0) return ORC_ERR_SHAPE;
+    if (mode < 0 || mode > 2) return ORC_ERR_MODE;
+    if (rounding != ORC_RNE && rounding != ORC_SR) return ORC_ERR_MODE;
+    if (mode == 0 && cols % 32 != 0) return ORC_ERR_SHAPE;
+    if (mode != 0 && rows % 32 != 0) return ORC_ERR_SHAPE;
+    const int64_t out_rows = mode == 0 ? rows : cols;
+    const int64_t out_cols = mode == 0 ? cols : rows;
+    const int64_t nb = out_cols / 32;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < out_rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float v[32];
+            mx_block_values(x, rows, cols, mode, sign_mask, r, b, v);
+            float am = 0.0f;
+            for (int i = 0; i < 32; ++i)
+                if (fabsf(v[i]) > am) am = fabsf(v[i]);
+            const int e = orc_mx_exponent(am);
+            scales[r * nb + b] = (uint8_t)(e + 127);
+            const float f = ldexpf(1.0f, -e);
+            for (int i = 0; i < 32; ++i) {
+                const float y = v[i] * f;
+                const int64_t c = 32 * b + i;
+                const uint8_t code = (rounding == ORC_RNE)
+                                         ? orc_e2m1_encode_rne(y)
+                                         : orc_e2m1_encode_sr(y, orc_sr_draw(seed, (uint64_t)(r * out_cols + c)));
+                put_code(codes + r * (out_cols / 2), c, code);
+            }
+        }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* Diagnostic GEMM with fp32 accumulation.                                  */
 /* ------------------------------------------------------------------------ */
 

@@ -145,3 +145,31 @@ def quantize_blocks(x_bits, blocks, draws=None):
                 c = sr_e2m1_code(y, draws[i])
             codes[i] = (sgn << 3) | c
     return codes, sbytes, amax, s_enc
+
+
+# --- MXFP4 (32-element blocks, UE8M0 scales, no tensor scale) --------------
+
+def mx_exponent(amax):
+    """The shared exponent e of an MXFP4 block: the integer with
+    4 <= amax * 2^-e < 8 (amax * 2^-e then rounds onto [4, 6], the top binade
+    of E2M1), clamped to [-127, 127]; -127 for amax = 0.  Found by search."""
+    if amax == 0:
+        return -127
+    e = 0
+    while amax * F(2) ** -e >= 8:
+        e += 1
+    while amax * F(2) ** -e < 4:
+        e -= 1
+    return min(max(e, -127), 127)
+
+
+def mx_quantize_block(x_bits, draws=None):
+    """(codes, scale byte) of one MXFP4 block given as bf16 bit patterns."""
+    vals = [bf16_bits_to_fraction(u) for u in x_bits]
+    e = mx_exponent(max(v for _, v in vals))
+    codes = []
+    for i, (sgn, mag) in enumerate(vals):
+        y = round_f32(mag * F(2) ** -e)
+        c = nearest_e2m1_code(y) if draws is None else sr_e2m1_code(y, draws[i])
+        codes.append((sgn << 3) | c)
+    return codes, e + 127
