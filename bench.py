@@ -44,6 +44,7 @@ M, K, N = 8192, 5120, 20480
 SEED = 0
 PEAK_F16_TFLOPS = 2500.0   # MI355X dense fp16/bf16 MFMA
 PEAK_HBM_GBPS = 8000.0     # MI355X HBM3E
+PEAK_FP4_TFLOPS = 10100.0  # MI355X dense fp4/fp6 MFMA
 
 
 def gemm_source_hash():
@@ -93,6 +94,54 @@ def quant_bytes():
             "quant_W": 2 * e_w + 2 * e_w + 2 * (e_w // 2 + e_w // 256),
             "amax_dY": 2 * e_dy, "quant_dY": enc(e_dy), "rht_dY": enc(e_dy), "rht_X": enc(e_x),
             "dual_dY": enc2(e_dy), "dual_X": enc2(e_x)}
+
+
+def mx_comparison(q, torch, layer, reps=5):
+    """The layer's three GEMMs in the comparison format MXFP4 (32-element
+    blocks, UE8M0 scales) on the native block-scaled FP4 MFMA, on the same
+    bf16 tensors: each operand quantised in the layout its pass contracts
+    over, then every GEMM and quantiser timed serialised with events."""
+    m = layer.mask
+    # name: (tensor, layout, sign mask, rounding, seed)
+    quants = {
+        "X rows (fprop)": (layer.x, q.MX_ROWS, 0, q.RNE, 0),
+        "W rows (fprop)": (layer.w, q.MX_ROWS, 0, q.RNE, 0),
+        "W cols (dgrad)": (layer.w, q.MX_COLS, 0, q.RNE, 0),
+        "dY rows SR (dgrad)": (layer.dy, q.MX_ROWS, 0, q.SR, 100),
+        "dY cols RHT SR (wgrad)": (layer.dy, q.MX_COLS_RHT, m, q.SR, 101),
+        "X cols RHT (wgrad)": (layer.x, q.MX_COLS_RHT, m, q.RNE, 0),
+    }
+    ops = {k: q.nvfp4_mx_quantize(*a) for k, a in quants.items()}
+    gemms = {
+        "fprop": (ops["X rows (fprop)"], ops["W rows (fprop)"], torch.bfloat16),
+        "dgrad": (ops["dY rows SR (dgrad)"], ops["W cols (dgrad)"], torch.bfloat16),
+        "wgrad": (ops["dY cols RHT SR (wgrad)"], ops["X cols RHT (wgrad)"], torch.float32),
+    }
+    outs = {k: q.nvfp4_mx_gemm(a, b, dt) for k, (a, b, dt) in gemms.items()}
+    torch.cuda.synchronize()
+
+    def timed(f):
+        f()
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        for _ in range(reps):
+            f()
+        e_.record()
+        torch.cuda.synchronize()
+        return s_.elapsed_time(e_) / reps
+
+    flop = 2.0 * layer.M * layer.N * layer.K
+    gemm_ms = {k: timed(lambda a=a, b=b, o=outs[k]: q.nvfp4_mx_gemm(a, b, out=o))
+               for k, (a, b, _) in gemms.items()}
+    quant_ms = {k: timed(lambda a=a, o=ops[k]: q.nvfp4_mx_quantize(*a, out=o))
+                for k, a in quants.items()}
+    tf = {k: flop / (v * 1e-3) / 1e12 for k, v in gemm_ms.items()}
+    return {"gemm_tflops": {k: round(v, 1) for k, v in tf.items()},
+            "gemm_ms": {k: round(v, 4) for k, v in gemm_ms.items()},
+            "frac_of_fp4_peak": {k: round(v / PEAK_FP4_TFLOPS, 4) for k, v in tf.items()},
+            "quantize_ms": {k: round(v, 4) for k, v in quant_ms.items()},
+            "kernel": "k_gemm_mx (v_mfma_scale_f32_32x32x64_f8f6f4, fp4 operands)",
+            "peak_tflops": PEAK_FP4_TFLOPS}
 
 
 def cpu_baseline(data, tokens=M):
@@ -273,6 +322,8 @@ def main():
             fp8[name] = 2.0 * L.M * L.N * L.K / (s_.elapsed_time(e_) / 3 * 1e-3) / 1e12
         datapaths = fp8
 
+    mx = None if mlp else mx_comparison(q, torch, step.layers[0])
+
     ms_step = wall * 1e3 / steps
     layer0 = step.layers[0]
     gemm_flop = 2.0 * layer0.M * layer0.N * layer0.K   # equal for every layer here
@@ -331,6 +382,10 @@ def main():
         result["quantize_frac_of_hbm_peak"] = {
             k: round(qb[k] / (avg[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3) for k in qb}
         result["ms_per_op"] = {k: round(v, 4) for k, v in avg.items()}
+    if mx is not None:
+        mx["speedup_vs_nvfp4"] = {k: round(v / result["gemm_tflops"][k], 2)
+                                  for k, v in mx["gemm_tflops"].items()}
+        result["mxfp4_comparison"] = mx
     result["roofline"] = {
         "kernel": "k_gemm_nv<bf16 out> (fprop, dgrad launches)", "bound": "mfma",
         "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",

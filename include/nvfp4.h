@@ -56,6 +56,12 @@ extern "C" {
 /* Block layouts. */
 #define NVFP4_BLOCK_1X16 0      /* one scale per 16 consecutive elements of a row */
 #define NVFP4_BLOCK_16X16 1     /* one scale per 16x16 tile (weights) */
+#define NVFP4_BLOCK_MX32 2      /* MXFP4: one UE8M0 scale per 32 elements of a row */
+
+/* MXFP4 quantiser layouts (nvfp4_mx_quantize). */
+#define NVFP4_MX_ROWS 0         /* blocks along the rows of x; result rows x cols */
+#define NVFP4_MX_COLS 1         /* the transposed matrix; result cols x rows */
+#define NVFP4_MX_COLS_RHT 2     /* as NVFP4_MX_COLS after the 16-point RHT */
 
 /* Rounding of the elements. */
 #define NVFP4_RNE 0             /* round to nearest, ties to even */
@@ -284,6 +290,55 @@ int nvfp4_gemm_fp8blk(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b
 int nvfp4_bf16_gemm(int32_t pass, const void* a, int64_t lda, const void* b, int64_t ldb,
                     int64_t M, int64_t N, int64_t K, void* c, int64_t ldc, int32_t c_dtype,
                     void* stream);
+
+/*
+ * nvfp4_mx_quantize -- MXFP4 quantisation, the format NVFP4 is compared with.
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.A (MXFP4: E2M1 elements in blocks of 32 sharing one
+ * UE8M0 power-of-two scale, no tensor-level scale); the conversion rule is
+ * the OCP Microscaling v1.0 one: shared exponent e = floor(log2(amax_b)) - 2
+ * clamped to [-127, 127] (-127 for an all-zero block), scale byte e + 127,
+ * element code = E2M1 rounding (RNE saturating, or SR as for
+ * nvfp4_quantize) of x * 2^-e.
+ *   x         device bf16, rows x ld_x elements, row-major; 16-byte aligned,
+ *             ld_x >= cols and a multiple of 8.
+ *   mode      NVFP4_MX_ROWS: blocks along the rows (cols a multiple of 32);
+ *             result rows x cols.
+ *             NVFP4_MX_COLS: the transposed matrix, blocks along the columns
+ *             of x (rows a multiple of 32, cols of 8); result cols x rows.
+ *             NVFP4_MX_COLS_RHT: as NVFP4_MX_COLS after the 16-point random
+ *             Hadamard transform of every 16-row chunk of each column, with
+ *             sign_mask as in nvfp4_rht_quantize (the wgrad operand, 2.B.2).
+ *   rounding, seed  NVFP4_RNE or NVFP4_SR; the draw of result element (r, c)
+ *             is indexed r * result_cols + c (2.B.4).
+ *   out       descriptor: codes (result rows x ld_codes, as for NVFP4) and
+ *             scales (result rows x ld_scales bytes, ld_scales a multiple of
+ *             4 and >= result_cols / 32; 4-byte aligned); codes_t and
+ *             scales_t must be NULL; amax and s_enc are not used.  rows,
+ *             cols and block (NVFP4_BLOCK_MX32) are filled in.
+ * Returns NVFP4_OK or a negative status; nothing is launched on error.
+ */
+int nvfp4_mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t mode,
+                      uint32_t sign_mask, int32_t rounding, uint64_t seed, nvfp4_tensor* out,
+                      void* stream);
+
+/*
+ * nvfp4_mx_gemm -- GEMM over MXFP4 operands on gfx950's block-scaled FP4
+ * matrix instructions, fp32 accumulation:
+ *   c[m, n] = sum_k a^[m, k] * b^[n, k]     (a: M x K, b: N x K, both
+ *   MXFP4 with blocks along K; x^ = code value * 2^(scale - 127)).
+ * The three passes of a linear layer take operands quantised accordingly:
+ * fprop (X, W) with NVFP4_MX_ROWS; dgrad (dY with NVFP4_MX_ROWS, W with
+ * NVFP4_MX_COLS); wgrad (dY and X with NVFP4_MX_COLS or NVFP4_MX_COLS_RHT).
+ * Defines: the comparison of Technische Zusammenfassung 2.A, measured as the
+ * speed of the 2.B.2 GEMMs in the other format.
+ *   a, b      MXFP4 descriptors (block NVFP4_BLOCK_MX32) with equal cols = K,
+ *             a multiple of 32.
+ *   c, ldc, c_dtype  as for nvfp4_gemm (no alpha: MXFP4 has no tensor scale).
+ * Returns NVFP4_OK or a negative status; nothing is enqueued on failure.
+ */
+int nvfp4_mx_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t ldc,
+                  int32_t c_dtype, void* stream);
 
 /* Human-readable name of a status code (static string). */
 const char* nvfp4_status_string(int32_t status);

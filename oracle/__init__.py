@@ -359,10 +359,10 @@ def mx_dequantize(q: QTensor):
 def mx_gemm(a: QTensor, b: QTensor, rows=None):
     """fp64 GEMM of dequantised MXFP4 operands, both rows x K:
     C[m, n] = sum_k a^[m, k] b^[n, k].  rows: optional output rows."""
-    A = mx_dequantize(a)
     if rows is not None:
-        A = A[np.asarray(rows)]
-    return A @ mx_dequantize(b).T
+        rows = np.asarray(rows)
+        a = QTensor(a.codes[rows], a.scales[rows], None, None, len(rows), a.cols, a.block)
+    return mx_dequantize(a) @ mx_dequantize(b).T
 
 
 def dequantize(q: QTensor):

@@ -20,11 +20,16 @@ import torch
 __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_gemm",
-    "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_gemm_fp8blk", "lib_path", "load_library",
+    "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_mx_quantize",
+    "nvfp4_mx_gemm", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "lib_path", "load_library",
 ]
 
 BLOCK_1X16 = 0
 BLOCK_16X16 = 1
+BLOCK_MX32 = 2     # MXFP4 comparison format: 32-element blocks, UE8M0 scales
+MX_ROWS = 0        # nvfp4_mx_quantize layouts
+MX_COLS = 1
+MX_COLS_RHT = 2
 RNE = 0
 SR = 1
 FPROP = 0
@@ -73,6 +78,10 @@ def load_library():
         L.nvfp4_rht_quantize.restype = ctypes.c_int
         L.nvfp4_quantize_dual.argtypes = [P, i64, i64, i64, u32, i32, u64, u64, P, P, D, D, P]
         L.nvfp4_quantize_dual.restype = ctypes.c_int
+        L.nvfp4_mx_quantize.argtypes = [P, i64, i64, i64, i32, u32, i32, u64, D, P]
+        L.nvfp4_mx_quantize.restype = ctypes.c_int
+        L.nvfp4_mx_gemm.argtypes = [D, D, P, i64, i32, P]
+        L.nvfp4_mx_gemm.restype = ctypes.c_int
         L.nvfp4_gemm.argtypes = [i32, D, D, P, i64, i32, P]
         L.nvfp4_gemm.restype = ctypes.c_int
         L.nvfp4_gemm_fp8blk.argtypes = [i32, D, D, P, i64, i32, P]
@@ -141,7 +150,8 @@ class NVFP4Tensor:
         return self.codes[:, : self.cols // 2].cpu().numpy()
 
     def scales_host(self):
-        return self.scales[:, : self.cols // 16].cpu().numpy()
+        per = 32 if self.block == BLOCK_MX32 else 16
+        return self.scales[:, : self.cols // per].cpu().numpy()
 
     def codes_t_host(self):
         return self.codes_t[:, : self.rows // 2].cpu().numpy()
@@ -154,8 +164,8 @@ def alloc_nvfp4(rows, cols, block=BLOCK_1X16, with_transpose=False, device=None)
     """Allocate the device buffers of a rows x cols NVFP4 tensor (padded leading dims)."""
     device = device or torch.device("cuda", torch.cuda.current_device())
     ld_c = _round_up(cols, 32) // 2
-    ld_s = _round_up(max(cols // 16, 1), 4)
-    srows = rows if block == BLOCK_1X16 else rows // 16
+    ld_s = _round_up(max(cols // (32 if block == BLOCK_MX32 else 16), 1), 4)
+    srows = rows // 16 if block == BLOCK_16X16 else rows
     codes = torch.empty((rows, ld_c), dtype=torch.uint8, device=device)
     scales = torch.empty((srows, ld_s), dtype=torch.uint8, device=device)
     amax = torch.empty(1, dtype=torch.float32, device=device)
@@ -227,6 +237,38 @@ def nvfp4_quantize_dual(x, sign_mask, rounding=RNE, seed=0, seed_rht=0, amax_in=
     out.rows, out.cols, out.block = d.rows, d.cols, d.block
     out_rht.rows, out_rht.cols, out_rht.block = dr.rows, dr.cols, dr.block
     return out, out_rht
+
+
+def nvfp4_mx_quantize(x, mode=MX_ROWS, sign_mask=0, rounding=RNE, seed=0, out=None, stream=None):
+    """MXFP4 quantisation (see nvfp4_mx_quantize in nvfp4.h); MX_ROWS gives
+    rows x cols, MX_COLS / MX_COLS_RHT the transposed cols x rows."""
+    _check_bf16(x)
+    rows, cols = x.shape
+    orows, ocols = (rows, cols) if mode == MX_ROWS else (cols, rows)
+    if out is None:
+        out = alloc_nvfp4(orows, ocols, BLOCK_MX32, False, x.device)
+    d = out.descriptor()
+    ld_x = x.stride(0) if cols > 0 else 0
+    st = load_library().nvfp4_mx_quantize(_ptr(x), rows, cols, ld_x, mode, sign_mask, rounding,
+                                          seed, ctypes.byref(d), _stream(stream))
+    _check(st, "nvfp4_mx_quantize")
+    out.rows, out.cols, out.block = d.rows, d.cols, d.block
+    return out
+
+
+def nvfp4_mx_gemm(a, b, out_dtype=torch.bfloat16, out=None, stream=None):
+    """c = a^ b^T over MXFP4 operands (see nvfp4_mx_gemm in nvfp4.h)."""
+    M, N = a.rows, b.rows
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
+        raise TypeError("output must be float32 or bfloat16 with a contiguous last dimension")
+    dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    da, db = a.descriptor(), b.descriptor()
+    st = load_library().nvfp4_mx_gemm(ctypes.byref(da), ctypes.byref(db), _ptr(out),
+                                      out.stride(0) if N > 0 else 0, dt, _stream(stream))
+    _check(st, "nvfp4_mx_gemm")
+    return out
 
 
 def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None, fp8_blocks=False):

@@ -74,6 +74,20 @@ int check_operand(const nvfp4_tensor* t)
     return NVFP4_OK;
 }
 
+
+// Checks of an MXFP4 descriptor (rows x cols, blocks of 32 along cols).
+// need_data: the codes and scales must be present (a non-empty tensor).
+int check_mx(const nvfp4_tensor* t, int64_t rows, int64_t cols)
+{
+    if (!t) return NVFP4_ERR_NULL;
+    if (rows > 0 && cols > 0 && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
+    if (t->codes_t || t->scales_t) return NVFP4_ERR_MODE;
+    if (!aligned(t->codes, 16) || t->ld_codes % 16 != 0) return NVFP4_ERR_ALIGN;
+    if (!aligned(t->scales, 4) || t->ld_scales % 4 != 0) return NVFP4_ERR_ALIGN;
+    if (t->ld_codes < round_up(cols, 32) / 2 || t->ld_scales < cols / 32) return NVFP4_ERR_SHAPE;
+    return NVFP4_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -287,6 +301,60 @@ int nvfp4_gemm_fp8blk(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b
                       int64_t ldc, int32_t c_dtype, void* stream)
 {
     return gemm_nvfp4(pass, a, b, c, ldc, c_dtype, stream, true);
+}
+
+int nvfp4_mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t mode,
+                      uint32_t sign_mask, int32_t rounding, uint64_t seed, nvfp4_tensor* out,
+                      void* stream)
+{
+    if (mode != NVFP4_MX_ROWS && mode != NVFP4_MX_COLS && mode != NVFP4_MX_COLS_RHT)
+        return NVFP4_ERR_MODE;
+    if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_MODE;
+    if (rows < 0 || cols < 0) return NVFP4_ERR_SHAPE;
+    if (mode == NVFP4_MX_ROWS && cols % 32 != 0) return NVFP4_ERR_SHAPE;
+    if (mode != NVFP4_MX_ROWS && (rows % 32 != 0 || cols % 8 != 0)) return NVFP4_ERR_SHAPE;
+    if (!x && rows > 0 && cols > 0) return NVFP4_ERR_NULL;
+    if (ld_x < cols) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld_x % 8 != 0) return NVFP4_ERR_ALIGN;
+    const int64_t orows = mode == NVFP4_MX_ROWS ? rows : cols;
+    const int64_t ocols = mode == NVFP4_MX_ROWS ? cols : rows;
+    int st = check_mx(out, orows, ocols);
+    if (st != NVFP4_OK) return st;
+
+    QOut q{};
+    q.codes = out->codes;
+    q.ld_codes = out->ld_codes;
+    q.scales = out->scales;
+    q.ld_scales = out->ld_scales;
+    nvfp4::launch_mx_quant(static_cast<const uint16_t*>(x), rows, cols, ld_x, mode,
+                           sign_mask & 0xFFFFu, rounding, seed, q, static_cast<hipStream_t>(stream));
+    out->rows = orows;
+    out->cols = ocols;
+    out->block = NVFP4_BLOCK_MX32;
+    return launch_status();
+}
+
+int nvfp4_mx_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t ldc,
+                  int32_t c_dtype, void* stream)
+{
+    if (c_dtype != NVFP4_OUT_BF16 && c_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_MODE;
+    if (!a || !b) return NVFP4_ERR_NULL;
+    if (a->block != NVFP4_BLOCK_MX32 || b->block != NVFP4_BLOCK_MX32) return NVFP4_ERR_MISMATCH;
+    if (a->rows < 0 || b->rows < 0 || a->cols < 0 || a->cols % 32 != 0) return NVFP4_ERR_SHAPE;
+    if (b->cols != a->cols) return NVFP4_ERR_MISMATCH;
+    int st = check_mx(a, a->rows, a->cols);
+    if (st != NVFP4_OK) return st;
+    st = check_mx(b, b->rows, b->cols);
+    if (st != NVFP4_OK) return st;
+    const int64_t M = a->rows, N = b->rows, K = a->cols;
+    if (!c && M > 0 && N > 0) return NVFP4_ERR_NULL;
+    if (!aligned(c, c_dtype == NVFP4_OUT_FP32 ? 16 : 8) || ldc % 4 != 0) return NVFP4_ERR_ALIGN;
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    const GemmOperand A{a->codes, a->ld_codes, a->scales, a->ld_scales, 0, nullptr};
+    const GemmOperand B{b->codes, b->ld_codes, b->scales, b->ld_scales, 0, nullptr};
+    nvfp4::launch_gemm_mx(A, B, M, N, K, c, ldc, c_dtype == NVFP4_OUT_FP32,
+                          static_cast<hipStream_t>(stream));
+    return launch_status();
 }
 
 int nvfp4_bf16_gemm(int32_t pass, const void* a, int64_t lda, const void* b, int64_t ldb,

@@ -360,6 +360,192 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
 namespace {
 
 // ---------------------------------------------------------------------------
+// MXFP4 x MXFP4 -- the format NVFP4 is compared with (32-element blocks, one
+// UE8M0 power-of-two scale each, no tensor scale).
+//
+// gfx950's block-scaled MFMA v_mfma_scale_f32_32x32x64_f8f6f4 with FP4
+// operands reads E2M1 codes directly with one E8M0 scale per lane: lane l
+// supplies row (A) or column (B) l % 32 and the 32 consecutive k of half
+// l / 32 of its 64-wide step -- exactly one MX block, 16 code bytes -- so the
+// operands enter the matrix cores as stored, with no decode.  Same tile,
+// wave grid, three register stages, LDS double buffer and epilogue as
+// k_gemm_nv; a K step is 128 (4 blocks, 64 code bytes per row) in two MFMA
+// sub-steps of 64.  LDS stage: A and B codes as 256 rows of 80 bytes (64 +
+// pad: 16-byte reads of 16 consecutive rows hit distinct banks), then each
+// row's 4 scale bytes for A and for B.  Thread t loads half h = t % 2 of
+// tile row t / 2 of both operands: 32 code bytes (blocks 2h, 2h+1) and 2
+// scale bytes each.
+// ---------------------------------------------------------------------------
+
+constexpr int kMxKS = 128;
+constexpr int kMxRow = 80;
+constexpr int kMxOp = 256 * kMxRow;
+constexpr int kMxStage = 2 * kMxOp + 2 * 256 * 4;
+
+typedef int v8i_t __attribute__((ext_vector_type(8)));
+
+struct MxRow {             // one thread's share of a K step
+    uint4 a0, a1, b0, b1;  // 32 code bytes of its A and B half rows
+    uint32_t s;            // A scales in bytes 0-1, B scales in bytes 2-3
+};
+
+__device__ __forceinline__ v8i_t mx_frag(const uint8_t* p)
+{
+    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    return v8i_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
+}
+
+}  // namespace
+
+template <bool kOutF32>
+__global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t M, int64_t N,
+                                                    int64_t K, void* __restrict__ c, int64_t ldc)
+{
+    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMxStage];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int g = lane >> 5, lr = lane & 31;
+    int64_t tile_m, tile_n;
+    tile_of(M, N, tile_m, tile_n);
+
+    // half h of tile row `row` (rows past the operand re-read its last row;
+    // they are never stored)
+    const int row = tid >> 1, h = tid & 1;
+    int64_t ra = tile_m * kBM + row, rb = tile_n * kBN + row;
+    ra = ra < M ? ra : M - 1;
+    rb = rb < N ? rb : N - 1;
+    const uint8_t* pa = static_cast<const uint8_t*>(A.data) + ra * A.ld + 32 * h;
+    const uint8_t* pb = static_cast<const uint8_t*>(B.data) + rb * B.ld + 32 * h;
+    const uint8_t* psa = A.scales + ra * A.ld_scales + 2 * h;
+    const uint8_t* psb = B.scales + rb * B.ld_scales + 2 * h;
+    const int64_t nblk = K >> 5;
+
+    auto load_full = [&](int64_t k0, MxRow& w) {
+        const uint4* qa = reinterpret_cast<const uint4*>(pa + (k0 >> 1));
+        const uint4* qb = reinterpret_cast<const uint4*>(pb + (k0 >> 1));
+        w.a0 = qa[0];
+        w.a1 = qa[1];
+        w.b0 = qb[0];
+        w.b1 = qb[1];
+        const uint32_t sa = *reinterpret_cast<const uint16_t*>(psa + (k0 >> 5));
+        const uint32_t sb = *reinterpret_cast<const uint16_t*>(psb + (k0 >> 5));
+        w.s = sa | (sb << 16);
+    };
+    // partial last step: blocks past K get zero codes (whatever their scale,
+    // they add zero); each 16-byte piece is one whole block
+    auto load_tail = [&](int64_t k0, MxRow& w) {
+        const int64_t b0 = (k0 >> 5) + 2 * h;
+        const uint4 z = make_uint4(0, 0, 0, 0);
+        const uint4* qa = reinterpret_cast<const uint4*>(pa + (k0 >> 1));
+        const uint4* qb = reinterpret_cast<const uint4*>(pb + (k0 >> 1));
+        w.a0 = b0 < nblk ? qa[0] : z;
+        w.b0 = b0 < nblk ? qb[0] : z;
+        w.a1 = b0 + 1 < nblk ? qa[1] : z;
+        w.b1 = b0 + 1 < nblk ? qb[1] : z;
+        uint32_t s = 0u;
+        for (int j = 0; j < 2; ++j)
+            if (b0 + j < nblk)
+                s |= ((uint32_t)psa[(k0 >> 5) + j] << (8 * j)) |
+                     ((uint32_t)psb[(k0 >> 5) + j] << (16 + 8 * j));
+        w.s = s;
+    };
+    auto put = [&](const MxRow& w, int st) {
+        uint8_t* base = lds + st * kMxStage;
+        uint4* da = reinterpret_cast<uint4*>(base + row * kMxRow + 32 * h);
+        uint4* db = reinterpret_cast<uint4*>(base + kMxOp + row * kMxRow + 32 * h);
+        da[0] = w.a0;
+        da[1] = w.a1;
+        db[0] = w.b0;
+        db[1] = w.b1;
+        uint16_t* sc = reinterpret_cast<uint16_t*>(base + 2 * kMxOp);
+        sc[row * 2 + h] = (uint16_t)w.s;
+        sc[512 + row * 2 + h] = (uint16_t)(w.s >> 16);
+    };
+
+    float16_t acc[4][2];
+    zero_acc(acc);
+    const int wm = wave >> 2, wn = wave & 3;
+    const int a_row = wm * 128 + lr;  // + 32 tm
+    const int b_row = wn * 64 + lr;   // + 32 tn
+
+    auto compute = [&](int st) {
+        const uint8_t* As = lds + st * kMxStage;
+        const uint8_t* Bs = As + kMxOp;
+        const uint32_t* Sa = reinterpret_cast<const uint32_t*>(As + 2 * kMxOp);
+        const uint32_t* Sb = Sa + 256;
+        uint32_t sa[4], sb[2];  // this lane's 4 block scales of the step, per fragment row
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm) sa[tm] = Sa[a_row + 32 * tm];
+#pragma unroll
+        for (int tn = 0; tn < 2; ++tn) sb[tn] = Sb[b_row + 32 * tn];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+            // lane half g of sub-step `sub` covers block 2 sub + g
+            const int blk = 2 * sub + g;
+            v8i_t af[4], bf[2];
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) af[tm] = mx_frag(As + (a_row + 32 * tm) * kMxRow + 16 * blk);
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) bf[tn] = mx_frag(Bs + (b_row + 32 * tn) * kMxRow + 16 * blk);
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+                    acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                        af[tm], bf[tn], acc[tm][tn], 4, 4, 0, (int)((sa[tm] >> (8 * blk)) & 0xFFu), 0,
+                        (int)((sb[tn] >> (8 * blk)) & 0xFFu));
+        }
+    };
+
+    // Step t's rows live in register stage t % 3 and its tile in LDS stage
+    // t % 2; loads are clamped to the last full step, as in k_gemm_nv.
+    const int64_t nsteps = (K + kMxKS - 1) / kMxKS;
+    const int64_t nfull = K / kMxKS;
+    int64_t s = 0;
+    MxRow g0, g1, g2;
+    if (nfull > 0) {
+        load_full(0, g0);
+        load_full((nfull > 1 ? 1 : 0) * kMxKS, g1);
+        load_full((nfull > 2 ? 2 : nfull - 1) * kMxKS, g2);
+        put(g0, 0);
+    }
+    __syncthreads();
+    auto step = [&](auto c3, int64_t t) {
+        constexpr int r = decltype(c3)::value;
+        const int st = (int)(t & 1);
+        MxRow& done = r == 0 ? g0 : (r == 1 ? g1 : g2);  // step t, already in LDS
+        MxRow& next = r == 0 ? g1 : (r == 1 ? g2 : g0);  // step t + 1
+        load_full((t + 3 < nfull ? t + 3 : nfull - 1) * kMxKS, done);
+        compute(st);
+        put(next, st ^ 1);  // past the last full step: harmless, never read
+        __syncthreads();
+    };
+    using I0 = std::integral_constant<int, 0>;
+    using I1 = std::integral_constant<int, 1>;
+    using I2 = std::integral_constant<int, 2>;
+    for (; s + 3 <= nfull; s += 3) {
+        step(I0{}, s);
+        step(I1{}, s + 1);
+        step(I2{}, s + 2);
+    }
+    if (s < nfull) step(I0{}, s++);
+    if (s < nfull) step(I1{}, s++);
+    if (nfull < nsteps) {  // partial last step, into LDS stage nfull % 2
+        load_tail(nfull * kMxKS, g0);
+        put(g0, (int)(nfull & 1));
+        __syncthreads();
+        compute((int)(nfull & 1));
+    }
+
+    __syncthreads();  // every wave is done reading the operand stages
+    store_tile<kOutF32>(acc, 1.0f, lds, tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c,
+                        ldc);
+}
+
+namespace {
+
+// ---------------------------------------------------------------------------
 // bf16 operands
 //
 // Thread rid (0..255 of its operand) moves 8 pieces of 16 bytes (8 values)
@@ -619,6 +805,19 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
         hipLaunchKernelGGL(k_gemm_nv<true>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
     else
         hipLaunchKernelGGL(k_gemm_nv<false>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
+}
+
+void launch_gemm_mx(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N, int64_t K,
+                    void* c, int64_t ldc, bool out_fp32, hipStream_t s)
+{
+    if (M == 0 || N == 0) return;
+    if (K == 0) return launch_fill_zero(M, N, c, ldc, out_fp32, s);
+    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, 0, nullptr, 0};
+    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, 0, nullptr, 0};
+    if (out_fp32)
+        hipLaunchKernelGGL(k_gemm_mx<true>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
+    else
+        hipLaunchKernelGGL(k_gemm_mx<false>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
 }
 
 template <class Src>

@@ -52,6 +52,11 @@ void launch_dual_quant(const uint16_t* x, int64_t tokens, int64_t channels, int6
                        const float* amax_src, const float* amax_rht_src, const QOut& o,
                        const QOut& o_rht, hipStream_t s);
 
+// MXFP4: mode 0 blocks of 32 along the rows of x; 1 the transposed matrix;
+// 2 the transposed matrix after the 16-point RHT (o: codes and scales only).
+void launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int mode,
+                     uint32_t mask, int rounding, uint64_t seed, const QOut& o, hipStream_t s);
+
 // C[m, n] = (1/s_enc_a) (1/s_enc_b) sum_k a^[m, k] b^[n, k]; out_fp32 selects
 // fp32 or bf16 (round to nearest even) output.
 void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
@@ -61,6 +66,11 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
 // block scales applied to the fp32 partials (K > 0).
 void launch_gemm_fp8blk(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
                         int64_t K, void* c, int64_t ldc, bool out_fp32, hipStream_t s);
+
+// C[m, n] = sum_k a^[m, k] b^[n, k] over MXFP4 operands (scales in the
+// GemmOperand's scales; s_enc and scale_row_shift unused).
+void launch_gemm_mx(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N, int64_t K,
+                    void* c, int64_t ldc, bool out_fp32, hipStream_t s);
 
 // C[m, n] = sum_k A[m, k] B[n, k] over bf16 operands; a_t / b_t: the operand
 // is stored K x rows (element (r, k) at k * ld + r) instead of rows x K.

@@ -583,6 +583,111 @@ __global__ __launch_bounds__(256) void k_dual_quant(
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 quantisers (the comparison format: 32-element blocks, one UE8M0
+// scale each, no tensor scale).  Shared exponent e = floor(log2(amax_b)) - 2
+// clamped to [-127, 127]; from the fp32 (or bf16) exponent field E of amax_b
+// that is max(E - 129, -127) (E = 0 for zero and subnormal maxima), so the
+// scale byte is max(E - 2, 0) and the element factor 2^-e has the fp32
+// exponent field min(256 - E, 254).
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ uint32_t mx_scale_byte(uint32_t E) { return E > 2u ? E - 2u : 0u; }
+
+__device__ __forceinline__ float mx_factor(uint32_t E)
+{
+    return __uint_as_float(min(256u - E, 254u) << 23);
+}
+
+// Blocks of 32 along the rows of x (rows x cols, cols a multiple of 32): one
+// thread per block (four 16-byte loads, a 16-byte code store, a scale byte).
+template <bool kSR>
+__global__ __launch_bounds__(256) void k_mx_quant_rows(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld, uint64_t seed,
+    uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales,
+    int64_t ld_scales)
+{
+    const int64_t nb = cols >> 5;
+    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (t >= rows * nb) return;
+    const int64_t r = t / nb;
+    const int64_t b = t - r * nb;
+    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 32);
+    const uint4 q[4] = {src[0], src[1], src[2], src[3]};
+    const uint32_t mb = max(max(absmax8(q[0]), absmax8(q[1])), max(absmax8(q[2]), absmax8(q[3])));
+    const uint32_t E = (mb >> 7) & 0xFFu;  // bf16 exponent field of the block amax
+    const float f = mx_factor(E);
+    uint32_t pk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const uint32_t w[4] = {q[j].x, q[j].y, q[j].z, q[j].w};
+        float v[8];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            v[2 * k] = bf16_lo(w[k]);
+            v[2 * k + 1] = bf16_hi(w[k]);
+        }
+        if constexpr (kSR)
+            pk[j] = encode8_sr(v, f, seed, (uint64_t)(r * cols + b * 32 + 8 * j) >> 3);
+        else
+            pk[j] = encode8_rne(v, f);
+    }
+    *reinterpret_cast<uint4*>(codes + r * ld_codes + b * 16) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+    scales[r * ld_scales + b] = (uint8_t)mx_scale_byte(E);
+}
+
+// The transposed matrix (channels x tokens), blocks of 32 along the tokens,
+// optionally after the 16-point RHT of every 16-token chunk.  Tile and
+// thread map are k_rht_quant's; a block's two 16-token chunks are held by
+// lanes t and t ^ 16 of one wave, so its amax is one lane shuffle.
+template <bool kSR, bool kRHT>
+__global__ __launch_bounds__(256) void k_mx_quant_cols(
+    const uint16_t* __restrict__ x, int64_t tokens, int64_t channels, int64_t ld, uint32_t mask,
+    uint64_t seed, uint8_t* __restrict__ codes, int64_t ld_codes, uint8_t* __restrict__ scales,
+    int64_t ld_scales)
+{
+    __shared__ uint2 scodes[kRhtCh][17];   // [channel][16-token chunk], padded
+    __shared__ uint8_t sscale[kRhtCh][8];  // [channel][32-token block]
+
+    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int64_t chb = (int64_t)blockIdx.x * kRhtCh, tokb = (int64_t)blockIdx.y * kRhtTok;
+    const int64_t ch0 = chb + cg * 8;
+    const int64_t tok0 = tokb + j * 16;
+    // tokens is a multiple of 32: both chunks of a block are valid or neither
+    if (ch0 < channels && tok0 < tokens) {
+        uint4 raw[16];
+        load_rht_raw(x, ld, tok0, ch0, raw);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float v[16];
+            unpack_channel(raw, c, v);
+            if constexpr (kRHT) rht16(v, mask);
+            uint32_t mb = __float_as_uint(absmax16(v));
+            mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16, 64));
+            const uint32_t E = mb >> 23;
+            const float f = mx_factor(E);
+            uint2 pk;
+            if constexpr (kSR)
+                pk = encode16_sr(v, f, seed, (uint64_t)((ch0 + c) * tokens + tok0) >> 3);
+            else
+                pk = encode16_rne(v, f);
+            scodes[cg * 8 + c][j] = pk;
+            if ((j & 1) == 0) sscale[cg * 8 + c][j >> 1] = (uint8_t)mx_scale_byte(E);
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int idx = it * 256 + threadIdx.x;
+        const int row = idx >> 4, q = idx & 15;
+        const int64_t ch = chb + row, tk = tokb + q * 16;
+        if (ch < channels && tk < tokens) {
+            *reinterpret_cast<uint2*>(codes + ch * ld_codes + (tk >> 1)) = scodes[row][q];
+            if ((q & 1) == 0) scales[ch * ld_scales + (tk >> 5)] = sscale[row][q >> 1];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
 
@@ -697,6 +802,32 @@ void launch_dual_quant(const uint16_t* x, int64_t tokens, int64_t channels, int6
     else
         hipLaunchKernelGGL(k_dual_quant<false>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
                            amax_src, amax_rht_src, seed, seed_rht, o, o_rht);
+}
+
+void launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int mode,
+                     uint32_t mask, int rounding, uint64_t seed, const QOut& o, hipStream_t s)
+{
+    if (rows == 0 || cols == 0) return;
+    const bool sr = rounding == 1;
+    if (mode == 0) {
+        dim3 g(grid_for(rows * (cols >> 5), 256, INT32_MAX));
+        if (sr)
+            hipLaunchKernelGGL(k_mx_quant_rows<true>, g, dim3(256), 0, s, x, rows, cols, ld, seed,
+                               o.codes, o.ld_codes, o.scales, o.ld_scales);
+        else
+            hipLaunchKernelGGL(k_mx_quant_rows<false>, g, dim3(256), 0, s, x, rows, cols, ld, seed,
+                               o.codes, o.ld_codes, o.scales, o.ld_scales);
+        return;
+    }
+    dim3 g((unsigned)((cols + kRhtCh - 1) / kRhtCh), (unsigned)((rows + kRhtTok - 1) / kRhtTok));
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, g, dim3(256), 0, s, x, rows, cols, ld, mask, seed, o.codes,
+                           o.ld_codes, o.scales, o.ld_scales);
+    };
+    if (mode == 1)
+        sr ? go(k_mx_quant_cols<true, false>) : go(k_mx_quant_cols<false, false>);
+    else
+        sr ? go(k_mx_quant_cols<true, true>) : go(k_mx_quant_cols<false, true>);
 }
 
 }  // namespace nvfp4

@@ -133,6 +133,45 @@ def test_dual_validation(lib, case, status):
                                    ctypes.byref(dr), None) == -4
 
 
+@pytest.mark.parametrize("args,status", [
+    # x, rows, cols, ld_x, mode, rounding
+    ((FAKE, 32, 48, 48, 0, 0), -2),         # rows mode: cols not whole blocks of 32
+    ((FAKE, 48, 32, 32, 1, 0), -2),         # transposed: rows not whole blocks of 32
+    ((FAKE, 32, 12, 16, 2, 0), -2),         # transposed: cols not a multiple of 8
+    ((FAKE, 32, 32, 32, 3, 0), -4),         # unknown mode
+    ((FAKE, 32, 32, 32, 0, 2), -4),         # unknown rounding
+    ((None, 32, 32, 32, 0, 0), -1),         # null input
+    ((FAKE + 8, 32, 32, 32, 0, 0), -3),     # misaligned input
+    ((FAKE, 32, 32, 16, 0, 0), -2),         # ld_x < cols
+])
+def test_mx_quantize_validation(lib, args, status):
+    x, rows, cols, ld, mode, rnd = args
+    d = _desc(codes=FAKE, scales=FAKE, ld_codes=16, ld_scales=4)
+    assert lib.nvfp4_mx_quantize(x, rows, cols, ld, mode, 0, rnd, 0, ctypes.byref(d), None) == status
+
+
+def test_mx_out_and_gemm_validation(lib):
+    def mx(rows, cols, **kw):
+        d = _desc(codes=FAKE, scales=FAKE, ld_codes=32, ld_scales=4, rows=rows, cols=cols, block=2)
+        for k, v in kw.items():
+            setattr(d, k, v)
+        return d
+    q = lambda d: lib.nvfp4_mx_quantize(FAKE, 32, 64, 64, 0, 0, 0, 0, ctypes.byref(d), None)
+    assert q(mx(0, 0, codes_t=FAKE)) == -4       # no transposed copies
+    assert q(mx(0, 0, ld_codes=16)) == -2        # rows of 64 codes need 32 bytes
+    assert q(mx(0, 0, ld_scales=2)) == -3
+    assert q(mx(0, 0, scales=None)) == -1
+    g = lambda a, b, c=FAKE, ldc=64, dt=1: lib.nvfp4_mx_gemm(ctypes.byref(a), ctypes.byref(b), c,
+                                                             ldc, dt, None)
+    assert g(mx(16, 64), mx(8, 64), dt=5) == -4
+    assert g(mx(16, 64), mx(8, 64, block=0)) == -5   # an NVFP4 operand
+    assert g(mx(16, 64), mx(8, 32)) == -5            # K mismatch
+    assert g(mx(16, 48), mx(8, 48)) == -2            # K not whole blocks
+    assert g(mx(16, 64), mx(8, 64), c=None) == -1
+    assert g(mx(16, 64), mx(8, 64), ldc=4) == -2     # ldc < N
+    assert g(mx(16, 64), mx(8, 64), c=FAKE + 8) == -3
+
+
 @pytest.mark.parametrize("fn", ["nvfp4_gemm", "nvfp4_gemm_fp8blk"])
 def test_gemm_validation(lib, fn):
     gemm = getattr(lib, fn)
