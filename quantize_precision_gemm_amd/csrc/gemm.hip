@@ -95,17 +95,17 @@ __device__ __forceinline__ void tile_of(int64_t M, int64_t N, int64_t& tile_m, i
     tile_n = in_group / gsz;
 }
 
-// Epilogue: each wave stages 32 output rows at a time through its part of
-// `lds` (fp32, alpha applied; every wave must be done with the operand
-// stages) and writes them back as 16-byte row segments.
+// Epilogue: each wave stages 32 output rows at a time through its own LDS
+// area `stage_out` (32 x kEpiStride floats; fp32, alpha applied; every wave
+// must be done with the operand stages) and writes them back as 16-byte row
+// segments.
 template <bool kOutF32>
 __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float alpha,
-                                           uint8_t* lds, int64_t m0, int64_t n0, int64_t M,
+                                           float* stage_out, int64_t m0, int64_t n0, int64_t M,
                                            int64_t N, void* __restrict__ c, int64_t ldc)
 {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     const int g = lane >> 5, lr = lane & 31;
-    float* stage_out = reinterpret_cast<float*>(lds) + wave * 32 * kEpiStride;
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
 #pragma unroll
@@ -353,7 +353,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
 
     const float alpha = (1.0f / *A.s_enc) * (1.0f / *B.s_enc);
     __syncthreads();  // every wave is done reading the operand stages
-    store_tile<kOutF32>(acc, alpha, lds, tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c,
+    store_tile<kOutF32>(acc, alpha, reinterpret_cast<float*>(lds) + wave * 32 * kEpiStride,
+                        tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c,
                         ldc);
 }
 
@@ -368,32 +369,38 @@ namespace {
 // supplies row (A) or column (B) l % 32 and the 32 consecutive k of half
 // l / 32 of its 64-wide step -- exactly one MX block, 16 code bytes -- so the
 // operands enter the matrix cores as stored, with no decode.  Same tile,
-// wave grid, three register stages, LDS double buffer and epilogue as
-// k_gemm_nv; a K step is 128 (4 blocks, 64 code bytes per row) in two MFMA
-// sub-steps of 64.  LDS stage: A and B codes as 256 rows of 80 bytes (64 +
-// pad: 16-byte reads of 16 consecutive rows hit distinct banks), then each
-// row's 4 scale bytes for A and for B.  Thread t loads half h = t % 2 of
-// tile row t / 2 of both operands: 32 code bytes (blocks 2h, 2h+1) and 2
-// scale bytes each.
+// wave grid and epilogue as k_gemm_nv; a K step is 128 (4 blocks, 64 code
+// bytes per row) in two MFMA sub-steps of 64, and a wave reads all its
+// fragments of a step before its first MFMA.
+//
+// No VGPR staging: the operands move from global memory straight into LDS
+// (global_load_lds_dwordx4, 16 bytes per lane, 1 KB per wave instruction
+// landing contiguously), three stages deep, two steps ahead.  Rows are 64
+// packed bytes; chunk c of row r sits at position c ^ swz(r) so that the
+// fragment reads (16 bytes of 16 consecutive rows) hit distinct banks.  Each
+// stage is its own array so that the compiler can tell that the loads in
+// flight never write the stage being read, and the steady-state barrier
+// carries no release fence, whose wait for every outstanding load would
+// empty the pipeline; the waits on the loads are the explicit vmcnt.
 // ---------------------------------------------------------------------------
 
 constexpr int kMxKS = 128;
-constexpr int kMxRow = 80;
-constexpr int kMxOp = 256 * kMxRow;
-constexpr int kMxStage = 2 * kMxOp + 2 * 256 * 4;
+constexpr int kMxA = 0, kMxB = 16384, kMxS = 32768;  // codes of A, B; scales (A, then B)
+constexpr int kMxStage = kMxS + 2048;
+static_assert(4 * 32 * kEpiStride * 4 <= kMxStage, "four waves' epilogue rows fit one stage");
 
 typedef int v8i_t __attribute__((ext_vector_type(8)));
-
-struct MxRow {             // one thread's share of a K step
-    uint4 a0, a1, b0, b1;  // 32 code bytes of its A and B half rows
-    uint32_t s;            // A scales in bytes 0-1, B scales in bytes 2-3
-};
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
 
 __device__ __forceinline__ v8i_t mx_frag(const uint8_t* p)
 {
-    const uint4 q = *reinterpret_cast<const uint4*>(p);
+    const u32x4_t q = *reinterpret_cast<const u32x4_t*>(p);
     return v8i_t{(int)q.x, (int)q.y, (int)q.z, (int)q.w, 0, 0, 0, 0};
 }
+
+__device__ __forceinline__ int mx_swz(int r) { return ((r >> 1) ^ (r >> 3)) & 3; }
 
 }  // namespace
 
@@ -401,66 +408,54 @@ template <bool kOutF32>
 __global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t M, int64_t N,
                                                     int64_t K, void* __restrict__ c, int64_t ldc)
 {
-    __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kMxStage];
+    __shared__ __attribute__((aligned(16))) uint8_t lds0[kMxStage];
+    __shared__ __attribute__((aligned(16))) uint8_t lds1[kMxStage];
+    __shared__ __attribute__((aligned(16))) uint8_t lds2[kMxStage];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = lane >> 5, lr = lane & 31;
     int64_t tile_m, tile_n;
     tile_of(M, N, tile_m, tile_n);
-
-    // half h of tile row `row` (rows past the operand re-read its last row;
-    // they are never stored)
-    const int row = tid >> 1, h = tid & 1;
-    int64_t ra = tile_m * kBM + row, rb = tile_n * kBN + row;
-    ra = ra < M ? ra : M - 1;
-    rb = rb < N ? rb : N - 1;
-    const uint8_t* pa = static_cast<const uint8_t*>(A.data) + ra * A.ld + 32 * h;
-    const uint8_t* pb = static_cast<const uint8_t*>(B.data) + rb * B.ld + 32 * h;
-    const uint8_t* psa = A.scales + ra * A.ld_scales + 2 * h;
-    const uint8_t* psb = B.scales + rb * B.ld_scales + 2 * h;
     const int64_t nblk = K >> 5;
 
-    auto load_full = [&](int64_t k0, MxRow& w) {
-        const uint4* qa = reinterpret_cast<const uint4*>(pa + (k0 >> 1));
-        const uint4* qb = reinterpret_cast<const uint4*>(pb + (k0 >> 1));
-        w.a0 = qa[0];
-        w.a1 = qa[1];
-        w.b0 = qb[0];
-        w.b1 = qb[1];
-        const uint32_t sa = *reinterpret_cast<const uint16_t*>(psa + (k0 >> 5));
-        const uint32_t sb = *reinterpret_cast<const uint16_t*>(psb + (k0 >> 5));
-        w.s = sa | (sb << 16);
-    };
-    // partial last step: blocks past K get zero codes (whatever their scale,
-    // they add zero); each 16-byte piece is one whole block
-    auto load_tail = [&](int64_t k0, MxRow& w) {
-        const int64_t b0 = (k0 >> 5) + 2 * h;
-        const uint4 z = make_uint4(0, 0, 0, 0);
-        const uint4* qa = reinterpret_cast<const uint4*>(pa + (k0 >> 1));
-        const uint4* qb = reinterpret_cast<const uint4*>(pb + (k0 >> 1));
-        w.a0 = b0 < nblk ? qa[0] : z;
-        w.b0 = b0 < nblk ? qb[0] : z;
-        w.a1 = b0 + 1 < nblk ? qa[1] : z;
-        w.b1 = b0 + 1 < nblk ? qb[1] : z;
-        uint32_t s = 0u;
-        for (int j = 0; j < 2; ++j)
-            if (b0 + j < nblk)
-                s |= ((uint32_t)psa[(k0 >> 5) + j] << (8 * j)) |
-                     ((uint32_t)psb[(k0 >> 5) + j] << (16 + 8 * j));
-        w.s = s;
-    };
-    auto put = [&](const MxRow& w, int st) {
-        uint8_t* base = lds + st * kMxStage;
-        uint4* da = reinterpret_cast<uint4*>(base + row * kMxRow + 32 * h);
-        uint4* db = reinterpret_cast<uint4*>(base + kMxOp + row * kMxRow + 32 * h);
-        da[0] = w.a0;
-        da[1] = w.a1;
-        db[0] = w.b0;
-        db[1] = w.b1;
-        uint16_t* sc = reinterpret_cast<uint16_t*>(base + 2 * kMxOp);
-        sc[row * 2 + h] = (uint16_t)w.s;
-        sc[512 + row * 2 + h] = (uint16_t)(w.s >> 16);
+    // Load plan: wave w moves code pieces q = 4w .. 4w+3 (piece q: operand
+    // q / 16, tile rows 16 (q % 16) + lane / 4; lane % 4 is the chunk
+    // position in LDS, holding chunk (lane % 4) ^ swz(row) of the row) and
+    // one scale piece (rows 64 (w % 4) + lane, 4 bytes).  Waves 0-3 move A,
+    // waves 4-7 move B, so every base pointer is wave-uniform; rows past the
+    // operand re-read its last row (never stored).
+    const bool wb = wave >= 4;
+    const uint8_t* gbase = static_cast<const uint8_t*>(wb ? B.data : A.data);
+    const int64_t gld = wb ? B.ld : A.ld;
+    const int64_t grow0 = wb ? tile_n * kBN : tile_m * kBM;
+    const int64_t glim = wb ? N : M;
+    uint32_t goff[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int r = 16 * ((4 * wave + i) & 15) + (lane >> 2);
+        int64_t gr = grow0 + r;
+        gr = gr < glim ? gr : glim - 1;
+        goff[i] = (uint32_t)(gr * gld) + 16u * (uint32_t)((lane & 3) ^ mx_swz(r));
+    }
+    const int cdst = (wb ? kMxB : kMxA) + 1024 * ((4 * wave) & 15);
+    const uint8_t* sbase = wb ? B.scales : A.scales;
+    uint32_t soff;
+    {
+        int64_t gr = grow0 + 64 * (wave & 3) + lane;
+        gr = gr < glim ? gr : glim - 1;
+        soff = (uint32_t)(gr * (wb ? B.ld_scales : A.ld_scales));
+    }
+    const int sdst = kMxS + (wb ? 1024 : 0) + 256 * (wave & 3);
+
+    auto issue = [&](int64_t k0, uint8_t* st) {
+        const uint8_t* gb = gbase + (k0 >> 1);
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((glb_void_t*)(gb + goff[i]),
+                                             (lds_void_t*)(st + cdst + 1024 * i), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(sbase + (k0 >> 5) + soff),
+                                         (lds_void_t*)(st + sdst), 4, 0, 0);
     };
 
     float16_t acc[4][2];
@@ -468,79 +463,124 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t 
     const int wm = wave >> 2, wn = wave & 3;
     const int a_row = wm * 128 + lr;  // + 32 tm
     const int b_row = wn * 64 + lr;   // + 32 tn
+    const int sw = mx_swz(lr);        // = swz of every fragment row of this lane
+    int aoff[2], boff[2];             // lane half g of sub-step s reads block 2s + g
+#pragma unroll
+    for (int sub = 0; sub < 2; ++sub) {
+        aoff[sub] = kMxA + a_row * 64 + 16 * ((2 * sub + g) ^ sw);
+        boff[sub] = kMxB + b_row * 64 + 16 * ((2 * sub + g) ^ sw);
+    }
 
-    auto compute = [&](int st) {
-        const uint8_t* As = lds + st * kMxStage;
-        const uint8_t* Bs = As + kMxOp;
-        const uint32_t* Sa = reinterpret_cast<const uint32_t*>(As + 2 * kMxOp);
+    auto compute = [&](const uint8_t* st) {
+        const uint32_t* Sa = reinterpret_cast<const uint32_t*>(st + kMxS);
         const uint32_t* Sb = Sa + 256;
-        uint32_t sa[4], sb[2];  // this lane's 4 block scales of the step, per fragment row
+        v8i_t af[2][4], bf[2][2];
+        uint32_t sa[4], sb[2];
+#pragma unroll
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+            for (int tm = 0; tm < 4; ++tm) af[sub][tm] = mx_frag(st + aoff[sub] + tm * 2048);
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn) bf[sub][tn] = mx_frag(st + boff[sub] + tn * 2048);
+        }
 #pragma unroll
         for (int tm = 0; tm < 4; ++tm) sa[tm] = Sa[a_row + 32 * tm];
 #pragma unroll
         for (int tn = 0; tn < 2; ++tn) sb[tn] = Sb[b_row + 32 * tn];
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
-            // lane half g of sub-step `sub` covers block 2 sub + g
             const int blk = 2 * sub + g;
-            v8i_t af[4], bf[2];
-#pragma unroll
-            for (int tm = 0; tm < 4; ++tm) af[tm] = mx_frag(As + (a_row + 32 * tm) * kMxRow + 16 * blk);
-#pragma unroll
-            for (int tn = 0; tn < 2; ++tn) bf[tn] = mx_frag(Bs + (b_row + 32 * tn) * kMxRow + 16 * blk);
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
 #pragma unroll
                 for (int tn = 0; tn < 2; ++tn)
                     acc[tm][tn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                        af[tm], bf[tn], acc[tm][tn], 4, 4, 0, (int)((sa[tm] >> (8 * blk)) & 0xFFu), 0,
-                        (int)((sb[tn] >> (8 * blk)) & 0xFFu));
+                        af[sub][tm], bf[sub][tn], acc[tm][tn], 4, 4, 0,
+                        (int)((sa[tm] >> (8 * blk)) & 0xFFu), 0, (int)((sb[tn] >> (8 * blk)) & 0xFFu));
         }
     };
 
-    // Step t's rows live in register stage t % 3 and its tile in LDS stage
-    // t % 2; loads are clamped to the last full step, as in k_gemm_nv.
-    const int64_t nsteps = (K + kMxKS - 1) / kMxKS;
-    const int64_t nfull = K / kMxKS;
-    int64_t s = 0;
-    MxRow g0, g1, g2;
-    if (nfull > 0) {
-        load_full(0, g0);
-        load_full((nfull > 1 ? 1 : 0) * kMxKS, g1);
-        load_full((nfull > 2 ? 2 : nfull - 1) * kMxKS, g2);
-        put(g0, 0);
-    }
-    __syncthreads();
-    auto step = [&](auto c3, int64_t t) {
-        constexpr int r = decltype(c3)::value;
-        const int st = (int)(t & 1);
-        MxRow& done = r == 0 ? g0 : (r == 1 ? g1 : g2);  // step t, already in LDS
-        MxRow& next = r == 0 ? g1 : (r == 1 ? g2 : g0);  // step t + 1
-        load_full((t + 3 < nfull ? t + 3 : nfull - 1) * kMxKS, done);
-        compute(st);
-        put(next, st ^ 1);  // past the last full step: harmless, never read
-        __syncthreads();
+    // Partial last step, through registers: blocks past K get zero codes
+    // (they add zero whatever their scale).  Thread t writes half t % 2 of
+    // tile row t / 2 of both operands.
+    auto tail = [&](int64_t k0, uint8_t* st) {
+        const int row = tid >> 1, h = tid & 1;
+        const int rs = mx_swz(row);
+#pragma unroll
+        for (int op = 0; op < 2; ++op) {
+            int64_t gr = (op ? tile_n * kBN : tile_m * kBM) + row;
+            const int64_t lim = op ? N : M;
+            gr = gr < lim ? gr : lim - 1;
+            const uint8_t* p = static_cast<const uint8_t*>(op ? B.data : A.data) +
+                               gr * (op ? B.ld : A.ld) + (k0 >> 1);
+            const uint8_t* ps = (op ? B.scales : A.scales) + gr * (op ? B.ld_scales : A.ld_scales);
+            uint32_t sc = 0u;
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                const int blk = 2 * h + j;  // block of the step = logical chunk of the row
+                u32x4_t q = {0u, 0u, 0u, 0u};
+                if ((k0 >> 5) + blk < nblk) {
+                    q = *reinterpret_cast<const u32x4_t*>(p + 16 * blk);
+                    sc |= (uint32_t)ps[(k0 >> 5) + blk] << (8 * j);
+                }
+                *reinterpret_cast<u32x4_t*>(st + (op ? kMxB : kMxA) + row * 64 + 16 * (blk ^ rs)) = q;
+            }
+            reinterpret_cast<uint16_t*>(st + kMxS + (op ? 1024 : 0))[row * 2 + h] = (uint16_t)sc;
+        }
     };
-    using I0 = std::integral_constant<int, 0>;
-    using I1 = std::integral_constant<int, 1>;
-    using I2 = std::integral_constant<int, 2>;
-    for (; s + 3 <= nfull; s += 3) {
-        step(I0{}, s);
-        step(I1{}, s + 1);
-        step(I2{}, s + 2);
+
+    // Step t uses stage t % 3: wait until this wave's loads of step t have
+    // landed (those of step t + 1, 5 per wave, may be in flight), barrier
+    // (every wave's loads landed, every wave done with step t - 1), start
+    // the loads of step t + 2 into the stage of step t - 1, compute step t.
+    const int64_t nfull = K / kMxKS;
+    if (nfull > 0) issue(0, lds0);
+    if (nfull > 1) issue(kMxKS, lds1);
+    auto sync = [&]() {
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    };
+    int64_t t = 0;
+    for (; t + 4 < nfull; t += 3) {
+        __builtin_amdgcn_s_waitcnt(0x0f75);  // vmcnt(5)
+        sync();
+        issue((t + 2) * kMxKS, lds2);
+        compute(lds0);
+        __builtin_amdgcn_s_waitcnt(0x0f75);
+        sync();
+        issue((t + 3) * kMxKS, lds0);
+        compute(lds1);
+        __builtin_amdgcn_s_waitcnt(0x0f75);
+        sync();
+        issue((t + 4) * kMxKS, lds1);
+        compute(lds2);
     }
-    if (s < nfull) step(I0{}, s++);
-    if (s < nfull) step(I1{}, s++);
-    if (nfull < nsteps) {  // partial last step, into LDS stage nfull % 2
-        load_tail(nfull * kMxKS, g0);
-        put(g0, (int)(nfull & 1));
+    for (; t < nfull; ++t) {  // the last (up to 4) full steps
+        const int st = (int)(t % 3);
+        uint8_t* cur = st == 0 ? lds0 : (st == 1 ? lds1 : lds2);
+        uint8_t* ahead = st == 0 ? lds2 : (st == 1 ? lds0 : lds1);
+        if (t + 1 < nfull)
+            __builtin_amdgcn_s_waitcnt(0x0f75);
+        else
+            __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0)
         __syncthreads();
-        compute((int)(nfull & 1));
+        if (t + 2 < nfull) issue((t + 2) * kMxKS, ahead);
+        compute(cur);
+    }
+    if (nfull * kMxKS < K) {
+        const int st = (int)(nfull % 3);
+        uint8_t* cur = st == 0 ? lds0 : (st == 1 ? lds1 : lds2);
+        __syncthreads();  // (no loads in flight here) the stage is free
+        tail(nfull * kMxKS, cur);
+        __syncthreads();
+        compute(cur);
     }
 
     __syncthreads();  // every wave is done reading the operand stages
-    store_tile<kOutF32>(acc, 1.0f, lds, tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c,
-                        ldc);
+    // waves 0-3 stage their output rows in lds0, waves 4-7 in lds1
+    float* stage_out = reinterpret_cast<float*>(wave < 4 ? lds0 : lds1) + (wave & 3) * 32 * kEpiStride;
+    store_tile<kOutF32>(acc, 1.0f, stage_out, tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N,
+                        c, ldc);
 }
 
 namespace {
@@ -761,7 +801,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(OpArgs A, OpArgs B, int64_
     }
 
     __syncthreads();  // every wave is done reading the operand stages
-    store_tile<kOutF32>(acc, 1.0f, &lds[0][0][0], tile_m * kBM + wm * 128, tile_n * kBN + wn * 64,
+    store_tile<kOutF32>(acc, 1.0f, reinterpret_cast<float*>(&lds[0][0][0]) + wave * 32 * kEpiStride,
+                        tile_m * kBM + wm * 128, tile_n * kBN + wn * 64,
                         M, N, c, ldc);
 }
 
