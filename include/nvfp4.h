@@ -333,7 +333,8 @@ int nvfp4_mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, i
  * Defines: the comparison of Technische Zusammenfassung 2.A, measured as the
  * speed of the 2.B.2 GEMMs in the other format.
  *   a, b      MXFP4 descriptors (block NVFP4_BLOCK_MX32) with equal cols = K,
- *             a multiple of 32.
+ *             a multiple of 32; each operand's codes (rows x ld_codes) and
+ *             scales (rows x ld_scales) span less than 4 GiB.
  *   c, ldc, c_dtype  as for nvfp4_gemm (no alpha: MXFP4 has no tensor scale).
  * Returns NVFP4_OK or a negative status; nothing is enqueued on failure.
  */

@@ -347,6 +347,11 @@ int nvfp4_mx_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t
     st = check_mx(b, b->rows, b->cols);
     if (st != NVFP4_OK) return st;
     const int64_t M = a->rows, N = b->rows, K = a->cols;
+    // the kernel addresses each operand with 32-bit offsets from its base
+    const int64_t lim = (int64_t)1 << 32;
+    if (M * a->ld_codes >= lim || N * b->ld_codes >= lim || M * a->ld_scales >= lim ||
+        N * b->ld_scales >= lim)
+        return NVFP4_ERR_SHAPE;
     if (!c && M > 0 && N > 0) return NVFP4_ERR_NULL;
     if (!aligned(c, c_dtype == NVFP4_OUT_FP32 ? 16 : 8) || ldc % 4 != 0) return NVFP4_ERR_ALIGN;
     if (ldc < N) return NVFP4_ERR_SHAPE;

@@ -170,6 +170,7 @@ def test_mx_out_and_gemm_validation(lib):
     assert g(mx(16, 64), mx(8, 64), c=None) == -1
     assert g(mx(16, 64), mx(8, 64), ldc=4) == -2     # ldc < N
     assert g(mx(16, 64), mx(8, 64), c=FAKE + 8) == -3
+    assert g(mx(1 << 27, 64), mx(8, 64)) == -2      # codes span 4 GiB: beyond 32-bit offsets
 
 
 @pytest.mark.parametrize("fn", ["nvfp4_gemm", "nvfp4_gemm_fp8blk"])
