@@ -85,6 +85,12 @@ def lib():
         L.orc_gemm_fp32.argtypes = [P, P, ctypes.c_int, ctypes.c_float, P, P, ctypes.c_int,
                                     ctypes.c_float, i64, i64, i64, P]
         L.orc_gemm_fp32.restype = ctypes.c_int
+        L.orc_rht_signs64.argtypes = [u64]
+        L.orc_rht_signs64.restype = u64
+        L.orc_rht_sized.argtypes = [P, ctypes.c_int, u64, P]
+        L.orc_rht_sized.restype = None
+        L.orc_rht_quantize_sized.argtypes = [P, i64, i64, ctypes.c_int, u64, ctypes.c_int, u64, P, P, P, P, P]
+        L.orc_rht_quantize_sized.restype = ctypes.c_int
         L.orc_mx_quantize.argtypes = [P, i64, i64, ctypes.c_int, u32, ctypes.c_int, u64, P, P]
         L.orc_mx_quantize.restype = ctypes.c_int
         L.orc_mx_exponent.argtypes = [ctypes.c_float]
@@ -258,6 +264,38 @@ def mx_quantize(x_u16, mode=MX_ROWS, sign_mask=0, rounding=RNE, seed=0):
     if rc != 0:
         raise ValueError(f"orc_mx_quantize: status {rc}")
     return QTensor(codes, scales, None, None, orows, ocols, BLOCK_MX32)
+
+
+def rht_signs64(seed):
+    """64 random signs (bit i: d_i = -1); the low 16 are rht_sign_mask(seed)."""
+    return int(lib().orc_rht_signs64(seed))
+
+
+def rht_sized(v, size, signs):
+    """The size-point transform (size 4, 16 or 64) of one fp32 vector."""
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    assert v.shape == (size,)
+    out = np.empty(size, np.float32)
+    lib().orc_rht_sized(_ptr(v), size, signs, _ptr(out))
+    return out
+
+
+def rht_quantize_sized(x_u16, size, signs, rounding=RNE, seed=0, amax_in=None):
+    """Wgrad operand with a size-point RHT along tokens (size 4, 16 or 64;
+    the ablation of Technische Zusammenfassung 2.B.2's 16 x 16 choice), then
+    transpose and 1x16 quantisation as in rht_quantize."""
+    x = _u16(x_u16)
+    tokens, channels = x.shape
+    codes = np.zeros((channels, tokens // 2), np.uint8)
+    scales = np.zeros((channels, tokens // 16), np.uint8)
+    amax = np.zeros(1, np.float32)
+    s_enc = np.zeros(1, np.float32)
+    ain = None if amax_in is None else np.array([amax_in], np.float32)
+    rc = lib().orc_rht_quantize_sized(_ptr(x), tokens, channels, size, signs, rounding, seed, _ptr(ain),
+                                      _ptr(codes), _ptr(scales), _ptr(amax), _ptr(s_enc))
+    if rc != 0:
+        raise ValueError(f"orc_rht_quantize_sized: status {rc}")
+    return QTensor(codes, scales, float(amax[0]), float(s_enc[0]), channels, tokens, BLOCK_1X16)
 
 
 def rht_transform(x_u16, sign_mask):

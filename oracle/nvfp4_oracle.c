@@ -456,6 +456,115 @@ int orc_rht_quantize(const uint16_t* x, int64_t tokens, int64_t channels, uint32
 }
 
 /* ------------------------------------------------------------------------ */
+/* RHT sizes other than 16 (ablation; [P1] TZ 2.B.2 reports 16 x 16 as the  */
+/* best size for large models, so others were compared).                    */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Reading: the D-point transform generalises the 16-point one unchanged in
+ * form -- v <- 2^-(log2 D / 2) * H_D * diag(d) * v, signs first, then the
+ * radix-2 butterfly with strides 1, 2, ..., D/2 (each sum and difference
+ * rounded to fp32), then the exact power-of-two normalisation -- for the
+ * sizes whose normalisation 1/sqrt(D) is a power of two: D = 4, 16, 64.
+ * d_i = -1 iff bit i of the 64-bit sign word is set; the 64 signs are
+ * words 0 (bits 0-31) and 1 (bits 32-63) of the Philox block that gives the
+ * 16-point signs, so the first 16 agree with orc_rht_sign_mask.
+ */
+uint64_t orc_rht_signs64(uint64_t seed)
+{
+    uint32_t ctr[4] = {0u, 0u, 0u, 1u};
+    uint32_t key[2] = {(uint32_t)seed, (uint32_t)(seed >> 32)};
+    uint32_t w[4];
+    orc_philox4x32_10(ctr, key, w);
+    return (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+}
+
+void orc_rht_sized(const float* in, int D, uint64_t signs, float* out)
+{
+    float v[64];
+    for (int i = 0; i < D; ++i) v[i] = ((signs >> i) & 1) ? -in[i] : in[i];
+    for (int h = 1; h < D; h <<= 1)
+        for (int i = 0; i < D; ++i)
+            if ((i & h) == 0) {
+                float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    const float norm = D == 4 ? 0.5f : (D == 16 ? 0.25f : 0.125f);
+    for (int i = 0; i < D; ++i) out[i] = v[i] * norm;
+}
+
+static int rht_size_ok(int D) { return D == 4 || D == 16 || D == 64; }
+
+/*
+ * The wgrad operand with a D-point transform along tokens (D = 4, 16, 64),
+ * then transpose and 1x16 quantisation exactly as orc_rht_quantize (blocks
+ * of 16 tokens, amax over the transformed tensor, SR index c*tokens + t).
+ * tokens must be a multiple of 16 and of D.
+ */
+int orc_rht_quantize_sized(const uint16_t* x, int64_t tokens, int64_t channels, int D,
+                           uint64_t signs, int rounding, uint64_t seed, const float* amax_in,
+                           uint8_t* codes, uint8_t* scales, float* amax_out, float* s_enc_out)
+{
+    if (!rht_size_ok(D)) return ORC_ERR_MODE;
+    if (rounding != ORC_RNE && rounding != ORC_SR) return ORC_ERR_MODE;
+    if (tokens < 0 || channels < 0 || tokens % 16 != 0 || tokens % D != 0) return ORC_ERR_SHAPE;
+    const int64_t nb = tokens / 16;
+
+    /* step 1: amax of the transformed operand */
+    float amax = 0.0f;
+    if (amax_in) {
+        amax = *amax_in;
+    } else {
+        for (int64_t c = 0; c < channels; ++c)
+            for (int64_t j = 0; j < tokens / D; ++j) {
+                float v[64], w[64];
+                for (int i = 0; i < D; ++i) v[i] = bf16_to_f32(x[(D * j + i) * channels + c]);
+                orc_rht_sized(v, D, signs, w);
+                for (int i = 0; i < D; ++i)
+                    if (fabsf(w[i]) > amax) amax = fabsf(w[i]);
+            }
+    }
+    const float s_enc = orc_tensor_scale(amax);
+    *amax_out = amax;
+    *s_enc_out = s_enc;
+
+    /* steps 2-4 per (channel, 16-token block): the transformed values of
+       the block (from the D-token chunk that holds it, or from its 16 / D
+       chunks when D = 4), block scale, factor, codes */
+#pragma omp parallel for schedule(static)
+    for (int64_t c = 0; c < channels; ++c)
+        for (int64_t b = 0; b < nb; ++b) {
+            const int64_t t0 = 16 * b;
+            const int64_t u0 = D >= 16 ? (t0 / D) * D : t0;   /* first transformed chunk */
+            const int64_t u1 = D >= 16 ? u0 + D : t0 + 16;      /* end of the last one */
+            float w16[16];
+            for (int64_t u = u0; u < u1; u += D) {
+                float v[64], w[64];
+                for (int i = 0; i < D; ++i) v[i] = bf16_to_f32(x[(u + i) * channels + c]);
+                orc_rht_sized(v, D, signs, w);
+                for (int i = 0; i < D; ++i)
+                    if (u + i >= t0 && u + i < t0 + 16) w16[u + i - t0] = w[i];
+            }
+            float am = 0.0f;
+            for (int i = 0; i < 16; ++i)
+                if (fabsf(w16[i]) > am) am = fabsf(w16[i]);
+            const uint8_t sb = orc_block_scale(am, s_enc);
+            scales[c * nb + b] = sb;
+            const float f = orc_block_factor(sb, s_enc);
+            for (int i = 0; i < 16; ++i) {
+                const float y = w16[i] * f;
+                const int64_t t = t0 + i;
+                const uint8_t code = (rounding == ORC_RNE)
+                                         ? orc_e2m1_encode_rne(y)
+                                         : orc_e2m1_encode_sr(y, orc_sr_draw(seed, (uint64_t)(c * tokens + t)));
+                put_code(codes + c * (tokens / 2), t, code);
+            }
+        }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* MXFP4, the format NVFP4 is compared with ([P1] TZ 2.A).                  */
 /* ------------------------------------------------------------------------ */
 
