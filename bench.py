@@ -144,6 +144,63 @@ def mx_comparison(q, torch, layer, reps=5):
             "peak_tflops": PEAK_FP4_TFLOPS}
 
 
+def rht_size_study(q, torch, dev, reps=3, rows=40):
+    """Size ablation of the wgrad RHT (Technische Zusammenfassung 2.B.2: the
+    pages report 16 x 16 as the best size): for transforms of 1 (none), 4,
+    16 and 64 tokens, the 12B-layer wgrad dW = dY^T X with both operands
+    quantised through the transform (dY SR, X RNE, one sign vector), its
+    relative Frobenius error on sampled output rows against the exact
+    product of the bf16 inputs, and the quantiser and GEMM times."""
+    import numpy as np
+    from quantize_precision_gemm_amd import workloads as wl
+
+    out = {}
+    settings = {
+        "layer inputs (dY log-normal rows, X Student-t(4))": None,
+        "outliers (dY and X normal with 0.1 % of entries x 50)": "outliers",
+    }
+    for name, kind in settings.items():
+        if kind is None:
+            data = wl.layer_inputs(wl.LAYER_12B, seed=SEED, with_w=False)
+        else:
+            rng = np.random.default_rng(SEED + 7)
+            data = {"X": wl.normal_with_outliers(rng, (M, K)),
+                    "dY": wl.normal_with_outliers(rng, (M, N))}
+        to_dev = lambda u: torch.from_numpy(u.view(np.int16)).to(dev).view(torch.bfloat16)
+        x, dy = to_dev(data["X"]), to_dev(data["dY"])
+        pick = np.sort(np.random.default_rng(SEED + 3).choice(N, rows, replace=False))
+        xf = wl.bf16_bits_to_f32(data["X"]).astype(np.float64)
+        exact = wl.bf16_bits_to_f32(np.ascontiguousarray(data["dY"][:, pick])).astype(np.float64).T @ xf
+        signs = q.nvfp4_rht_signs64(SEED + 1000)
+        res = {}
+        for size in (1, 4, 16, 64):
+            gdyt = q.nvfp4_rht_quantize_sized(dy, size, signs, q.SR, SEED + 101)
+            gxt = q.nvfp4_rht_quantize_sized(x, size, signs, q.RNE)
+            dw = q.nvfp4_gemm(q.WGRAD, gdyt, gxt, out_dtype=torch.float32)
+            torch.cuda.synchronize()
+            got = dw[torch.from_numpy(pick).to(dev)].double().cpu().numpy()
+            err = float(np.linalg.norm(got - exact) / np.linalg.norm(exact))
+
+            def timed(f):
+                f()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(reps):
+                    f()
+                b.record()
+                torch.cuda.synchronize()
+                return a.elapsed_time(b) / reps
+            t_dy = timed(lambda: q.nvfp4_rht_quantize_sized(dy, size, signs, q.SR, SEED + 101, out=gdyt))
+            t_x = timed(lambda: q.nvfp4_rht_quantize_sized(x, size, signs, q.RNE, out=gxt))
+            res[str(size)] = {"wgrad_rel_fro_err": err, "quant_dY_ms": round(t_dy, 4),
+                              "quant_X_ms": round(t_x, 4)}
+        out[name] = res
+        del x, dy
+    return {"study": "wgrad RHT size (1 = no transform)", "workload": f"12B-layer wgrad: M={M}, "
+            f"N={N}, K={K}; error on {rows} sampled rows of dW against the exact dY^T X",
+            "results": out}
+
+
 def cpu_baseline(data, tokens=M):
     """The oracle on a token slice of the step; W's quantisation, which does not
     scale with tokens, is timed in full and counted at tokens/M of its time."""
@@ -225,6 +282,9 @@ def main():
                     help="time the step with the dual quantisers (one encode pass per tensor "
                          "for both operands) instead of separate ones; the other schedule is "
                          "timed beside it either way")
+    ap.add_argument("--rht-study", action="store_true",
+                    help="only run the wgrad RHT size ablation (sizes 1, 4, 16, 64) and print its "
+                         "JSON line")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="only run a plain elementwise copy of 1 GiB (bf16 negation, 3 launches): "
@@ -254,6 +314,9 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"calibration": "torch.neg bf16", "bytes_read_per_launch": 2 * n,
                           "bytes_written_per_launch": 2 * n, "launches": 3}), flush=True)
+        return
+    if args.rht_study:
+        print(json.dumps(rht_size_study(q, torch, dev)), flush=True)
         return
     if mlp:
         data, step = None, build_mlp_step(q, torch, dev, args.fused_quant)

@@ -200,6 +200,31 @@ int nvfp4_quantize_dual(const void* x, int64_t tokens, int64_t channels, int64_t
                         nvfp4_tensor* out_rht, void* stream);
 
 /*
+ * nvfp4_rht_quantize_sized -- nvfp4_rht_quantize with a transform of `size`
+ * tokens: 1 (no transform: the plain transposing quantiser), 4, 16 or 64.
+ * For the size ablation of "Pretraining Large Language Models with NVFP4",
+ * Technische Zusammenfassung 2.B.2 (16 x 16 was the best size for large
+ * models).  The D-point transform is the 16-point one generalised: signs,
+ * radix-2 butterfly with strides 1 .. D/2 in fp32, then the exact factor
+ * 2^-(log2 D / 2); size 16 gives exactly nvfp4_rht_quantize's result.
+ *   tokens    a multiple of 16 and of size; channels a multiple of 8.
+ *   signs     bit i set: the i-th sign of a chunk is -1 (bits 0 .. size-1
+ *             are used; nvfp4_rht_signs64 draws them).
+ *   other arguments, layout and errors as for nvfp4_rht_quantize; the amax
+ *             (if not given) is taken over the transformed values.
+ */
+int nvfp4_rht_quantize_sized(const void* x, int64_t tokens, int64_t channels, int64_t ld_x,
+                             int32_t size, uint64_t signs, int32_t rounding, uint64_t seed,
+                             const float* amax_in, nvfp4_tensor* out, void* stream);
+
+/*
+ * nvfp4_rht_signs64 -- host helper: 64 random signs, words 0 (bits 0-31) and
+ * 1 (bits 32-63) of the Philox4x32-10 block of nvfp4_rht_sign_mask, whose 16
+ * bits are the low 16 here.
+ */
+uint64_t nvfp4_rht_signs64(uint64_t seed);
+
+/*
  * nvfp4_amax -- tensor amax of a bf16 matrix and, optionally, of its 16-point
  * random Hadamard transform along the rows, in one pass over the data.
  * Defines: "Pretraining Large Language Models with NVFP4", Technische

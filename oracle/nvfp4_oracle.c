@@ -490,11 +490,13 @@ void orc_rht_sized(const float* in, int D, uint64_t signs, float* out)
                 v[i] = a + b;
                 v[i + h] = a - b;
             }
-    const float norm = D == 4 ? 0.5f : (D == 16 ? 0.25f : 0.125f);
+    const float norm = D == 1 ? 1.0f : (D == 4 ? 0.5f : (D == 16 ? 0.25f : 0.125f));
     for (int i = 0; i < D; ++i) out[i] = v[i] * norm;
 }
 
-static int rht_size_ok(int D) { return D == 4 || D == 16 || D == 64; }
+/* D = 1 is no transform (only the sign of bit 0): the plain transposing
+   quantiser, the baseline of the size comparison */
+static int rht_size_ok(int D) { return D == 1 || D == 4 || D == 16 || D == 64; }
 
 /*
  * The wgrad operand with a D-point transform along tokens (D = 4, 16, 64),

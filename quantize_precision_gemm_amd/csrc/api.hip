@@ -195,6 +195,37 @@ int nvfp4_quantize_dual(const void* x, int64_t tokens, int64_t channels, int64_t
     return launch_status();
 }
 
+int nvfp4_rht_quantize_sized(const void* x, int64_t tokens, int64_t channels, int64_t ld_x,
+                             int32_t size, uint64_t signs, int32_t rounding, uint64_t seed,
+                             const float* amax_in, nvfp4_tensor* out, void* stream)
+{
+    if (size != 1 && size != 4 && size != 16 && size != 64) return NVFP4_ERR_MODE;
+    if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_MODE;
+    if (tokens < 0 || channels < 0 || tokens % 16 != 0 || tokens % size != 0 || channels % 8 != 0)
+        return NVFP4_ERR_SHAPE;
+    if (!x && tokens > 0 && channels > 0) return NVFP4_ERR_NULL;
+    if (ld_x < channels) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld_x % 8 != 0) return NVFP4_ERR_ALIGN;
+    if (amax_in && !aligned(amax_in, 4)) return NVFP4_ERR_ALIGN;
+    if (out && (out->codes_t || out->scales_t)) return NVFP4_ERR_MODE;
+    int st = check_out(out, channels, tokens, NVFP4_BLOCK_1X16);
+    if (st != NVFP4_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const float* amax_src = amax_in;
+    if (!amax_src) {
+        nvfp4::launch_rhtd_amax(xb, tokens, channels, ld_x, size, signs, out->amax, s);
+        amax_src = out->amax;
+    }
+    nvfp4::launch_rhtd_quant(xb, tokens, channels, ld_x, size, signs, rounding, seed, amax_src,
+                             qout_of(out), s);
+    out->rows = channels;
+    out->cols = tokens;
+    out->block = NVFP4_BLOCK_1X16;
+    return launch_status();
+}
+
 int nvfp4_amax(const void* x, int64_t rows, int64_t cols, int64_t ld_x, uint32_t sign_mask,
                float* amax, float* amax_rht, void* stream)
 {
@@ -236,6 +267,13 @@ uint32_t nvfp4_rht_sign_mask(uint64_t seed)
     uint32_t c[4] = {0u, 0u, 0u, 1u};
     philox_host(c, (uint32_t)seed, (uint32_t)(seed >> 32));
     return c[0] & 0xFFFFu;
+}
+
+uint64_t nvfp4_rht_signs64(uint64_t seed)
+{
+    uint32_t c[4] = {0u, 0u, 0u, 1u};
+    philox_host(c, (uint32_t)seed, (uint32_t)(seed >> 32));
+    return (uint64_t)c[0] | ((uint64_t)c[1] << 32);
 }
 
 }  // extern "C"

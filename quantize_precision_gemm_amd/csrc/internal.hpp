@@ -52,6 +52,13 @@ void launch_dual_quant(const uint16_t* x, int64_t tokens, int64_t channels, int6
                        const float* amax_src, const float* amax_rht_src, const QOut& o,
                        const QOut& o_rht, hipStream_t s);
 
+// Sized RHT (size 1, 4, 16 or 64 tokens) + transpose + 1x16 quantisation.
+void launch_rhtd_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld, int size,
+                      uint64_t signs, float* amax, hipStream_t s);
+void launch_rhtd_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld, int size,
+                       uint64_t signs, int rounding, uint64_t seed, const float* amax_src,
+                       const QOut& o, hipStream_t s);
+
 // MXFP4: mode 0 blocks of 32 along the rows of x; 1 the transposed matrix;
 // 2 the transposed matrix after the 16-point RHT (o: codes and scales only).
 void launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int mode,

@@ -583,6 +583,136 @@ __global__ __launch_bounds__(256) void k_dual_quant(
 }
 
 // ---------------------------------------------------------------------------
+// Sized random Hadamard transforms (1, 4, 16 or 64 points) for the size
+// ablation of the wgrad operands.  Same tile and thread map as k_rht_quant
+// (a thread: 16 tokens x 8 channels); a 64-point chunk spans the lanes
+// t, t ^ 16, t ^ 32, t ^ 48 of one wave, whose last two butterfly stages
+// (strides 16 and 32) exchange values with lane shuffles.  Size 1 is the
+// plain transposing quantiser (no transform) -- the baseline of the study.
+// The transform: signs, butterfly strides 1 .. D/2 (each sum and difference
+// rounded to fp32, in that order), then the exact normalisation 2^-(log2 D/2).
+// ---------------------------------------------------------------------------
+
+template <int D>
+__device__ __forceinline__ void rht_sized(float (&v)[16], uint64_t signs, int j)
+{
+    // sign of token i of this lane's chunk: bit (16 j + i) mod D
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int bit = D >= 16 ? (16 * (j & (D / 16 - 1)) + i) : (i & (D - 1));
+        v[i] = __uint_as_float(__float_as_uint(v[i]) ^ ((uint32_t)((signs >> bit) & 1u) << 31));
+    }
+#pragma unroll
+    for (int h = 1; h < (D < 16 ? D : 16); h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+            if ((i & h) == 0) {
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
+    if constexpr (D == 64) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {  // strides 16 and 32 tokens: partner chunk j ^ (1 << s)
+            const bool upper = (j >> s) & 1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+                const float o = __shfl_xor(v[i], 16 << s, 64);
+                v[i] = upper ? o - v[i] : v[i] + o;
+            }
+        }
+    }
+    const float norm = D == 64 ? 0.125f : (D == 16 ? 0.25f : (D == 4 ? 0.5f : 1.0f));
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] *= norm;
+}
+
+template <int D>
+__global__ __launch_bounds__(256) void k_rhtd_amax(const uint16_t* __restrict__ x, int64_t tokens,
+                                                   int64_t channels, int64_t ld, uint64_t signs,
+                                                   uint32_t* __restrict__ amax_bits)
+{
+    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int64_t bch = (channels + kRhtCh - 1) / kRhtCh, btok = (tokens + kRhtTok - 1) / kRhtTok;
+    uint32_t m = 0u;
+    for (int64_t bt = blockIdx.x; bt < bch * btok; bt += gridDim.x) {
+        const int64_t ch0 = (bt % bch) * kRhtCh + cg * 8;
+        const int64_t tok0 = (bt / bch) * kRhtTok + j * 16;
+        // tokens is a multiple of 16 and of D: a D-token chunk is valid as a
+        // whole, so the shuffle partners of a valid lane are valid
+        if (ch0 < channels && tok0 < tokens) {
+            uint4 raw[16];
+            load_rht_raw(x, ld, tok0, ch0, raw);
+#pragma unroll
+            for (int c = 0; c < 8; ++c) {
+                float v[16];
+                unpack_channel(raw, c, v);
+                rht_sized<D>(v, signs, j);
+                m = max(m, __float_as_uint(absmax16(v)));
+            }
+        }
+    }
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) merge_amax(amax_bits, max(max(red[0], red[1]), max(red[2], red[3])));
+}
+
+template <bool kSR, int D>
+__global__ __launch_bounds__(256) void k_rhtd_quant(
+    const uint16_t* __restrict__ x, int64_t tokens, int64_t channels, int64_t ld, uint64_t signs,
+    const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
+    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    float* __restrict__ amax_out, float* __restrict__ s_enc_out)
+{
+    __shared__ uint2 scodes[kRhtCh][17];
+    __shared__ uint8_t sscale[kRhtCh][16];
+
+    const int cg = threadIdx.x & 15, j = threadIdx.x >> 4;
+    const int64_t chb = (int64_t)blockIdx.x * kRhtCh, tokb = (int64_t)blockIdx.y * kRhtTok;
+    const int64_t ch0 = chb + cg * 8;
+    const int64_t tok0 = tokb + j * 16;
+    const float amax = *amax_src;
+    const float s_enc = tensor_scale(amax);
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) {
+        *amax_out = amax;
+        *s_enc_out = s_enc;
+    }
+    if (ch0 < channels && tok0 < tokens) {
+        uint4 raw[16];
+        load_rht_raw(x, ld, tok0, ch0, raw);
+#pragma unroll
+        for (int c = 0; c < 8; ++c) {
+            float v[16];
+            unpack_channel(raw, c, v);
+            rht_sized<D>(v, signs, j);
+            const uint32_t sb = block_scale(absmax16(v), s_enc);
+            const float f = block_factor(sb, s_enc);
+            uint2 pk;
+            if constexpr (kSR)
+                pk = encode16_sr(v, f, seed, (uint64_t)((ch0 + c) * tokens + tok0) >> 3);
+            else
+                pk = encode16_rne(v, f);
+            scodes[cg * 8 + c][j] = pk;
+            sscale[cg * 8 + c][j] = (uint8_t)sb;
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+        const int idx = it * 256 + threadIdx.x;
+        const int row = idx >> 4, q = idx & 15;
+        const int64_t ch = chb + row, tk = tokb + q * 16;
+        if (ch < channels && tk < tokens) {
+            *reinterpret_cast<uint2*>(codes + ch * ld_codes + (tk >> 1)) = scodes[row][q];
+            scales[ch * ld_scales + (tk >> 4)] = sscale[row][q];
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // MXFP4 quantisers (the comparison format: 32-element blocks, one UE8M0
 // scale each, no tensor scale).  Shared exponent e = floor(log2(amax_b)) - 2
 // clamped to [-127, 127]; from the fp32 (or bf16) exponent field E of amax_b
@@ -828,6 +958,44 @@ void launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, 
         sr ? go(k_mx_quant_cols<true, false>) : go(k_mx_quant_cols<false, false>);
     else
         sr ? go(k_mx_quant_cols<true, true>) : go(k_mx_quant_cols<false, true>);
+}
+
+void launch_rhtd_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld, int size,
+                      uint64_t signs, float* amax, hipStream_t s)
+{
+    uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, bits);
+    if (tokens == 0 || channels == 0) return;
+    dim3 g(grid_for(((channels + kRhtCh - 1) / kRhtCh) * ((tokens + kRhtTok - 1) / kRhtTok), 1, kAmaxGrid));
+    auto go = [&](auto kern) { hipLaunchKernelGGL(kern, g, dim3(256), 0, s, x, tokens, channels, ld, signs, bits); };
+    switch (size) {
+        case 1: go(k_rhtd_amax<1>); break;
+        case 4: go(k_rhtd_amax<4>); break;
+        case 16: go(k_rhtd_amax<16>); break;
+        default: go(k_rhtd_amax<64>); break;
+    }
+}
+
+void launch_rhtd_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld, int size,
+                       uint64_t signs, int rounding, uint64_t seed, const float* amax_src,
+                       const QOut& o, hipStream_t s)
+{
+    if (tokens == 0 || channels == 0) {
+        hipLaunchKernelGGL(k_publish, dim3(1), dim3(1), 0, s, amax_src, o.amax, o.s_enc);
+        return;
+    }
+    dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
+    auto go = [&](auto kern) {
+        hipLaunchKernelGGL(kern, g, dim3(256), 0, s, x, tokens, channels, ld, signs, amax_src, seed,
+                           o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc);
+    };
+    const bool sr = rounding == 1;
+    switch (size) {
+        case 1: sr ? go(k_rhtd_quant<true, 1>) : go(k_rhtd_quant<false, 1>); break;
+        case 4: sr ? go(k_rhtd_quant<true, 4>) : go(k_rhtd_quant<false, 4>); break;
+        case 16: sr ? go(k_rhtd_quant<true, 16>) : go(k_rhtd_quant<false, 16>); break;
+        default: sr ? go(k_rhtd_quant<true, 64>) : go(k_rhtd_quant<false, 64>); break;
+    }
 }
 
 }  // namespace nvfp4

@@ -173,6 +173,19 @@ def test_mx_out_and_gemm_validation(lib):
     assert g(mx(1 << 27, 64), mx(8, 64)) == -2      # codes span 4 GiB: beyond 32-bit offsets
 
 
+def test_rht_sized_validation(lib):
+    d = _desc(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, ld_codes=32, ld_scales=4)
+    q = lambda tokens, channels, size, rnd=0: lib.nvfp4_rht_quantize_sized(
+        FAKE, tokens, channels, 16, size, 0, rnd, 0, None, ctypes.byref(d), None)
+    assert q(64, 16, 8) == -4            # size 8: normalisation not a power of two
+    assert q(64, 16, 32) == -4
+    assert q(48, 16, 64) == -2           # tokens not whole 64-token chunks
+    assert q(24, 16, 4) == -2            # tokens not a multiple of 16
+    assert q(64, 12, 4) == -2            # channels not a multiple of 8
+    assert q(64, 16, 4, rnd=3) == -4
+    assert lib.nvfp4_rht_signs64(7) & 0xFFFF == lib.nvfp4_rht_sign_mask(7)
+
+
 @pytest.mark.parametrize("fn", ["nvfp4_gemm", "nvfp4_gemm_fp8blk"])
 def test_gemm_validation(lib, fn):
     gemm = getattr(lib, fn)

@@ -107,3 +107,16 @@ def test_shapes_and_sizes_checked():
         oracle.rht_quantize_sized(x, 64, 0)      # 48 tokens: not whole 64-token chunks
     with pytest.raises(ValueError):
         oracle.rht_quantize_sized(x, 8, 0)       # size 8: normalisation not a power of two
+
+
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_size1_is_the_plain_transposed_quantiser(rounding):
+    # no transform: the wgrad operand is the 1x16 quantisation of x^T, whose
+    # SR index r * tokens + t is the same as the sized quantiser's
+    rng = np.random.default_rng(40 + rounding)
+    x = wl.lognormal_rows(rng, (64, 40))
+    got = oracle.rht_quantize_sized(x, 1, 0, rounding, 8)
+    want = oracle.quantize(np.ascontiguousarray(x.T), oracle.BLOCK_1X16, rounding, 8)
+    np.testing.assert_array_equal(got.codes, want.codes)
+    np.testing.assert_array_equal(got.scales, want.scales)
+    assert got.amax == want.amax
