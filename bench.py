@@ -240,6 +240,14 @@ def build_layer_step(q, torch, dev, fused_quant=False):
     return data, TrainingStep(torch, [layer], dev)
 
 
+def as_mxfp4(q, torch, dev, step):
+    """The same step over the same tensors with every NVFP4 layer in MXFP4."""
+    from quantize_precision_gemm_amd.step import MXFP4Linear, NVFP4Linear, TrainingStep
+    layers = [MXFP4Linear(q, torch, l.x, l.w, l.dy, l.seed) if isinstance(l, NVFP4Linear) else l
+              for l in step.layers]
+    return TrainingStep(torch, layers, dev)
+
+
 def with_schedule(q, torch, dev, step, fused_quant):
     """The same step over the same tensors, with the NVFP4 layers' quantisers
     fused (nvfp4_quantize_dual) or separate."""
@@ -348,6 +356,18 @@ def main():
     torch.cuda.synchronize()
     alt_ms = (time.perf_counter() - t0) * 1e3 / steps
 
+    # the same step in the comparison format MXFP4, timed the same way
+    mxs = as_mxfp4(q, torch, dev, step)
+    for _ in range(warmup):
+        mxs.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        mxs.run()
+    torch.cuda.synchronize()
+    mx_ms = (time.perf_counter() - t0) * 1e3 / steps
+    del mxs
+
     # per-operation times: separate, serialised passes with events
     times = {}
     for _ in range(max(3, steps // 2)):
@@ -449,6 +469,11 @@ def main():
         mx["speedup_vs_nvfp4"] = {k: round(v / result["gemm_tflops"][k], 2)
                                   for k, v in mx["gemm_tflops"].items()}
         result["mxfp4_comparison"] = mx
+    result["mxfp4_step"] = {
+        "ms_per_step": round(mx_ms, 4),
+        "tflops": round(step.flops() / (mx_ms * 1e-3) / 1e12, 2),
+        "note": "the same step with every NVFP4 layer in MXFP4 (MXFP4Linear: no amax passes, "
+                "W quantised along K and along N), timed the same way"}
     result["roofline"] = {
         "kernel": "k_gemm_nv<bf16 out> (fprop, dgrad launches)", "bound": "mfma",
         "achieved": round(achieved, 1), "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",

@@ -117,6 +117,68 @@ class NVFP4Linear:
         ]
 
 
+class MXFP4Linear:
+    """One linear layer's training step in MXFP4, the format the pages set
+    NVFP4 against (Technische Zusammenfassung 2.A): E2M1 with one UE8M0
+    scale per 32 elements, no tensor scale, so no amax passes.  The roles
+    follow the NVFP4 recipe: X and W RNE, dY SR, the wgrad operands through
+    the 16-point RHT along tokens.  MXFP4 has no 2D blocks, so W is
+    quantised twice: along K for fprop and along N for dgrad.
+    Outputs as NVFP4Linear's."""
+
+    def __init__(self, q, torch, x, w, dy, seed):
+        self.q, self.torch = q, torch
+        self.x, self.w, self.dy = x, w, dy
+        M, K = x.shape
+        N = w.shape[0]
+        assert w.shape == (N, K) and dy.shape == (M, N)
+        self.M, self.K, self.N = M, K, N
+        dev = x.device
+        self.seed = seed
+        mx = lambda r, c: q.alloc_nvfp4(r, c, q.BLOCK_MX32, device=dev)
+        self.gx, self.gw, self.gwt = mx(M, K), mx(N, K), mx(K, N)
+        self.gdy, self.gdyt, self.gxt = mx(M, N), mx(N, M), mx(K, M)
+        self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        self.dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)
+        self.mask = q.nvfp4_rht_sign_mask(seed + RHT_SEED)
+
+    def flops(self):
+        return 3 * 2.0 * self.M * self.N * self.K
+
+    def weight_ops(self):
+        q = self.q
+        return [("mx_quant_W", lambda: q.nvfp4_mx_quantize(self.w, q.MX_ROWS, out=self.gw)),
+                ("mx_quant_Wt", lambda: q.nvfp4_mx_quantize(self.w, q.MX_COLS, out=self.gwt))]
+
+    def forward_ops(self):
+        q = self.q
+        return [("mx_quant_X", lambda: q.nvfp4_mx_quantize(self.x, q.MX_ROWS, out=self.gx)),
+                ("mx_fprop", lambda: q.nvfp4_mx_gemm(self.gx, self.gw, out=self.y))]
+
+    def backward_shared_ops(self):
+        return []
+
+    def backward_quant_ops(self):
+        q = self.q
+        return [("mx_quant_dY", lambda: q.nvfp4_mx_quantize(self.dy, q.MX_ROWS, 0, q.SR,
+                                                            self.seed + SR_SEED_DY, out=self.gdy))]
+
+    def dgrad_ops(self):
+        q = self.q
+        return [("mx_dgrad", lambda: q.nvfp4_mx_gemm(self.gdy, self.gwt, out=self.dx))]
+
+    def wgrad_ops(self):
+        q = self.q
+        return [
+            ("mx_rht_dY", lambda: q.nvfp4_mx_quantize(self.dy, q.MX_COLS_RHT, self.mask, q.SR,
+                                                      self.seed + SR_SEED_DY_RHT, out=self.gdyt)),
+            ("mx_rht_X", lambda: q.nvfp4_mx_quantize(self.x, q.MX_COLS_RHT, self.mask, q.RNE,
+                                                     out=self.gxt)),
+            ("mx_wgrad", lambda: q.nvfp4_mx_gemm(self.gdyt, self.gxt, out=self.dw)),
+        ]
+
+
 class BF16Linear:
     """One linear layer's training step kept in bf16: the three GEMMs on the
     layer's own tensors, fp32 accumulation; outputs as NVFP4Linear's."""

@@ -214,3 +214,29 @@ def test_mx_gemm_full_size(env, pass_):
     rows = np.unique(np.concatenate([[0, qa.rows - 1], rng.choice(qa.rows, 40, replace=False)]))
     print(f"mx full {pass_}: gemm", flush=True)
     _check_gemm(env, qa, qb, oa, ob, rows, f"{pass_} full")
+
+
+def test_mx_training_step(env):
+    # the MXFP4 layer of the training step runs exactly the calls it names:
+    # its outputs equal the library calls made one by one (bit for bit) and
+    # the oracle's MXFP4 passes (within the GEMM tolerance)
+    torch, oracle, q, wl, dev = env
+    from quantize_precision_gemm_amd.step import MXFP4Linear, TrainingStep, SR_SEED_DY, SR_SEED_DY_RHT
+    rng = np.random.default_rng(33)
+    M, K, N, seed = 512, 384, 640, 7
+    xb, wb, dyb = wl.normal(rng, (M, K), 1.0), wl.normal(rng, (N, K), 0.02), wl.lognormal_rows(rng, (M, N))
+    x, w, dy = to_dev(xb, dev), to_dev(wb, dev), to_dev(dyb, dev)
+    print("mx training step", flush=True)
+    layer = MXFP4Linear(q, torch, x, w, dy, seed)
+    TrainingStep(torch, [layer], dev).run()
+    mask = layer.mask
+    y = q.nvfp4_mx_gemm(q.nvfp4_mx_quantize(x), q.nvfp4_mx_quantize(w))
+    dx = q.nvfp4_mx_gemm(q.nvfp4_mx_quantize(dy, q.MX_ROWS, 0, q.SR, seed + SR_SEED_DY),
+                         q.nvfp4_mx_quantize(w, q.MX_COLS))
+    dw = q.nvfp4_mx_gemm(q.nvfp4_mx_quantize(dy, q.MX_COLS_RHT, mask, q.SR, seed + SR_SEED_DY_RHT),
+                         q.nvfp4_mx_quantize(x, q.MX_COLS_RHT, mask), torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(layer.y, y) and torch.equal(layer.dx, dx) and torch.equal(layer.dw, dw)
+    odw = oracle.mx_gemm(oracle.mx_quantize(dyb, oracle.MX_COLS_RHT, mask, oracle.SR, seed + SR_SEED_DY_RHT),
+                         oracle.mx_quantize(xb, oracle.MX_COLS_RHT, mask))
+    assert rel_fro(layer.dw.cpu().numpy(), odw) <= TOL
