@@ -91,6 +91,8 @@ def lib():
         L.orc_rht_sized.restype = None
         L.orc_rht_quantize_sized.argtypes = [P, i64, i64, ctypes.c_int, u64, ctypes.c_int, u64, P, P, P, P, P]
         L.orc_rht_quantize_sized.restype = ctypes.c_int
+        L.orc_quantize_rht_rows.argtypes = [P, i64, i64, ctypes.c_int, u32, ctypes.c_int, u64, P, P, P, P, P]
+        L.orc_quantize_rht_rows.restype = ctypes.c_int
         L.orc_mx_quantize.argtypes = [P, i64, i64, ctypes.c_int, u32, ctypes.c_int, u64, P, P]
         L.orc_mx_quantize.restype = ctypes.c_int
         L.orc_mx_exponent.argtypes = [ctypes.c_float]
@@ -296,6 +298,25 @@ def rht_quantize_sized(x_u16, size, signs, rounding=RNE, seed=0, amax_in=None):
     if rc != 0:
         raise ValueError(f"orc_rht_quantize_sized: status {rc}")
     return QTensor(codes, scales, float(amax[0]), float(s_enc[0]), channels, tokens, BLOCK_1X16)
+
+
+def quantize_rht_rows(x_u16, sign_mask, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None):
+    """The fprop / dgrad operand with the 16-point RHT along its rows (the
+    contraction dimension), then NVFP4 quantisation as quantize(); the
+    ablation of Technische Zusammenfassung 2.B.2's wgrad-only choice."""
+    x = _u16(x_u16)
+    rows, cols = x.shape
+    codes = np.zeros((rows, cols // 2), np.uint8)
+    sr = rows if block == BLOCK_1X16 else rows // 16
+    scales = np.zeros((sr, cols // 16), np.uint8)
+    amax = np.zeros(1, np.float32)
+    s_enc = np.zeros(1, np.float32)
+    ain = None if amax_in is None else np.array([amax_in], np.float32)
+    rc = lib().orc_quantize_rht_rows(_ptr(x), rows, cols, block, sign_mask, rounding, seed, _ptr(ain),
+                                     _ptr(codes), _ptr(scales), _ptr(amax), _ptr(s_enc))
+    if rc != 0:
+        raise ValueError(f"orc_quantize_rht_rows: status {rc}")
+    return QTensor(codes, scales, float(amax[0]), float(s_enc[0]), rows, cols, block)
 
 
 def rht_transform(x_u16, sign_mask):

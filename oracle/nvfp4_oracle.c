@@ -23,6 +23,7 @@
 #include <float.h>
 #include <math.h>
 #include <stdint.h>
+#include <stdlib.h>
 #include <string.h>
 
 #define ORC_OK 0
@@ -563,6 +564,92 @@ int orc_rht_quantize_sized(const uint16_t* x, int64_t tokens, int64_t channels, 
                 put_code(codes + c * (tokens / 2), t, code);
             }
         }
+    return ORC_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* RHT on the fprop / dgrad operands (ablation; [P1] TZ 2.B.2 reports no    */
+/* significant benefit there, which is why the recipe keeps it to wgrad).   */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Reading: for fprop and dgrad the transform runs along the contraction
+ * dimension, i.e. along the rows of X, W (fprop) and dY, W^T (dgrad): the
+ * 16-point transform of R-11 on every aligned 16-element chunk of a row --
+ * exactly the chunk of a 1x16 block, and a row of a 16x16 tile -- with one
+ * sign vector for both operands of a GEMM, so that (A Q^T)(B Q^T)^T = A B^T.
+ * Then NVFP4 quantisation as orc_quantize (tensor amax over the transformed
+ * values; 1x16 or 16x16 blocks; SR index r * cols + c).
+ */
+int orc_quantize_rht_rows(const uint16_t* x, int64_t rows, int64_t cols, int block,
+                          uint32_t sign_mask, int rounding, uint64_t seed, const float* amax_in,
+                          uint8_t* codes, uint8_t* scales, float* amax_out, float* s_enc_out)
+{
+    if (rows < 0 || cols < 0 || cols % 16 != 0) return ORC_ERR_SHAPE;
+    if (block == ORC_BLOCK_16X16 && rows % 16 != 0) return ORC_ERR_SHAPE;
+    if (block != ORC_BLOCK_1X16 && block != ORC_BLOCK_16X16) return ORC_ERR_MODE;
+    if (rounding != ORC_RNE && rounding != ORC_SR) return ORC_ERR_MODE;
+    const int64_t nb = cols / 16;
+
+    /* the transformed rows (fp32), chunk by chunk */
+    float* t = (float*)malloc(sizeof(float) * (size_t)(rows * cols > 0 ? rows * cols : 1));
+    if (!t) return ORC_ERR_SHAPE;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t b = 0; b < nb; ++b) {
+            float v[16];
+            for (int i = 0; i < 16; ++i) v[i] = bf16_to_f32(x[r * cols + 16 * b + i]);
+            orc_rht16(v, sign_mask, t + r * cols + 16 * b);
+        }
+
+    /* step 1: tensor amax over the transformed values */
+    float amax = 0.0f;
+    if (amax_in) {
+        amax = *amax_in;
+    } else {
+        for (int64_t i = 0; i < rows * cols; ++i)
+            if (fabsf(t[i]) > amax) amax = fabsf(t[i]);
+    }
+    const float s_enc = orc_tensor_scale(amax);
+    *amax_out = amax;
+    *s_enc_out = s_enc;
+
+    /* step 2: block scales */
+    if (block == ORC_BLOCK_1X16) {
+#pragma omp parallel for schedule(static)
+        for (int64_t r = 0; r < rows; ++r)
+            for (int64_t b = 0; b < nb; ++b) {
+                float am = 0.0f;
+                for (int i = 0; i < 16; ++i)
+                    if (fabsf(t[r * cols + 16 * b + i]) > am) am = fabsf(t[r * cols + 16 * b + i]);
+                scales[r * nb + b] = orc_block_scale(am, s_enc);
+            }
+    } else {
+#pragma omp parallel for schedule(static)
+        for (int64_t tr = 0; tr < rows / 16; ++tr)
+            for (int64_t b = 0; b < nb; ++b) {
+                float am = 0.0f;
+                for (int i = 0; i < 16; ++i)
+                    for (int j = 0; j < 16; ++j)
+                        if (fabsf(t[(16 * tr + i) * cols + 16 * b + j]) > am)
+                            am = fabsf(t[(16 * tr + i) * cols + 16 * b + j]);
+                scales[tr * nb + b] = orc_block_scale(am, s_enc);
+            }
+    }
+
+    /* step 3: element codes */
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c) {
+            const uint8_t sb = block == ORC_BLOCK_1X16 ? scales[r * nb + c / 16]
+                                                       : scales[(r / 16) * nb + c / 16];
+            const float y = t[r * cols + c] * orc_block_factor(sb, s_enc);
+            const uint8_t code = (rounding == ORC_RNE)
+                                     ? orc_e2m1_encode_rne(y)
+                                     : orc_e2m1_encode_sr(y, orc_sr_draw(seed, (uint64_t)(r * cols + c)));
+            put_code(codes + r * (cols / 2), c, code);
+        }
+    free(t);
     return ORC_OK;
 }
 

@@ -120,3 +120,44 @@ def test_size1_is_the_plain_transposed_quantiser(rounding):
     np.testing.assert_array_equal(got.codes, want.codes)
     np.testing.assert_array_equal(got.scales, want.scales)
     assert got.amax == want.amax
+
+
+# --- RHT along the rows: the fprop / dgrad operands --------------------------
+
+@pytest.mark.parametrize("block", [0, 1])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_row_rht_quantiser_equals_quantised_matrix_form(block, rounding):
+    # integer inputs: the per-chunk transform (Sylvester form) is exact and
+    # bf16-representable, so the plain quantiser applied to it gives the same
+    # codes (as values: exact zeros may carry either sign), scales and scale
+    rng = np.random.default_rng(50 + 2 * block + rounding)
+    rows, cols = 48, 96
+    xi = rng.integers(-6, 7, (rows, cols))
+    x = wl.f32_to_bf16_bits(xi.astype(np.float32))
+    mask = oracle.rht_sign_mask(13)
+    d = np.array([-1 if (mask >> i) & 1 else 1 for i in range(16)], np.int64)
+    H = hadamard(16)
+    T = (xi.reshape(rows, cols // 16, 16) * d) @ H.T / 4.0      # H symmetric: row chunk v -> H D v
+    tb = wl.f32_to_bf16_bits(T.reshape(rows, cols).astype(np.float32))
+    assert np.array_equal(wl.bf16_bits_to_f32(tb).astype(np.float64), T.reshape(rows, cols))
+    want = oracle.quantize(tb, block, rounding, 3)
+    got = oracle.quantize_rht_rows(x, mask, block, rounding, 3)
+    gv = oracle.E2M1_VALUES[oracle.unpack_codes(got.codes, cols)]
+    wv = oracle.E2M1_VALUES[oracle.unpack_codes(want.codes, cols)]
+    np.testing.assert_array_equal(gv, wv)
+    np.testing.assert_array_equal(got.scales, want.scales)
+    assert got.amax == want.amax and got.s_enc == want.s_enc
+
+
+def test_row_rht_preserves_the_product():
+    # one sign vector for both operands: the transforms cancel in A B^T
+    rng = np.random.default_rng(60)
+    a = wl.f32_to_bf16_bits(rng.integers(-8, 9, (8, 64)).astype(np.float32))
+    b = wl.f32_to_bf16_bits(rng.integers(-8, 9, (5, 64)).astype(np.float32))
+    mask = oracle.rht_sign_mask(2)
+    ta = np.concatenate([oracle.rht16(wl.bf16_bits_to_f32(a)[r, 16 * j:16 * j + 16], mask)
+                         for r in range(8) for j in range(4)]).reshape(8, 64).astype(np.float64)
+    tb = np.concatenate([oracle.rht16(wl.bf16_bits_to_f32(b)[r, 16 * j:16 * j + 16], mask)
+                         for r in range(5) for j in range(4)]).reshape(5, 64).astype(np.float64)
+    exact = wl.bf16_bits_to_f32(a).astype(np.float64) @ wl.bf16_bits_to_f32(b).astype(np.float64).T
+    np.testing.assert_array_equal(ta @ tb.T, exact)
