@@ -145,12 +145,14 @@ def mx_comparison(q, torch, layer, reps=5):
 
 
 def rht_size_study(q, torch, dev, reps=3, rows=40):
-    """Size ablation of the wgrad RHT (Technische Zusammenfassung 2.B.2: the
-    pages report 16 x 16 as the best size): for transforms of 1 (none), 4,
-    16 and 64 tokens, the 12B-layer wgrad dW = dY^T X with both operands
-    quantised through the transform (dY SR, X RNE, one sign vector), its
-    relative Frobenius error on sampled output rows against the exact
-    product of the bf16 inputs, and the quantiser and GEMM times."""
+    """RHT ablations (Technische Zusammenfassung 2.B.2: 16 x 16 was the best
+    size, and the transform brought no significant benefit on fprop and
+    dgrad): for transforms of 1 (none), 4, 16 and 64 tokens, the 12B-layer
+    wgrad dW = dY^T X with both operands quantised through the transform (dY
+    SR, X RNE, one sign vector), its relative Frobenius error on sampled
+    output rows against the exact product of the bf16 inputs and the
+    quantiser times; then fprop and dgrad with and without the transform
+    along their contraction dimension."""
     import numpy as np
     from quantize_precision_gemm_amd import workloads as wl
 
@@ -196,9 +198,39 @@ def rht_size_study(q, torch, dev, reps=3, rows=40):
                               "quant_X_ms": round(t_x, 4)}
         out[name] = res
         del x, dy
-    return {"study": "wgrad RHT size (1 = no transform)", "workload": f"12B-layer wgrad: M={M}, "
-            f"N={N}, K={K}; error on {rows} sampled rows of dW against the exact dY^T X",
-            "results": out}
+    # RHT on fprop and dgrad: the 16-point transform along the contraction
+    # dimension of both operands (X, W along K; dY, W^T along N) against
+    # the recipe's untransformed operands, on the layer inputs
+    data = wl.layer_inputs(wl.LAYER_12B, seed=SEED)
+    to_dev = lambda u: torch.from_numpy(u.view(np.int16)).to(dev).view(torch.bfloat16)
+    x, w, dy = to_dev(data["X"]), to_dev(data["W"]), to_dev(data["dY"])
+    wt = w.t().contiguous()          # W^T (K x N): its rows run along N
+    pick = np.sort(np.random.default_rng(SEED + 5).choice(M, rows, replace=False))
+    pt = torch.from_numpy(pick).to(dev)
+    xf = wl.bf16_bits_to_f32(data["X"][pick]).astype(np.float64)
+    wf = wl.bf16_bits_to_f32(data["W"]).astype(np.float64)
+    dyf = wl.bf16_bits_to_f32(data["dY"][pick]).astype(np.float64)
+    exact_y, exact_dx = xf @ wf.T, dyf @ wf
+    mask = q.nvfp4_rht_sign_mask(SEED + 1000)
+    err = lambda got, ref: float(np.linalg.norm(got - ref) / np.linalg.norm(ref))
+    gx = q.nvfp4_quantize(x, q.BLOCK_1X16, q.RNE)
+    gw = q.nvfp4_quantize(w, q.BLOCK_16X16, q.RNE, with_transpose=True)
+    gdy = q.nvfp4_quantize(dy, q.BLOCK_1X16, q.SR, SEED + 100)
+    y0 = q.nvfp4_gemm(q.FPROP, gx, gw, out_dtype=torch.float32)[pt].double().cpu().numpy()
+    dx0 = q.nvfp4_gemm(q.DGRAD, gdy, gw, out_dtype=torch.float32)[pt].double().cpu().numpy()
+    hx = q.nvfp4_quantize_rht_rows(x, mask, q.BLOCK_1X16, q.RNE)
+    hw = q.nvfp4_quantize_rht_rows(w, mask, q.BLOCK_16X16, q.RNE)
+    hdy = q.nvfp4_quantize_rht_rows(dy, mask, q.BLOCK_1X16, q.SR, SEED + 100)
+    hwt = q.nvfp4_quantize_rht_rows(wt, mask, q.BLOCK_16X16, q.RNE)
+    y1 = q.nvfp4_gemm(q.FPROP, hx, hw, out_dtype=torch.float32)[pt].double().cpu().numpy()
+    dx1 = q.nvfp4_gemm(q.FPROP, hdy, hwt, out_dtype=torch.float32)[pt].double().cpu().numpy()
+    torch.cuda.synchronize()
+    fd = {"fprop": {"no transform (recipe)": err(y0, exact_y), "RHT along K": err(y1, exact_y)},
+          "dgrad": {"no transform (recipe)": err(dx0, exact_dx), "RHT along N": err(dx1, exact_dx)}}
+    return {"study": "wgrad RHT size (1 = no transform); RHT on fprop / dgrad",
+            "workload": f"12B layer: M={M}, N={N}, K={K}; relative Frobenius error on {rows} "
+                        f"sampled output rows against the exact product of the bf16 inputs",
+            "results": out, "fprop_dgrad_rht": fd}
 
 
 def cpu_baseline(data, tokens=M):

@@ -200,6 +200,23 @@ int nvfp4_quantize_dual(const void* x, int64_t tokens, int64_t channels, int64_t
                         nvfp4_tensor* out_rht, void* stream);
 
 /*
+ * nvfp4_quantize_rht_rows -- nvfp4_quantize after the 16-point random
+ * Hadamard transform of every aligned 16-element chunk of each row (along
+ * the contraction dimension of fprop and dgrad operands).  For the ablation
+ * of "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.B.2 (the transform brought no significant benefit on
+ * fprop and dgrad, so the recipe keeps it to wgrad).  With one sign mask for
+ * both operands of a GEMM the transforms cancel in the product.
+ *   Arguments, layout and errors as for nvfp4_quantize; sign_mask as for
+ *   nvfp4_rht_quantize; the amax (if not given) is taken over the
+ *   transformed values.  With 16x16 blocks an optional transposed copy is
+ *   the transpose of the transformed tensor's codes.
+ */
+int nvfp4_quantize_rht_rows(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block,
+                            uint32_t sign_mask, int32_t rounding, uint64_t seed,
+                            const float* amax_in, nvfp4_tensor* out, void* stream);
+
+/*
  * nvfp4_rht_quantize_sized -- nvfp4_rht_quantize with a transform of `size`
  * tokens: 1 (no transform: the plain transposing quantiser), 4, 16 or 64.
  * For the size ablation of "Pretraining Large Language Models with NVFP4",

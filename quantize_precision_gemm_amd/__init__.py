@@ -21,7 +21,7 @@ __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_gemm",
     "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_mx_quantize",
-    "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "lib_path", "load_library",
+    "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "lib_path", "load_library",
 ]
 
 BLOCK_1X16 = 0
@@ -82,6 +82,8 @@ def load_library():
         L.nvfp4_mx_quantize.restype = ctypes.c_int
         L.nvfp4_mx_gemm.argtypes = [D, D, P, i64, i32, P]
         L.nvfp4_mx_gemm.restype = ctypes.c_int
+        L.nvfp4_quantize_rht_rows.argtypes = [P, i64, i64, i64, i32, u32, i32, u64, P, D, P]
+        L.nvfp4_quantize_rht_rows.restype = ctypes.c_int
         L.nvfp4_rht_quantize_sized.argtypes = [P, i64, i64, i64, i32, u64, i32, u64, P, D, P]
         L.nvfp4_rht_quantize_sized.restype = ctypes.c_int
         L.nvfp4_rht_signs64.argtypes = [u64]
@@ -241,6 +243,23 @@ def nvfp4_quantize_dual(x, sign_mask, rounding=RNE, seed=0, seed_rht=0, amax_in=
     out.rows, out.cols, out.block = d.rows, d.cols, d.block
     out_rht.rows, out_rht.cols, out_rht.block = dr.rows, dr.cols, dr.block
     return out, out_rht
+
+
+def nvfp4_quantize_rht_rows(x, sign_mask, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None,
+                            with_transpose=False, out=None, stream=None):
+    """nvfp4_quantize after the 16-point RHT along the rows (see
+    nvfp4_quantize_rht_rows in nvfp4.h)."""
+    _check_bf16(x)
+    rows, cols = x.shape
+    if out is None:
+        out = alloc_nvfp4(rows, cols, block, with_transpose and block == BLOCK_16X16, x.device)
+    d = out.descriptor()
+    st = load_library().nvfp4_quantize_rht_rows(_ptr(x), rows, cols, x.stride(0), block, sign_mask,
+                                                rounding, seed, _ptr(amax_in), ctypes.byref(d),
+                                                _stream(stream))
+    _check(st, "nvfp4_quantize_rht_rows")
+    out.rows, out.cols, out.block = d.rows, d.cols, d.block
+    return out
 
 
 def nvfp4_rht_quantize_sized(x, size, signs, rounding=RNE, seed=0, amax_in=None, out=None,

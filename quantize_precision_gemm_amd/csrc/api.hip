@@ -195,6 +195,37 @@ int nvfp4_quantize_dual(const void* x, int64_t tokens, int64_t channels, int64_t
     return launch_status();
 }
 
+int nvfp4_quantize_rht_rows(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t block,
+                            uint32_t sign_mask, int32_t rounding, uint64_t seed,
+                            const float* amax_in, nvfp4_tensor* out, void* stream)
+{
+    if (block != NVFP4_BLOCK_1X16 && block != NVFP4_BLOCK_16X16) return NVFP4_ERR_MODE;
+    if (rounding != NVFP4_RNE && rounding != NVFP4_SR) return NVFP4_ERR_MODE;
+    if (rows < 0 || cols < 0 || cols % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (block == NVFP4_BLOCK_16X16 && rows % 16 != 0) return NVFP4_ERR_SHAPE;
+    if (!x && rows > 0 && cols > 0) return NVFP4_ERR_NULL;
+    if (ld_x < cols) return NVFP4_ERR_SHAPE;
+    if (!aligned(x, 16) || ld_x % 8 != 0) return NVFP4_ERR_ALIGN;
+    if (amax_in && !aligned(amax_in, 4)) return NVFP4_ERR_ALIGN;
+    int st = check_out(out, rows, cols, block);
+    if (st != NVFP4_OK) return st;
+
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const uint16_t* xb = static_cast<const uint16_t*>(x);
+    const uint32_t mask = sign_mask & 0xFFFFu;
+    const float* amax_src = amax_in;
+    if (!amax_src) {
+        nvfp4::launch_amax_rows_rht(xb, rows, cols, ld_x, mask, out->amax, s);
+        amax_src = out->amax;
+    }
+    nvfp4::launch_quant_rht_rows(xb, rows, cols, ld_x, block, mask, rounding, seed, amax_src,
+                                 qout_of(out), s);
+    out->rows = rows;
+    out->cols = cols;
+    out->block = block;
+    return launch_status();
+}
+
 int nvfp4_rht_quantize_sized(const void* x, int64_t tokens, int64_t channels, int64_t ld_x,
                              int32_t size, uint64_t signs, int32_t rounding, uint64_t seed,
                              const float* amax_in, nvfp4_tensor* out, void* stream)

@@ -52,6 +52,14 @@ void launch_dual_quant(const uint16_t* x, int64_t tokens, int64_t channels, int6
                        const float* amax_src, const float* amax_rht_src, const QOut& o,
                        const QOut& o_rht, hipStream_t s);
 
+// The 16-point RHT on every 16-element row chunk, then the quantisation of
+// launch_quant (fprop / dgrad ablation).
+void launch_amax_rows_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t mask,
+                          float* amax, hipStream_t s);
+void launch_quant_rht_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int block,
+                           uint32_t mask, int rounding, uint64_t seed, const float* amax_src,
+                           const QOut& o, hipStream_t s);
+
 // Sized RHT (size 1, 4, 16 or 64 tokens) + transpose + 1x16 quantisation.
 void launch_rhtd_amax(const uint16_t* x, int64_t tokens, int64_t channels, int64_t ld, int size,
                       uint64_t signs, float* amax, hipStream_t s);

@@ -174,12 +174,14 @@ __device__ __forceinline__ uint2 encode16_sr(const float (&v)[16], float f, uint
 // 1x16 quantiser: one thread per 16-element block.
 // ---------------------------------------------------------------------------
 
-template <bool kSR>
+// kRht: the 16-point RHT of the block first (the fprop / dgrad ablation;
+// the transform runs along the rows, i.e. within the block).
+template <bool kSR, bool kRht = false>
 __global__ __launch_bounds__(256) void k_quant_1x16(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
     int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
-    float* __restrict__ amax_out, float* __restrict__ s_enc_out)
+    float* __restrict__ amax_out, float* __restrict__ s_enc_out, uint32_t mask = 0u)
 {
     const int64_t nb = cols >> 4;
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -195,6 +197,7 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
     const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 16);
     float v[16];
     unpack16(src[0], src[1], v);
+    if constexpr (kRht) rht16(v, mask);
     const uint32_t sb = block_scale(absmax16(v), s_enc);
     const float f = block_factor(sb, s_enc);
     uint2 pk;
@@ -216,13 +219,15 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
 
 constexpr int kW2Rows = 128, kW2Cols = 128;
 
-template <bool kSR>
+// kRht: the 16-point RHT of every tile row first (fprop / dgrad ablation).
+template <bool kSR, bool kRht = false>
 __global__ __launch_bounds__(256) void k_quant_16x16(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
     int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
     uint8_t* __restrict__ codes_t, int64_t ld_codes_t, uint8_t* __restrict__ scales_t,
-    int64_t ld_scales_t, float* __restrict__ amax_out, float* __restrict__ s_enc_out)
+    int64_t ld_scales_t, float* __restrict__ amax_out, float* __restrict__ s_enc_out,
+    uint32_t mask = 0u)
 {
     __shared__ __attribute__((aligned(16))) uint8_t tcodes[kW2Cols][kW2Rows / 2 + 16];  // [col][row/2]
 
@@ -245,6 +250,7 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
         if (valid) {
             const uint4* src = reinterpret_cast<const uint4*>(x + (row0 + i) * ld + col0);
             unpack16(src[0], src[1], v[i]);
+            if constexpr (kRht) rht16(v[i], mask);
         } else {
 #pragma unroll
             for (int j = 0; j < 16; ++j) v[i][j] = 0.0f;
@@ -817,6 +823,32 @@ __global__ __launch_bounds__(256) void k_mx_quant_cols(
     }
 }
 
+// max |RHT(x)| with the transform on every aligned 16-element chunk of the
+// rows (fprop / dgrad ablation): one chunk per thread, grid-stride.
+__global__ __launch_bounds__(256) void k_amax_rows_rht(const uint16_t* __restrict__ x, int64_t rows,
+                                                       int64_t cols, int64_t ld, uint32_t mask,
+                                                       uint32_t* __restrict__ amax_bits)
+{
+    const int64_t nb = cols >> 4;
+    uint32_t m = 0u;
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; t < rows * nb; t += stride) {
+        const int64_t r = t / nb, b = t - r * nb;
+        const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 16);
+        float v[16];
+        unpack16(src[0], src[1], v);
+        rht16_unscaled(v, mask);
+        // rounding is monotonic: the max of the scaled values is the scaled max
+        m = max(m, __float_as_uint(absmax16(v) * 0.25f));
+    }
+    m = wave_max_u32(m);
+    __shared__ uint32_t red[4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (lane == 0) red[wave] = m;
+    __syncthreads();
+    if (threadIdx.x == 0) merge_amax(amax_bits, max(max(red[0], red[1]), max(red[2], red[3])));
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -995,6 +1027,44 @@ void launch_rhtd_quant(const uint16_t* x, int64_t tokens, int64_t channels, int6
         case 4: sr ? go(k_rhtd_quant<true, 4>) : go(k_rhtd_quant<false, 4>); break;
         case 16: sr ? go(k_rhtd_quant<true, 16>) : go(k_rhtd_quant<false, 16>); break;
         default: sr ? go(k_rhtd_quant<true, 64>) : go(k_rhtd_quant<false, 64>); break;
+    }
+}
+
+void launch_amax_rows_rht(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, uint32_t mask,
+                          float* amax, hipStream_t s)
+{
+    uint32_t* bits = reinterpret_cast<uint32_t*>(amax);
+    hipLaunchKernelGGL(k_zero_u32, dim3(1), dim3(1), 0, s, bits);
+    const int64_t work = rows * (cols >> 4);
+    if (work == 0) return;
+    hipLaunchKernelGGL(k_amax_rows_rht, dim3(grid_for(work, 256, 2048)), dim3(256), 0, s, x, rows, cols,
+                       ld, mask, bits);
+}
+
+void launch_quant_rht_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int block,
+                           uint32_t mask, int rounding, uint64_t seed, const float* amax_src,
+                           const QOut& o, hipStream_t s)
+{
+    const bool sr = rounding == 1;
+    if (rows == 0 || cols == 0) {
+        hipLaunchKernelGGL(k_publish, dim3(1), dim3(1), 0, s, amax_src, o.amax, o.s_enc);
+        return;
+    }
+    if (block == 0) {
+        dim3 g(grid_for(rows * (cols >> 4), 256, INT32_MAX));
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, g, dim3(256), 0, s, x, rows, cols, ld, amax_src, seed, o.codes,
+                               o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc, mask);
+        };
+        sr ? go(k_quant_1x16<true, true>) : go(k_quant_1x16<false, true>);
+    } else {
+        dim3 g((unsigned)((cols + kW2Cols - 1) / kW2Cols), (unsigned)((rows + kW2Rows - 1) / kW2Rows));
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, g, dim3(256), 0, s, x, rows, cols, ld, amax_src, seed, o.codes,
+                               o.ld_codes, o.scales, o.ld_scales, o.codes_t, o.ld_codes_t, o.scales_t,
+                               o.ld_scales_t, o.amax, o.s_enc, mask);
+        };
+        sr ? go(k_quant_16x16<true, true>) : go(k_quant_16x16<false, true>);
     }
 }
 

@@ -76,3 +76,44 @@ def test_sized_full_size(env, size):
     g = q.nvfp4_rht_quantize_sized(to_dev(x, dev), size, signs, q.RNE)
     torch.cuda.synchronize()
     assert_same_quant(g, oracle.rht_quantize_sized(x, size, signs, oracle.RNE), f"rht{size} full X")
+
+
+# --- RHT along the rows (fprop / dgrad operands) ------------------------------
+
+@pytest.mark.parametrize("block", [0, 1])
+@pytest.mark.parametrize("shape", [(16, 16), (48, 80), (160, 1040), (272, 2064)])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_row_rht_matches_oracle(env, block, shape, rounding):
+    torch, oracle, q, wl, dev = env
+    rng = np.random.default_rng(block * 7 + shape[0] + shape[1] + rounding)
+    x = wl.normal_with_outliers(rng, shape) if rounding == 0 else wl.lognormal_rows(rng, shape)
+    mask = int(rng.integers(0, 65536))
+    print(f"row rht block={block} {shape} r={rounding}", flush=True)
+    g = q.nvfp4_quantize_rht_rows(to_dev(x, dev), mask, block, rounding, 17)
+    torch.cuda.synchronize()
+    assert_same_quant(g, oracle.quantize_rht_rows(x, mask, block, rounding, 17), f"row rht {shape}")
+
+
+def test_row_rht_strided_amax_in_and_product(env):
+    torch, oracle, q, wl, dev = env
+    rng = np.random.default_rng(5)
+    full = wl.student_t_unit_var(rng, (64, 336), 4)
+    x = np.ascontiguousarray(full[:, :320])
+    xd = to_dev(full, dev)[:, :320]
+    print("row rht strided", flush=True)
+    g = q.nvfp4_quantize_rht_rows(xd, 0x3C5A, 0, 1, 6)
+    amax = torch.tensor([4.0], dtype=torch.float32, device=dev)
+    h = q.nvfp4_quantize_rht_rows(xd, 0x3C5A, 1, 0, 0, amax_in=amax)
+    torch.cuda.synchronize()
+    assert_same_quant(g, oracle.quantize_rht_rows(x, 0x3C5A, 0, 1, 6), "row rht strided")
+    assert_same_quant(h, oracle.quantize_rht_rows(x, 0x3C5A, 1, 0, 0, amax_in=4.0), "row rht amax_in")
+    # the fprop GEMM on row-transformed operands approximates the plain product
+    w = wl.normal(rng, (48, 320), 0.05)
+    gw = q.nvfp4_quantize_rht_rows(to_dev(w, dev), 0x3C5A, 1, 0)
+    gx = q.nvfp4_quantize_rht_rows(xd, 0x3C5A, 0, 0)
+    y = q.nvfp4_gemm(q.FPROP, gx, gw, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ref = oracle.gemm(oracle.FPROP, oracle.quantize_rht_rows(x, 0x3C5A, 0, 0),
+                      oracle.quantize_rht_rows(w, 0x3C5A, 1, 0))
+    from tests.gpu_util import rel_fro
+    assert rel_fro(y.cpu().numpy(), ref) <= 1e-5
