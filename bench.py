@@ -144,6 +144,63 @@ def mx_comparison(q, torch, layer, reps=5):
             "peak_tflops": PEAK_FP4_TFLOPS}
 
 
+def epilogue_amax_comparison(q, torch, layer, reps=5, rounds=5):
+    """Quantise-in-epilogue: the fprop output Y (the next layer's X) and the
+    dgrad output dX (the previous layer's dY) are quantised into both of
+    their operands by the dual quantiser.  Separate: GEMM, then the dual
+    quantiser with its own read for the two maxima.  Fused: the GEMM
+    epilogue emits the maxima (nvfp4_gemm_amax) and the dual quantiser takes
+    them.  Each op and each pair is timed serialised with events on the
+    layer's operands (reps launches per timing, the variants alternating,
+    median of `rounds`); both schedules must give identical operands."""
+    dev = layer.y.device
+    f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
+
+    def timed(f):
+        f()
+        s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s_.record()
+        for _ in range(reps):
+            f()
+        e_.record()
+        torch.cuda.synchronize()
+        return s_.elapsed_time(e_) / reps
+
+    out, same = {}, True
+    for name, P, a, out_t, rnd in (("fprop (Y, next X: RNE)", q.FPROP, layer.gx, layer.y, q.RNE),
+                                   ("dgrad (dX, previous dY: SR)", q.DGRAD, layer.gdy, layer.dx, q.SR)):
+        rows, cols = out_t.shape
+        ops = [q.alloc_nvfp4(rows, cols, q.BLOCK_1X16, device=dev) for _ in range(2)]
+        opsr = [q.alloc_nvfp4(cols, rows, q.BLOCK_1X16, device=dev) for _ in range(2)]
+        am, ar = f32(), f32()
+        gemm = lambda: q.nvfp4_gemm(P, a, layer.gw, out=out_t)
+        gemm_amax = lambda: q.nvfp4_gemm_amax(P, a, layer.gw, layer.mask, out=out_t, amax=am,
+                                              amax_rht=ar)
+        dual = lambda: q.nvfp4_quantize_dual(out_t, layer.mask, rnd, 11, 12, out=ops[0],
+                                             out_rht=opsr[0])
+        dual_in = lambda: q.nvfp4_quantize_dual(out_t, layer.mask, rnd, 11, 12, amax_in=am,
+                                                amax_rht_in=ar, out=ops[1], out_rht=opsr[1])
+        fns = {"gemm_ms": gemm, "gemm_amax_ms": gemm_amax, "dual_quant_own_amax_ms": dual,
+               "dual_quant_given_amax_ms": dual_in,
+               "separate_pair_ms": lambda: (gemm(), dual()),
+               "fused_pair_ms": lambda: (gemm_amax(), dual_in())}
+        runs = {k: [] for k in fns}
+        for _ in range(rounds):  # alternate the variants; median of the rounds
+            for k, f in fns.items():
+                runs[k].append(timed(f))
+        t = {k: sorted(v)[len(v) // 2] for k, v in runs.items()}
+        t["saving_ms"] = t["separate_pair_ms"] - t["fused_pair_ms"]
+        gemm(), dual(), gemm_amax(), dual_in()
+        torch.cuda.synchronize()
+        for u, v in ((ops[0], ops[1]), (opsr[0], opsr[1])):
+            same = same and torch.equal(u.codes, v.codes) and torch.equal(u.scales, v.scales) \
+                and u.s_enc.item() == v.s_enc.item()
+        out[name] = {k: round(v, 4) for k, v in t.items()}
+    out["identical_operands"] = bool(same)
+    out["kernel"] = "k_gemm_nv<bf16 out, epilogue maxima> + k_dual_quant (amax given)"
+    return out
+
+
 def rht_size_study(q, torch, dev, reps=3, rows=40):
     """RHT ablations (Technische Zusammenfassung 2.B.2: 16 x 16 was the best
     size, and the transform brought no significant benefit on fprop and
@@ -438,6 +495,7 @@ def main():
         datapaths = fp8
 
     mx = None if mlp else mx_comparison(q, torch, step.layers[0])
+    epi = None if mlp else epilogue_amax_comparison(q, torch, step.layers[0])
 
     ms_step = wall * 1e3 / steps
     layer0 = step.layers[0]
@@ -501,6 +559,8 @@ def main():
         mx["speedup_vs_nvfp4"] = {k: round(v / result["gemm_tflops"][k], 2)
                                   for k, v in mx["gemm_tflops"].items()}
         result["mxfp4_comparison"] = mx
+    if epi is not None:
+        result["quantize_in_epilogue"] = epi
     result["mxfp4_step"] = {
         "ms_per_step": round(mx_ms, 4),
         "tflops": round(step.flops() / (mx_ms * 1e-3) / 1e12, 2),

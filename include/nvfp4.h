@@ -309,6 +309,33 @@ int nvfp4_gemm_fp8blk(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b
                       int64_t ldc, int32_t c_dtype, void* stream);
 
 /*
+ * nvfp4_gemm_amax -- nvfp4_gemm for FPROP or DGRAD with bf16 output whose
+ * epilogue also reduces that output to the tensor maxima of its next
+ * quantisation: amax_out = max |c| (the amax of the two-level scale) and, if
+ * amax_rht_out is given, the amax of c's 16-point random Hadamard transform
+ * along its rows (tokens) in aligned 16-row chunks -- the wgrad operand's.
+ * Defines: "Pretraining Large Language Models with NVFP4", Technische
+ * Zusammenfassung 2.A (the FP32 tensor-level scale comes from the tensor's
+ * amax) and 2.B.2 (a layer output becomes the next layer's fprop operand
+ * and, after the transform, its wgrad operand).  The codes still need the
+ * tensor scale before any block can be encoded, so they come from a second
+ * pass: nvfp4_quantize_dual(c, ..., amax_in = amax_out, amax_rht_in =
+ * amax_rht_out) then skips its own read for the maxima; both maxima equal
+ * nvfp4_amax(c) exactly.
+ *   pass, a, b, c, ldc   as for nvfp4_gemm (c is bf16); NVFP4_ERR_MODE for
+ *                        WGRAD (its fp32 output is not quantised again).
+ *   sign_mask            the transform's signs, as for nvfp4_rht_quantize.
+ *   amax_out             device float, required; overwritten.
+ *   amax_rht_out         device float or null; overwritten.  With it, the
+ *                        output rows must be a multiple of 16
+ *                        (NVFP4_ERR_SHAPE).
+ * Returns NVFP4_OK or a negative status; nothing is enqueued on failure.
+ */
+int nvfp4_gemm_amax(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                    int64_t ldc, uint32_t sign_mask, float* amax_out, float* amax_rht_out,
+                    void* stream);
+
+/*
  * nvfp4_bf16_gemm -- the three GEMMs of a linear layer that stays in BF16
  * (no quantisation); bf16 products accumulated in fp32.
  * Defines: "Pretraining Large Language Models with NVFP4", Technische

@@ -21,7 +21,7 @@ __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_gemm",
     "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_mx_quantize",
-    "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "lib_path", "load_library",
+    "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "nvfp4_gemm_amax", "lib_path", "load_library",
 ]
 
 BLOCK_1X16 = 0
@@ -91,6 +91,8 @@ def load_library():
         L.nvfp4_gemm.argtypes = [i32, D, D, P, i64, i32, P]
         L.nvfp4_gemm.restype = ctypes.c_int
         L.nvfp4_gemm_fp8blk.argtypes = [i32, D, D, P, i64, i32, P]
+        L.nvfp4_gemm_amax.argtypes = [i32, D, D, P, i64, u32, P, P, P]
+        L.nvfp4_gemm_amax.restype = ctypes.c_int
         L.nvfp4_gemm_fp8blk.restype = ctypes.c_int
         L.nvfp4_amax.argtypes = [P, i64, i64, i64, u32, P, P, P]
         L.nvfp4_amax.restype = ctypes.c_int
@@ -333,6 +335,35 @@ def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None, fp8
             _stream(stream))
     _check(st, "nvfp4_gemm_fp8blk" if fp8_blocks else "nvfp4_gemm")
     return out
+
+
+def nvfp4_gemm_amax(pass_, a, b, sign_mask=0, rht=True, out=None, amax=None, amax_rht=None,
+                    stream=None):
+    """FPROP / DGRAD GEMM with bf16 output whose epilogue also writes the
+    output's tensor amax and, with rht=True, the amax of its 16-point RHT
+    along the rows (see nvfp4_gemm_amax in nvfp4.h).
+
+    Returns (c, amax, amax_rht or None); the maxima are one-element float32
+    device tensors, ready as amax_in / amax_rht_in of nvfp4_quantize_dual."""
+    M = a.rows
+    N = b.cols if pass_ == DGRAD else b.rows
+    dev = a.codes.device
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+    if out.dtype != torch.bfloat16 or out.stride(1) != 1:
+        raise TypeError("output must be bfloat16 with a contiguous last dimension")
+    if amax is None:
+        amax = torch.empty(1, dtype=torch.float32, device=dev)
+    if rht and amax_rht is None:
+        amax_rht = torch.empty(1, dtype=torch.float32, device=dev)
+    if not rht:
+        amax_rht = None
+    da, db = a.descriptor(), b.descriptor()
+    st = load_library().nvfp4_gemm_amax(pass_, ctypes.byref(da), ctypes.byref(db), _ptr(out),
+                                        out.stride(0), sign_mask, _ptr(amax), _ptr(amax_rht),
+                                        _stream(stream))
+    _check(st, "nvfp4_gemm_amax")
+    return out, amax, amax_rht
 
 
 def nvfp4_bf16_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None):

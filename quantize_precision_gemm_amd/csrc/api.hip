@@ -312,22 +312,21 @@ uint64_t nvfp4_rht_signs64(uint64_t seed)
 namespace {
 
 // Validation and operand set-up shared by the two NVFP4 GEMM datapaths.
-int gemm_nvfp4(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t ldc,
-               int32_t c_dtype, void* stream, bool fp8_blocks)
+// Validates the operands of one NVFP4 GEMM pass and resolves them to the
+// kernel's A (M x K) and B (N x K) operands.
+int resolve_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, GemmOperand& A,
+                 GemmOperand& B, int64_t& M, int64_t& N, int64_t& K)
 {
     if (pass != NVFP4_FPROP && pass != NVFP4_DGRAD && pass != NVFP4_WGRAD) return NVFP4_ERR_MODE;
-    if (c_dtype != NVFP4_OUT_BF16 && c_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_MODE;
     int st = check_operand(a);
     if (st != NVFP4_OK) return st;
     st = check_operand(b);
     if (st != NVFP4_OK) return st;
-    if (!c && a->rows > 0 && (pass == NVFP4_DGRAD ? b->cols : b->rows) > 0) return NVFP4_ERR_NULL;
-    if (!aligned(c, c_dtype == NVFP4_OUT_FP32 ? 16 : 8) || ldc % 4 != 0) return NVFP4_ERR_ALIGN;
     if (a->block != NVFP4_BLOCK_1X16) return NVFP4_ERR_MISMATCH;
 
-    GemmOperand A{a->codes, a->ld_codes, a->scales, a->ld_scales, 0, a->s_enc};
-    GemmOperand B;
-    int64_t M = a->rows, N, K = a->cols;
+    A = GemmOperand{a->codes, a->ld_codes, a->scales, a->ld_scales, 0, a->s_enc};
+    M = a->rows;
+    K = a->cols;
     if (pass == NVFP4_DGRAD) {
         // c = dY (M x N) * W (N x K): W^T (K x N) is the 16x16-block operand
         if (b->block != NVFP4_BLOCK_16X16) return NVFP4_ERR_MISMATCH;
@@ -346,6 +345,19 @@ int gemm_nvfp4(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void*
                         b->block == NVFP4_BLOCK_16X16 ? 4 : 0, b->s_enc};
         N = b->rows;
     }
+    return NVFP4_OK;
+}
+
+int gemm_nvfp4(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t ldc,
+               int32_t c_dtype, void* stream, bool fp8_blocks)
+{
+    if (c_dtype != NVFP4_OUT_BF16 && c_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_MODE;
+    GemmOperand A, B;
+    int64_t M, N, K;
+    const int st = resolve_gemm(pass, a, b, A, B, M, N, K);
+    if (st != NVFP4_OK) return st;
+    if (!c && M > 0 && N > 0) return NVFP4_ERR_NULL;
+    if (!aligned(c, c_dtype == NVFP4_OUT_FP32 ? 16 : 8) || ldc % 4 != 0) return NVFP4_ERR_ALIGN;
     if (ldc < N) return NVFP4_ERR_SHAPE;
     const bool f32 = c_dtype == NVFP4_OUT_FP32;
     hipStream_t s = static_cast<hipStream_t>(stream);
@@ -370,6 +382,25 @@ int nvfp4_gemm_fp8blk(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b
                       int64_t ldc, int32_t c_dtype, void* stream)
 {
     return gemm_nvfp4(pass, a, b, c, ldc, c_dtype, stream, true);
+}
+
+int nvfp4_gemm_amax(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                    int64_t ldc, uint32_t sign_mask, float* amax_out, float* amax_rht_out,
+                    void* stream)
+{
+    if (pass != NVFP4_FPROP && pass != NVFP4_DGRAD) return NVFP4_ERR_MODE;
+    GemmOperand A, B;
+    int64_t M, N, K;
+    const int st = resolve_gemm(pass, a, b, A, B, M, N, K);
+    if (st != NVFP4_OK) return st;
+    if (!amax_out || (!c && M > 0 && N > 0)) return NVFP4_ERR_NULL;
+    if (!aligned(c, 8) || ldc % 4 != 0 || !aligned(amax_out, 4) || !aligned(amax_rht_out, 4))
+        return NVFP4_ERR_ALIGN;
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    if (amax_rht_out && M % 16 != 0) return NVFP4_ERR_SHAPE;  // whole 16-token chunks
+    nvfp4::launch_gemm_nt_amax(A, B, M, N, K, static_cast<uint16_t*>(c), ldc, amax_out,
+                               amax_rht_out, sign_mask & 0xFFFFu, static_cast<hipStream_t>(stream));
+    return launch_status();
 }
 
 int nvfp4_mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, int32_t mode,

@@ -99,22 +99,118 @@ __device__ __forceinline__ void tile_of(int64_t M, int64_t N, int64_t& tile_m, i
 // area `stage_out` (32 x kEpiStride floats; fp32, alpha applied; every wave
 // must be done with the operand stages) and writes them back as 16-byte row
 // segments.
-template <bool kOutF32>
+//
+// kAmax (bf16 output only) also folds the output into the tensor maxima its
+// next quantisation needs: 1 = max |y| over the bf16 values (into
+// amax_bits[0]); 2 = that and the max over the 16-point RHT, along the rows
+// (tokens), of every aligned 16-row chunk of a column (into amax_rht_bits[0];
+// M a multiple of 16).  The values are rounded to bf16 before they are
+// staged, so both maxima see exactly the stored tensor; they go out as uint
+// bits of non-negative floats through one atomic max per wave.
+//
+// The transform runs on the accumulator registers.  In the 32 x 32 MFMA
+// result a lane holds column lr of row 8 (e / 4) + 4 g + e % 4, so a 16-row
+// chunk of a column is split between lanes lr and lr + 32 (row bit 2 = g),
+// 8 values each: row bits 0, 1 are bits 0, 1 of e and row bit 3 is bit 2.
+// Strides 1 and 2 run in each lane; then v_permlane32_swap trades the
+// column-tn = 0 values of lanes 32-63 for the column-tn = 1 values of lanes
+// 0-31, so every lane holds one whole chunk (lane l: column l of the 64) and runs
+// strides 4 and 8 -- the butterfly order of the transform, so the fp32
+// values are the ones a separate pass computes.
+template <bool kOutF32, int kAmax = 0>
 __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float alpha,
                                            float* stage_out, int64_t m0, int64_t n0, int64_t M,
-                                           int64_t N, void* __restrict__ c, int64_t ldc)
+                                           int64_t N, void* __restrict__ c, int64_t ldc,
+                                           uint32_t* amax_bits = nullptr,
+                                           uint32_t* amax_rht_bits = nullptr, uint32_t mask = 0u)
 {
+    static_assert(kAmax == 0 || !kOutF32, "output maxima are taken of bf16 outputs");
     const int lane = threadIdx.x & 63;
     const int g = lane >> 5, lr = lane & 31;
+    uint32_t am = 0u;  // max |y| as float bits (magnitudes compare as integers)
+    float rm = 0.0f;   // max |unscaled transform|
+    const bool inside = m0 + 128 <= M && n0 + 64 <= N;  // the wave's whole slab is stored
+    uint32_t sgn[8];  // sign bit of row 8 (k / 4) + 4 g + k % 4 of a chunk
+    if constexpr (kAmax == 2) {
+        const uint32_t mg = g ? (mask >> 4) : mask;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sgn[k] = ((mg >> ((k >> 2) * 8 + (k & 3))) & 1u) << 31;
+    }
 #pragma unroll
     for (int tm = 0; tm < 4; ++tm) {
+        float y[2][16];
 #pragma unroll
         for (int tn = 0; tn < 2; ++tn)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
                 const int r = (e >> 2) * 8 + g * 4 + (e & 3);
-                stage_out[r * kEpiStride + 32 * tn + lr] = acc[tm][tn][e] * alpha;
+                float v = acc[tm][tn][e] * alpha;
+                if constexpr (kAmax > 0) v = __uint_as_float((uint32_t)f32_to_bf16_rne(v) << 16);
+                y[tn][e] = v;
+                stage_out[r * kEpiStride + 32 * tn + lr] = v;
             }
+        if constexpr (kAmax > 0) {
+            if (inside) {
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e)
+                        am = max(am, __float_as_uint(y[tn][e]) & 0x7FFFFFFFu);
+            } else {
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) {
+                        const int64_t row = m0 + 32 * tm + (e >> 2) * 8 + g * 4 + (e & 3);
+                        if (row < M && n0 + 32 * tn + lr < N)
+                            am = max(am, __float_as_uint(y[tn][e]) & 0x7FFFFFFFu);
+                    }
+            }
+        }
+        if constexpr (kAmax == 2) {
+#pragma unroll
+            for (int ch = 0; ch < 2; ++ch) {
+                float h[2][8];
+#pragma unroll
+                for (int tn = 0; tn < 2; ++tn) {
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        h[tn][k] = __uint_as_float(__float_as_uint(y[tn][8 * ch + k]) ^ sgn[k]);
+#pragma unroll
+                    for (int st = 1; st <= 2; st <<= 1)
+#pragma unroll
+                        for (int k = 0; k < 8; ++k)
+                            if ((k & st) == 0) {
+                                const float a = h[tn][k], b = h[tn][k + st];
+                                h[tn][k] = a + b;
+                                h[tn][k + st] = a - b;
+                            }
+                }
+                float lo[8], hi[8];  // the chunk's rows with bit 2 clear / set
+#pragma unroll
+                for (int k = 0; k < 8; ++k) {
+                    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(h[0][k]),
+                                                                    __float_as_uint(h[1][k]),
+                                                                    false, false);
+                    const float a = __uint_as_float(r[0]), b = __uint_as_float(r[1]);
+                    lo[k] = a + b;  // stride 4
+                    hi[k] = a - b;
+                }
+#pragma unroll
+                for (int k = 0; k < 4; ++k) {  // stride 8
+                    const float a = lo[k], b = lo[k + 4], c2 = hi[k], d = hi[k + 4];
+                    lo[k] = a + b;
+                    lo[k + 4] = a - b;
+                    hi[k] = c2 + d;
+                    hi[k + 4] = c2 - d;
+                }
+                if (n0 + lane < N && m0 + 32 * tm + 16 * ch < M)
+#pragma unroll
+                    for (int k = 0; k < 8; ++k)
+                        rm = __builtin_fmaxf(rm, __builtin_fmaxf(__builtin_fabsf(lo[k]),
+                                                                 __builtin_fabsf(hi[k])));
+            }
+        }
         __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0): this wave's LDS writes are done
         __builtin_amdgcn_wave_barrier();
         // 32 rows x 64 columns = 32 x 16 float4; lane handles float4 (row, q)
@@ -136,8 +232,18 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float a
                     }
                 } else {
                     uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
-                    const uint16_t b0 = f32_to_bf16_rne(v.x), b1 = f32_to_bf16_rne(v.y);
-                    const uint16_t b2 = f32_to_bf16_rne(v.z), b3 = f32_to_bf16_rne(v.w);
+                    uint16_t b0, b1, b2, b3;
+                    if constexpr (kAmax > 0) {  // staged values are bf16 already
+                        b0 = (uint16_t)(__float_as_uint(v.x) >> 16);
+                        b1 = (uint16_t)(__float_as_uint(v.y) >> 16);
+                        b2 = (uint16_t)(__float_as_uint(v.z) >> 16);
+                        b3 = (uint16_t)(__float_as_uint(v.w) >> 16);
+                    } else {
+                        b0 = f32_to_bf16_rne(v.x);
+                        b1 = f32_to_bf16_rne(v.y);
+                        b2 = f32_to_bf16_rne(v.z);
+                        b3 = f32_to_bf16_rne(v.w);
+                    }
                     if (col + 4 <= N) {
                         *reinterpret_cast<uint2*>(dst) =
                             make_uint2(b0 | ((uint32_t)b1 << 16), b2 | ((uint32_t)b3 << 16));
@@ -150,6 +256,15 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float a
             }
         }
         __builtin_amdgcn_wave_barrier();
+    }
+    if constexpr (kAmax > 0) {
+        const uint32_t ab = wave_max_u32(am);
+        if (lane == 0) atomicMax(amax_bits, ab);
+        if constexpr (kAmax == 2) {
+            // rounding is monotonic: the max of the scaled values is the scaled max
+            const uint32_t rb = wave_max_u32(__float_as_uint(rm * 0.25f));
+            if (lane == 0) atomicMax(amax_rht_bits, rb);
+        }
     }
 }
 
@@ -204,9 +319,12 @@ struct NvRow {     // one thread's share of a K step
 
 }  // namespace
 
-template <bool kOutF32>
+template <bool kOutF32, int kAmax = 0>
 __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t M, int64_t N,
-                                                    int64_t K, void* __restrict__ c, int64_t ldc)
+                                                    int64_t K, void* __restrict__ c, int64_t ldc,
+                                                    uint32_t* amax_bits = nullptr,
+                                                    uint32_t* amax_rht_bits = nullptr,
+                                                    uint32_t mask = 0u)
 {
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
 
@@ -353,9 +471,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
 
     const float alpha = (1.0f / *A.s_enc) * (1.0f / *B.s_enc);
     __syncthreads();  // every wave is done reading the operand stages
-    store_tile<kOutF32>(acc, alpha, reinterpret_cast<float*>(lds) + wave * 32 * kEpiStride,
-                        tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c,
-                        ldc);
+    store_tile<kOutF32, kAmax>(acc, alpha, reinterpret_cast<float*>(lds) + wave * 32 * kEpiStride,
+                               tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c, ldc,
+                               amax_bits, amax_rht_bits, mask);
 }
 
 namespace {
@@ -846,6 +964,33 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
         hipLaunchKernelGGL(k_gemm_nv<true>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
     else
         hipLaunchKernelGGL(k_gemm_nv<false>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
+}
+
+// Zeroes the output maxima (a kernel, not a memset, so the sequence can be
+// captured in a graph).
+__global__ void k_zero_amax(uint32_t* a, uint32_t* b)
+{
+    *a = 0u;
+    if (b) *b = 0u;
+}
+
+void launch_gemm_nt_amax(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
+                         int64_t K, uint16_t* c, int64_t ldc, float* amax, float* amax_rht,
+                         uint32_t mask, hipStream_t s)
+{
+    uint32_t* ab = reinterpret_cast<uint32_t*>(amax);
+    uint32_t* rb = reinterpret_cast<uint32_t*>(amax_rht);
+    hipLaunchKernelGGL(k_zero_amax, dim3(1), dim3(1), 0, s, ab, rb);
+    if (M == 0 || N == 0) return;
+    if (K == 0) return launch_fill_zero(M, N, c, ldc, false, s);  // maxima stay 0
+    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc, 0};
+    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc, 0};
+    if (rb)
+        hipLaunchKernelGGL((k_gemm_nv<false, 2>), tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K,
+                           static_cast<void*>(c), ldc, ab, rb, mask);
+    else
+        hipLaunchKernelGGL((k_gemm_nv<false, 1>), tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K,
+                           static_cast<void*>(c), ldc, ab, rb, mask);
 }
 
 void launch_gemm_mx(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N, int64_t K,

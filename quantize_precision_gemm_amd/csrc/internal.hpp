@@ -77,6 +77,13 @@ void launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, 
 void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
                     int64_t K, void* c, int64_t ldc, bool out_fp32, hipStream_t s);
 
+// launch_gemm_nt with bf16 output whose epilogue also writes the output's
+// tensor amax (max |c|) and, if amax_rht is not null, the amax of its
+// 16-point RHT along the rows (M a multiple of 16); both are zeroed first.
+void launch_gemm_nt_amax(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
+                         int64_t K, uint16_t* c, int64_t ldc, float* amax, float* amax_rht,
+                         uint32_t mask, hipStream_t s);
+
 // The same product by the other datapath: FP8 MFMA per 16-element block,
 // block scales applied to the fp32 partials (K > 0).
 void launch_gemm_fp8blk(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,

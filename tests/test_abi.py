@@ -210,6 +210,30 @@ def test_gemm_validation(lib, fn):
     assert gemm(0, ctypes.byref(a), ctypes.byref(op(40, 64, 1)), FAKE, 64, 0, None) == -2
 
 
+def test_gemm_amax_validation(lib):
+    def op(rows, cols, block=0, **kw):
+        base = dict(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, rows=rows, cols=cols,
+                    ld_codes=max(16, ((cols + 31) // 32) * 16), ld_scales=max(4, cols // 16),
+                    block=block)
+        base.update(kw)
+        return _desc(**base)
+
+    g = lib.nvfp4_gemm_amax
+    a, w, a40 = op(32, 64), op(48, 64, 1), op(40, 64)
+    ra, rw = ctypes.byref(a), ctypes.byref(w)
+    assert g(2, ra, ctypes.byref(op(48, 64)), FAKE, 64, 1, FAKE, FAKE, None) == -4  # wgrad
+    assert g(7, ra, rw, FAKE, 64, 1, FAKE, FAKE, None) == -4
+    assert g(0, ra, rw, FAKE, 64, 1, None, FAKE, None) == -1          # amax_out required
+    assert g(0, ra, rw, None, 64, 1, FAKE, FAKE, None) == -1
+    assert g(0, ra, rw, FAKE + 2, 64, 1, FAKE, FAKE, None) == -3
+    assert g(0, ra, rw, FAKE, 64, 1, FAKE + 2, FAKE, None) == -3
+    assert g(0, ra, rw, FAKE, 64, 1, FAKE, FAKE + 1, None) == -3
+    assert g(0, ra, rw, FAKE, 16, 1, FAKE, FAKE, None) == -2          # ldc < N
+    assert g(0, ctypes.byref(a40), rw, FAKE, 64, 1, FAKE, FAKE, None) == -2  # 40 rows with RHT
+    assert g(0, rw, ra, FAKE, 64, 1, FAKE, FAKE, None) == -5
+    assert g(1, ctypes.byref(op(32, 48)), rw, FAKE, 64, 1, FAKE, FAKE, None) == -1  # no W^T
+
+
 def test_amax_validation(lib):
     out = FAKE
     assert lib.nvfp4_amax(FAKE, 16, 12, 16, 1, out, out, None) == -2      # cols % 8
