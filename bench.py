@@ -18,7 +18,7 @@ X Student-t(4) at unit variance, W ~ N(0, 0.02), dY with log-normal row
 magnitudes.  They are resident in HBM before timing starts.
 
 value = 3 * 2*M*N*K / (wall time of one step), in TFLOP/s, quantisation
-included; dgrad and wgrad start together on two streams.  Per-operation
+included; dgrad and wgrad run concurrently on two streams.  Per-operation
 times come from separate serialised passes with HIP events on the stream
 the library launches on.  The roofline entry is for the dominant kernel, the
 bf16-output GEMM (fprop and dgrad launches).  The CPU baseline is the

@@ -59,7 +59,8 @@ class NVFP4Linear:
     # wgrad): one fused pass computes both tensor maxima of each.  With
     # fused_quant one encode pass also emits both operands of each tensor
     # (nvfp4_quantize_dual), so X and dY are read twice per step instead of
-    # three times.
+    # three times; the RHT encodes then run before fprop and dgrad instead of
+    # beside them on the second stream.
     def weight_ops(self):
         q = self.q
         return [("quant_W", lambda: q.nvfp4_quantize(self.w, q.BLOCK_16X16, q.RNE, out=self.gw))]
@@ -78,15 +79,6 @@ class NVFP4Linear:
             quant,
             ("fprop", lambda: q.nvfp4_gemm(q.FPROP, self.gx, self.gw, out=self.y)),
         ]
-
-    def forward_side_ops(self):
-        """Work on X that only wgrad needs: runs beside the fprop once X's
-        maxima exist (the dual quantiser already made it)."""
-        q = self.q
-        if self.fused_quant:
-            return []
-        return [("rht_X", lambda: q.nvfp4_rht_quantize(self.x, self.mask, q.RNE,
-                                                       amax_in=self.ax_rht, out=self.gxt))]
 
     def backward_shared_ops(self):
         """The backward work both branches (dgrad, wgrad) wait for."""
@@ -119,6 +111,8 @@ class NVFP4Linear:
             ("rht_dY", lambda: q.nvfp4_rht_quantize(self.dy, self.mask, q.SR,
                                                     self.seed + SR_SEED_DY_RHT,
                                                     amax_in=self.ady_rht, out=self.gdyt)),
+            ("rht_X", lambda: q.nvfp4_rht_quantize(self.x, self.mask, q.RNE,
+                                                   amax_in=self.ax_rht, out=self.gxt)),
             wgrad,
         ]
 
@@ -162,11 +156,6 @@ class MXFP4Linear:
         return [("mx_quant_X", lambda: q.nvfp4_mx_quantize(self.x, q.MX_ROWS, out=self.gx)),
                 ("mx_fprop", lambda: q.nvfp4_mx_gemm(self.gx, self.gw, out=self.y))]
 
-    def forward_side_ops(self):
-        q = self.q
-        return [("mx_rht_X", lambda: q.nvfp4_mx_quantize(self.x, q.MX_COLS_RHT, self.mask, q.RNE,
-                                                         out=self.gxt))]
-
     def backward_shared_ops(self):
         return []
 
@@ -184,6 +173,8 @@ class MXFP4Linear:
         return [
             ("mx_rht_dY", lambda: q.nvfp4_mx_quantize(self.dy, q.MX_COLS_RHT, self.mask, q.SR,
                                                       self.seed + SR_SEED_DY_RHT, out=self.gdyt)),
+            ("mx_rht_X", lambda: q.nvfp4_mx_quantize(self.x, q.MX_COLS_RHT, self.mask, q.RNE,
+                                                     out=self.gxt)),
             ("mx_wgrad", lambda: q.nvfp4_mx_gemm(self.gdyt, self.gxt, out=self.dw)),
         ]
 
@@ -208,9 +199,6 @@ class BF16Linear:
         return 3 * 2.0 * self.M * self.N * self.K
 
     def weight_ops(self):
-        return []
-
-    def forward_side_ops(self):
         return []
 
     def forward_ops(self):
@@ -238,17 +226,15 @@ class TrainingStep:
     The weights do not depend on anything else in the step: their
     quantisation runs on a second stream from the start, beside the
     activations' amax and quantisation on the main stream, and each layer's
-    fprop waits for its own weight.  The wgrad operand of X needs only X and
-    its maxima, so it is made on the second stream beside the fprop.  Per
-    layer in the backward pass, the main stream first makes every operand
-    both backward GEMMs need (the maxima of dY, its dgrad and wgrad
-    operands); then dgrad runs on the main stream and wgrad on the second
-    one, started together so that each fills the other's last, partial wave
-    of workgroups (a quantiser launched beside a running GEMM gets few
-    compute units and would hold back the GEMM that waits for it).  Wgrad
-    feeds nothing later in the step, so it also overlaps the next layer's
-    backward work.  The step ends with the main stream waiting for the
-    second one.
+    fprop waits for its own weight.  Per layer in the backward pass, the
+    work both branches wait for runs on the main stream (the amax pass over
+    dY, plus the dual encode when the layer fuses its quantisers); then the
+    main stream quantises dY (SR, unless already done) and runs dgrad while
+    the wgrad branch (RHT operands, which need only the maxima, unless
+    already encoded, and the wgrad GEMM) runs on the second stream.  Wgrad feeds nothing later in the step, so it overlaps with dgrad
+    and with the next layer's backward work: each GEMM's last, partial wave
+    of workgroups is filled by the other's.  The step ends with the main
+    stream waiting for the second one.
     """
 
     def __init__(self, torch, layers, device):
@@ -289,23 +275,17 @@ class TrainingStep:
             ops = layer.forward_ops()
             for n, f in ops[:-1]:
                 call(n, f)
-            side_ops = layer.forward_side_ops()
-            if side_ops:
-                self.side.wait_stream(main)
-                with torch.cuda.stream(self.side):
-                    for n, f in side_ops:
-                        call(n, f)
             main.wait_event(ev)
             call(*ops[-1])  # the layer's fprop
         for layer in reversed(self.layers):
-            wg = layer.wgrad_ops()
-            for n, f in (layer.backward_shared_ops() + layer.backward_quant_ops() + wg[:-1]):
+            for n, f in layer.backward_shared_ops():
                 call(n, f)
             self.side.wait_stream(main)
-            for n, f in layer.dgrad_ops():
+            for n, f in layer.backward_quant_ops() + layer.dgrad_ops():
                 call(n, f)
             with torch.cuda.stream(self.side):
-                call(*wg[-1])  # the layer's wgrad GEMM
+                for n, f in layer.wgrad_ops():
+                    call(n, f)
         main.wait_stream(self.side)
 
     def serial_ops(self):
@@ -313,13 +293,11 @@ class TrainingStep:
         ops = []
         for i, layer in enumerate(self.layers):
             fw = layer.forward_ops()
-            ops += [(i, n, f) for n, f in fw[:-1] + layer.forward_side_ops() + layer.weight_ops()
-                    + fw[-1:]]
+            ops += [(i, n, f) for n, f in fw[:-1] + layer.weight_ops() + fw[-1:]]
         for i in reversed(range(len(self.layers))):
             layer = self.layers[i]
-            wg = layer.wgrad_ops()
-            for part in (layer.backward_shared_ops(), layer.backward_quant_ops(), wg[:-1],
-                         layer.dgrad_ops(), wg[-1:]):
+            for part in (layer.backward_shared_ops(), layer.backward_quant_ops(), layer.dgrad_ops(),
+                         layer.wgrad_ops()):
                 ops += [(i, n, f) for n, f in part]
         return ops
 
