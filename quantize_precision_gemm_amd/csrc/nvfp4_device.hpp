@@ -23,6 +23,7 @@ typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef float float16_t __attribute__((ext_vector_type(16)));
 typedef float float4_t __attribute__((ext_vector_type(4)));
+typedef float float2_t __attribute__((vector_size(8)));
 
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
@@ -85,27 +86,50 @@ __device__ __forceinline__ uint32_t e2m1_rne_pk(uint32_t old, float y0, float y1
     return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y0, y1, 1.0f, sel);
 }
 
-// Stochastic rounding of one fp32 value onto the E2M1 grid with a 16-bit
-// draw u16: with lo the grid point at or below |y| and g the gap above it,
-// round up iff u16 < P = trunc((|y| - lo) / g * 2^16); |y| >= 6 gives 6.
-// Evaluated without branches on the fp32 bit pattern b of |y|:
-//   1 <= |y| < 6 : the grid keeps one mantissa bit, so lo's code is
-//                  (b >> 22) - 252 and (|y| - lo) / g is mantissa bits
-//                  [21:0] / 2^22, i.e. P = bits [21:6];
-//   |y| < 1      : Q = trunc(|y| * 2^17) (exact) has lo's code in bit 16
-//                  (0 or 0.5) and P in bits [15:0].
-__device__ __forceinline__ uint32_t e2m1_sr(float y, uint32_t u16)
+// Stochastic rounding onto the E2M1 grid with a 16-bit draw u16 per value:
+// with lo the grid point at or below |y| and g the gap above it, round up
+// iff u16 < P = trunc((|y| - lo) / g * 2^16); |y| >= 6 gives 6; the sign is
+// kept (also of zero).
+//
+// gfx950's v_cvt_scalef32_sr_pk_fp4_f32 (unit scale) rounds the first value
+// of its pair up iff bits [31:16] of its random operand plus the top 16 bits
+// of the fraction it discards carry out of 16 bits; with the operand's low
+// 16 bits zero nothing carries in from below.  The operand
+// (0xFFFF - u16) << 16 therefore gives exactly the rule above:
+// u16 < P  <=>  (0xFFFF - u16) + P >= 2^16.  The pair's second value reads
+// bits [30:15], which overlap, so every value gets an instruction of its
+// own (the same value in both slots).  Each conversion writes byte 0 of its
+// own result, code in the low nibble; the other bytes are not relied on
+// (the compiler does not carry the destination's old bytes through the
+// byte-select forms of this instruction).
+__device__ __forceinline__ uint32_t e2m1_sr_conv(float y, uint32_t rnd)
 {
-    const uint32_t yb = __float_as_uint(y);
-    const uint32_t ab = yb & 0x7FFFFFFFu;
-    // only read when |y| < 1; the clamp keeps the conversion in range
-    const uint32_t q = (uint32_t)(__uint_as_float(min(ab, 0x3F7FFFFFu)) * 131072.0f);
-    const bool small = ab < 0x3F800000u;  // |y| < 1
-    const uint32_t cl = small ? (q >> 16) : ((ab >> 22) - 252u);
-    const uint32_t P = small ? (q & 0xFFFFu) : ((ab >> 6) & 0xFFFFu);
-    uint32_t code = cl + (u16 < P ? 1u : 0u);
-    code = (ab >= 0x40C00000u) ? 7u : code;  // |y| >= 6 (also Inf)
-    return code | ((yb >> 28) & 8u);
+    const float2_t v = {y, y};
+    return __builtin_amdgcn_cvt_scalef32_sr_pk_fp4_f32(0u, v, rnd, 1.0f, 0);
+}
+
+// Byte 0 of a, b, c, d -> bytes 0, 1, 2, 3.
+__device__ __forceinline__ uint32_t gather_byte0(uint32_t a, uint32_t b, uint32_t c, uint32_t d)
+{
+    const uint32_t ab = __builtin_amdgcn_perm(b, a, 0x0c0c0400u);
+    const uint32_t cd = __builtin_amdgcn_perm(d, c, 0x0c0c0400u);
+    return __builtin_amdgcn_perm(cd, ab, 0x05040100u);
+}
+
+// Eight values with their draws (Draws8 layout: element 2k takes the low
+// half of word k, element 2k+1 the high half) -> 8 codes, low nibble first.
+__device__ __forceinline__ uint32_t e2m1_sr8(const float (&y)[8], const uint32_t (&w)[4])
+{
+    uint32_t t[8];
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const uint32_t n = ~w[k];
+        t[2 * k] = e2m1_sr_conv(y[2 * k], n << 16);
+        t[2 * k + 1] = e2m1_sr_conv(y[2 * k + 1], n & 0xFFFF0000u);
+    }
+    const uint32_t ev = gather_byte0(t[0], t[2], t[4], t[6]);
+    const uint32_t od = gather_byte0(t[1], t[3], t[5], t[7]);
+    return (ev & 0x0F0F0F0Fu) | ((od << 4) & 0xF0F0F0F0u);
 }
 
 // Philox4x32-10 block function (Salmon, Moraes, Dror, Shaw, "Parallel Random

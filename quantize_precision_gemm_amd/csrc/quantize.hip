@@ -160,14 +160,15 @@ __device__ __forceinline__ uint2 encode16_rne(const float (&v)[16], float f)
 __device__ __forceinline__ uint2 encode16_sr(const float (&v)[16], float f, uint64_t seed,
                                              uint64_t g8)
 {
-    Draws8 d0 = sr_draws8(seed, g8);
-    Draws8 d1 = sr_draws8(seed, g8 + 1);
-    uint32_t lo = 0u, hi = 0u;
+    const Draws8 d0 = sr_draws8(seed, g8);
+    const Draws8 d1 = sr_draws8(seed, g8 + 1);
+    float y0[8], y1[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) lo |= e2m1_sr(v[i] * f, d0.get(i)) << (4 * i);
-#pragma unroll
-    for (int i = 0; i < 8; ++i) hi |= e2m1_sr(v[8 + i] * f, d1.get(i)) << (4 * i);
-    return make_uint2(lo, hi);
+    for (int i = 0; i < 8; ++i) {
+        y0[i] = v[i] * f;
+        y1[i] = v[8 + i] * f;
+    }
+    return make_uint2(e2m1_sr8(y0, d0.w), e2m1_sr8(y1, d1.w));
 }
 
 // ---------------------------------------------------------------------------
@@ -501,10 +502,10 @@ __device__ __forceinline__ uint32_t encode8_sr(const float (&v)[8], float f, uin
                                                uint64_t g8)
 {
     const Draws8 d = sr_draws8(seed, g8);
-    uint32_t w = 0u;
+    float y[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) w |= e2m1_sr(v[i] * f, d.get(i)) << (4 * i);
-    return w;
+    for (int i = 0; i < 8; ++i) y[i] = v[i] * f;
+    return e2m1_sr8(y, d.w);
 }
 
 template <bool kSR>
