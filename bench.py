@@ -291,6 +291,43 @@ def rht_size_study(q, torch, dev, reps=3, rows=40):
             "results": out, "fprop_dgrad_rht": fd}
 
 
+def copy_gbps(torch, dev, reps=5):
+    """Device copy of 1 GiB of bf16 (read + write bytes / time), the measured
+    stream rate the quantisers are also reported against."""
+    n = 1 << 29
+    src = torch.ones(n, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    s_, e_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s_.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e_.record()
+    torch.cuda.synchronize()
+    ms = s_.elapsed_time(e_) / reps
+    del src, dst
+    return 2.0 * 2 * n / (ms * 1e-3) / 1e9
+
+
+def device_info(torch, dev):
+    """Name, architecture, compute units and the current shader-clock DPM
+    level (from sysfs, if readable) of the GPU the bench ran on."""
+    p = torch.cuda.get_device_properties(dev)
+    sclk = None
+    try:
+        import glob
+        for f in sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk")):
+            lines = [l.strip() for l in open(f) if "*" in l]
+            if lines:
+                sclk = lines[0]
+                break
+    except OSError:
+        sclk = None
+    return {"name": p.name, "arch": p.gcnArchName, "compute_units": p.multi_processor_count,
+            "sclk_dpm_level": sclk}
+
+
 def cpu_baseline(data, tokens=M):
     """The oracle on a token slice of the step; W's quantisation, which does not
     scale with tokens, is timed in full and counted at tokens/M of its time."""
@@ -521,6 +558,7 @@ def main():
         "vs_baseline": None,
         "dtype": "f16",
         "data": "synthetic",
+        "device": device_info(torch, dev),
     }
     names = ("separate quantisers", "dual quantisers (nvfp4_quantize_dual)")
     result["schedules_ms_per_step"] = {
@@ -558,6 +596,10 @@ def main():
         result["quantize_gbps"] = {k: round(qb[k] / (avg[k] * 1e-3) / 1e9, 1) for k in qb}
         result["quantize_frac_of_hbm_peak"] = {
             k: round(qb[k] / (avg[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3) for k in qb}
+        cgb = copy_gbps(torch, dev)
+        result["copy_gbps"] = round(cgb, 1)
+        result["quantize_frac_of_copy"] = {
+            k: round(qb[k] / (avg[k] * 1e-3) / 1e9 / cgb, 3) for k in qb}
         result["ms_per_op"] = {k: round(v, 4) for k, v in avg.items()}
     if mx is not None:
         mx["speedup_vs_nvfp4"] = {k: round(v / result["gemm_tflops"][k], 2)
