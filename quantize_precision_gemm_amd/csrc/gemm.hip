@@ -312,9 +312,9 @@ constexpr int kAOp = kOpBytes;
 constexpr int kBOp = 256 * kBRow;
 constexpr int kStage = kAOp + kBOp + 256 * 4;
 
-struct NvRow {     // one thread's share of a K step
-    uint4 ca, cb;  // 16 code bytes of its A and B half rows
-    uint32_t s;    // A scales in bytes 0-1, B scales in bytes 2-3
+struct NvRow {      // one thread's share of a K step
+    uint4 ca, cb;   // 16 code bytes of its A and B half rows
+    uint32_t sa, sb;  // its 2 A and 2 B scale bytes, as loaded
 };
 
 }  // namespace
@@ -349,9 +349,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
     auto load_full = [&](int64_t k0, NvRow& w) {
         w.ca = *reinterpret_cast<const uint4*>(pa + (k0 >> 1));
         w.cb = *reinterpret_cast<const uint4*>(pb + (k0 >> 1));
-        const uint32_t sa = *reinterpret_cast<const uint16_t*>(psa + (k0 >> 4));
-        const uint32_t sb = *reinterpret_cast<const uint16_t*>(psb + (k0 >> 4));
-        w.s = sa | (sb << 16);
+        w.sa = *reinterpret_cast<const uint16_t*>(psa + (k0 >> 4));
+        w.sb = *reinterpret_cast<const uint16_t*>(psb + (k0 >> 4));
     };
     // partial last step: blocks past K get zero scales, so their codes decode
     // to zero (the 16 code bytes of a half row with one valid block still lie
@@ -360,17 +359,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
         const int64_t b0 = (k0 >> 4) + 2 * h;
         w.ca = b0 < nblk ? *reinterpret_cast<const uint4*>(pa + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
         w.cb = b0 < nblk ? *reinterpret_cast<const uint4*>(pb + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
-        uint32_t s = 0u;
+        uint32_t sa = 0u, sb = 0u;
         for (int j = 0; j < 2; ++j)
-            if (b0 + j < nblk)
-                s |= ((uint32_t)psa[(k0 >> 4) + j] << (8 * j)) |
-                     ((uint32_t)psb[(k0 >> 4) + j] << (16 + 8 * j));
-        w.s = s;
+            if (b0 + j < nblk) {
+                sa |= (uint32_t)psa[(k0 >> 4) + j] << (8 * j);
+                sb |= (uint32_t)psb[(k0 >> 4) + j] << (8 * j);
+            }
+        w.sa = sa;
+        w.sb = sb;
     };
     // A half row decoded to fp16 q * S in natural k order; B half row stored raw
     auto put = [&](const NvRow& w, int st) {
         uint8_t* base = lds + st * kStage;
-        const half2_t pair = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.s, 1.0f, false);
+        const half2_t pair = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.sa, 1.0f, false);
         const half2_t S0 = __builtin_shufflevector(pair, pair, 0, 0);
         const half2_t S1 = __builtin_shufflevector(pair, pair, 1, 1);
         const uint32_t cw[4] = {w.ca.x, w.ca.y, w.ca.z, w.ca.w};
@@ -379,7 +380,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
             *reinterpret_cast<half8_t*>(base + row * kRowBytes + 64 * h + 16 * d) =
                 decode8(cw[d], d < 2 ? S0 : S1);
         *reinterpret_cast<uint4*>(base + kAOp + row * kBRow + 16 * h) = w.cb;
-        *reinterpret_cast<uint16_t*>(base + kAOp + kBOp + row * 4 + 2 * h) = (uint16_t)(w.s >> 16);
+        *reinterpret_cast<uint16_t*>(base + kAOp + kBOp + row * 4 + 2 * h) = (uint16_t)w.sb;
     };
 
     float16_t acc[4][2];
@@ -426,6 +427,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
                 for (int tn = 0; tn < 2; ++tn)
                     acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_f16(af[cur][tm], bf[tn], acc[tm][tn], 0, 0, 0);
         }
+        // Issue order of the LDS reads and MFMAs: the B words, B scales and
+        // the A fragments of sub-steps 0 and 1 first, then each sub-step's 8
+        // MFMAs followed by the A reads of the sub-step after next, so every
+        // fragment is read a whole sub-step (8 MFMAs) before its use.  Left
+        // to itself the scheduler issues each read two MFMAs ahead to save
+        // registers, which exposes the LDS latency.
+        __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // 12 LDS reads
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // sub-step 0
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // A of sub-step 2
+        __builtin_amdgcn_sched_group_barrier(0x008, 8, 0);   // sub-step 1
+        __builtin_amdgcn_sched_group_barrier(0x100, 4, 0);   // A of sub-step 3
+        __builtin_amdgcn_sched_group_barrier(0x008, 16, 0);  // sub-steps 2, 3
     };
 
     // Step t's rows live in register stage t % 3 and its tile in LDS stage
