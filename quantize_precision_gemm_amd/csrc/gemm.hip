@@ -36,8 +36,8 @@
 // bf16 (k_gemm_bf16).  A bf16 operand is either "rows x K" (layout N) or
 // "K x rows" (layout T, rows contiguous), so the three bf16 passes read X,
 // W and dY where they lie.  Per step each thread moves 8 pieces of 16 bytes
-// into the 16-bit LDS tile, transposing an 8x8 block in registers for layout
-// T; its loads run one step ahead.
+// into LDS, where a layout-T tile stays K-major and its MFMA fragments come
+// from gfx950's transposing LDS reads; the loads run one step ahead.
 //
 // Lane layout of v_mfma_f32_32x32x16_{f16,bf16}: lane l supplies row (A) or
 // column (B) l % 32 and 8 consecutive k (the "half" l / 32 of the 16-wide
@@ -67,7 +67,6 @@ struct OpArgs {
     int64_t ld_scales;
     int scale_shift;        // NVFP4: scale row = row >> scale_shift
     const float* s_enc;     // NVFP4: tensor encode scale
-    int trans;              // bf16: 1 = stored K x rows (layout T), 0 = rows x K (layout N)
 };
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
@@ -720,98 +719,136 @@ namespace {
 // bf16 operands
 //
 // Thread rid (0..255 of its operand) moves 8 pieces of 16 bytes (8 values)
-// per step; kg = rid % 8 names the 8-wide k group of the step it covers and
-// c = rid / 8 the rows.
-// Layout N (rows x K): piece j is row c + 32 j, k group kg -- a wave's load
-//   covers 8 full 128-byte row segments.
-// Layout T (K x rows): piece j is k row 8 kg + j, rows 8c .. 8c+7 -- again 8
-//   full 128-byte segments per wave load; the 8x8 block is transposed in
-//   registers so that piece i becomes row 8c + i, k group kg.
-// Either way the 8 lanes of equal c write 128 consecutive LDS bytes, which
-// keeps the stage writes free of bank conflicts.  K and the row count are
-// multiples of 8, so a piece is wholly inside or wholly outside the operand.
-// kMode: 0 = both operands N, 1 = both T, 2 = per operand (OpArgs::trans);
-// in mode 2 both layouts' arithmetic runs and a select keeps one, so the two
-// halves of the workgroup run the same instructions.
+// per step.  The two layouts keep different LDS tiles, each 36 KB a stage:
+// Layout N (rows x K, K contiguous; Bf16RowsK): LDS rows of 64 k at a
+//   144-byte pitch.  kg = rid % 8 names the 8-wide k group, c = rid / 8 the
+//   rows: piece j is row c + 32 j, k group kg -- a wave's load covers 8 full
+//   128-byte row segments, and the 8 lanes of equal c write 128 consecutive
+//   LDS bytes.  A lane's MFMA fragment (row l % 32, k 8 (l / 32) .. +7) is
+//   one 16-byte read.
+// Layout T (K x rows, rows contiguous; Bf16KRows): the tile stays as it lies
+//   in memory, 64 k-rows of 256 values at a 576-byte pitch.  ck = rid % 32
+//   names the 8-row chunk and kr = rid / 32 the k-row: piece p is k-row
+//   kr + 8 p -- 32 lanes read and write 512 contiguous bytes.  A fragment
+//   comes from two transposing LDS reads (ds_read_b64_tr_b16): within each
+//   16-lane group, result element j of lane i is element 16 j + i of the 16
+//   lanes' 4-value pieces taken in lane order, so lane r of the group points
+//   at k-row k0 + r / 4, rows m0 + 4 (r % 4) .. +3, and every lane receives
+//   4 consecutive k of its own row.  Each transposing read touches 4 k-rows;
+//   the pitch of 512 + 64 bytes starts them 64 bytes apart in the banks.
+// K and the row count are multiples of 8, so a piece is wholly inside or
+// wholly outside the operand.
 // ---------------------------------------------------------------------------
-template <int kMode>
-struct Bf16Src {
-    struct Row {
-        uint4 v[8];
-    };
-    const uint16_t* base;  // piece 0 of step 0
-    int64_t ld, K, kstride, jstride;
-    int kg, c, cmax;
-    bool t_;
+struct Bf16Row {
+    uint4 v[8];
+};
 
-    __device__ __forceinline__ bool trans() const { return kMode == 2 ? t_ : kMode == 1; }
+// Per-thread load state of either layout: the first piece's address and two
+// small indices whose meaning depends on the layout.
+struct Bf16Load {
+    const uint16_t* base;
+    int64_t ld, K;
+    int i0, i1;
+};
 
+struct Bf16RowsK {
     // rid: this thread's index within its operand, r0: the tile's first row,
     // lim: rows of the operand
-    __device__ __forceinline__ Bf16Src(const OpArgs& o, int rid, int64_t r0, int64_t lim, int64_t K_)
+    static __device__ __forceinline__ Bf16Load make(const OpArgs& o, int rid, int64_t r0, int64_t lim,
+                                                    int64_t K)
     {
-        t_ = o.trans != 0;
-        ld = o.ld;
-        K = K_;
-        kg = rid & 7;
-        c = rid >> 3;
-        const uint16_t* d = static_cast<const uint16_t*>(o.data);
-        if (trans()) {
-            int64_t rc = r0 + 8 * c;  // first row of the piece; past the end: re-read the last piece
-            rc = rc + 8 <= lim ? rc : lim - 8;
-            base = d + (int64_t)(8 * kg) * ld + rc;
-            cmax = 0x7fffffff;
-            kstride = ld;
-            jstride = ld;
-        } else {
-            base = d + r0 * ld + 8 * kg;
-            const int64_t left = lim - r0 - 1;  // last valid row offset within the tile
-            cmax = left < 255 ? (int)left : 255;
-            kstride = 1;
-            jstride = ld;
-        }
+        const int kg = rid & 7, c = rid >> 3;
+        const int64_t left = lim - r0 - 1;  // last valid row offset within the tile
+        const int cmax = left < 255 ? (int)left : 255;
+        return Bf16Load{static_cast<const uint16_t*>(o.data) + r0 * o.ld + 8 * kg, o.ld, K, c, cmax};
     }
-    // row offset (N: row c + 32 j clamped; T: k row j) times ld
-    __device__ __forceinline__ const uint4* piece(int64_t k0, int j) const
+    // piece j: row c + 32 j (rows past the operand re-read its last row)
+    static __device__ __forceinline__ const uint4* piece(const Bf16Load& L, int64_t k0, int j)
     {
-        const int r = trans() ? j : min(c + 32 * j, cmax);
-        return reinterpret_cast<const uint4*>(base + (int64_t)r * jstride + k0 * kstride);
+        return reinterpret_cast<const uint4*>(L.base + (int64_t)min(L.i0 + 32 * j, L.i1) * L.ld + k0);
     }
-    __device__ __forceinline__ void load_full(int64_t k0, Row& w) const
+    static __device__ __forceinline__ void load_full(const Bf16Load& L, int64_t k0, Bf16Row& w)
     {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) w.v[j] = *piece(k0, j);
+        for (int j = 0; j < 8; ++j) w.v[j] = *piece(L, k0, j);
     }
     // partial last step: pieces past K read as zero
-    __device__ __forceinline__ void load_tail(int64_t k0, Row& w) const
+    static __device__ __forceinline__ void load_tail(const Bf16Load& L, int kg, int64_t k0, Bf16Row& w)
     {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int64_t k = k0 + 8 * kg + (trans() ? j : 0);
-            w.v[j] = (k < K) ? *piece(k0, j) : make_uint4(0, 0, 0, 0);
-        }
+        for (int j = 0; j < 8; ++j) w.v[j] = (k0 + 8 * kg < L.K) ? *piece(L, k0, j) : make_uint4(0, 0, 0, 0);
     }
-    __device__ __forceinline__ void store(const Row& w, uint8_t* __restrict__ op) const
+    static __device__ __forceinline__ void store(const Bf16Row& w, int rid, uint8_t* __restrict__ op)
     {
-        // T: w.v[j] holds rows 8c .. 8c+7 at k = 8kg + j, two rows per dword;
-        // row 2d + h of the block takes half h of dword d of every piece
-        const uint32_t* v = reinterpret_cast<const uint32_t*>(w.v);
-        const int rbase = trans() ? 8 * c : c, rstep = trans() ? 1 : 32;
+        const int kg = rid & 7, c = rid >> 3;
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int d = i >> 1;
-            const uint32_t sel = (i & 1) ? 0x07060302u : 0x05040100u;
-            uint4 t = w.v[i];
-            if (kMode != 0) {
-                uint4 u;
-                u.x = __builtin_amdgcn_perm(v[4 * 1 + d], v[4 * 0 + d], sel);
-                u.y = __builtin_amdgcn_perm(v[4 * 3 + d], v[4 * 2 + d], sel);
-                u.z = __builtin_amdgcn_perm(v[4 * 5 + d], v[4 * 4 + d], sel);
-                u.w = __builtin_amdgcn_perm(v[4 * 7 + d], v[4 * 6 + d], sel);
-                if (trans()) t = u;
-            }
-            *reinterpret_cast<uint4*>(op + (rbase + rstep * i) * kRowBytes + 16 * kg) = t;
-        }
+        for (int j = 0; j < 8; ++j) *reinterpret_cast<uint4*>(op + (c + 32 * j) * kRowBytes + 16 * kg) = w.v[j];
+    }
+    // A lane's fragment (row `row` + lane % 32, sub-step 0) sits at byte
+    // frag_off(row, lane); 32 rows further on add kRows32, a sub-step kSub.
+    static constexpr int kRows32 = 32 * kRowBytes, kSub = 32;
+    static __device__ __forceinline__ int frag_off(int row, int lane)
+    {
+        return (row + (lane & 31)) * kRowBytes + 16 * (lane >> 5);
+    }
+    static __device__ __forceinline__ bf16x8_t frag(const uint8_t* at)
+    {
+        return *reinterpret_cast<const bf16x8_t*>(at);
+    }
+};
+
+constexpr int kTPitch = 576;  // LDS bytes per k-row of a layout-T tile: 256 values + 64 pad
+static_assert(64 * kTPitch == kOpBytes, "both layouts fill one operand stage");
+
+typedef short short4_t __attribute__((ext_vector_type(4)));
+
+struct Bf16KRows {
+    static __device__ __forceinline__ Bf16Load make(const OpArgs& o, int rid, int64_t r0, int64_t lim,
+                                                    int64_t K)
+    {
+        const int ck = rid & 31, kr = rid >> 5;
+        int64_t m = r0 + 8 * ck;  // chunks past the operand re-read its last chunk
+        m = m + 8 <= lim ? m : lim - 8;
+        return Bf16Load{static_cast<const uint16_t*>(o.data) + (int64_t)kr * o.ld + m, o.ld, K, kr, 0};
+    }
+    static __device__ __forceinline__ const uint4* piece(const Bf16Load& L, int64_t k0, int p)
+    {
+        return reinterpret_cast<const uint4*>(L.base + (k0 + 8 * p) * L.ld);
+    }
+    static __device__ __forceinline__ void load_full(const Bf16Load& L, int64_t k0, Bf16Row& w)
+    {
+#pragma unroll
+        for (int p = 0; p < 8; ++p) w.v[p] = *piece(L, k0, p);
+    }
+    static __device__ __forceinline__ void load_tail(const Bf16Load& L, int, int64_t k0, Bf16Row& w)
+    {
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            w.v[p] = (k0 + L.i0 + 8 * p < L.K) ? *piece(L, k0, p) : make_uint4(0, 0, 0, 0);
+    }
+    static __device__ __forceinline__ void store(const Bf16Row& w, int rid, uint8_t* __restrict__ op)
+    {
+        const int ck = rid & 31, kr = rid >> 5;
+#pragma unroll
+        for (int p = 0; p < 8; ++p) *reinterpret_cast<uint4*>(op + (kr + 8 * p) * kTPitch + 16 * ck) = w.v[p];
+    }
+    // lane r of 16-lane group G points at k-row 8 (G / 2) + r / 4 (+ 4 for
+    // the second read), rows row + 16 (G % 2) + 4 (r % 4) .. +3
+    static constexpr int kRows32 = 64, kSub = 16 * kTPitch;
+    static __device__ __forceinline__ int frag_off(int row, int lane)
+    {
+        const int G = lane >> 4, r = lane & 15;
+        return (8 * (G >> 1) + (r >> 2)) * kTPitch + 2 * (row + 16 * (G & 1) + 4 * (r & 3));
+    }
+    static __device__ __forceinline__ bf16x8_t frag(const uint8_t* at)
+    {
+        typedef __attribute__((address_space(3))) short4_t lds_short4;
+        lds_short4* p0 = (lds_short4*)(__attribute__((address_space(3))) uint8_t*)(at);
+        lds_short4* p1 = (lds_short4*)(__attribute__((address_space(3))) uint8_t*)(at + 4 * kTPitch);
+        const short4_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+        const short4_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+        typedef short short8_t __attribute__((ext_vector_type(8)));
+        return __builtin_bit_cast(bf16x8_t, (short8_t)__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
     }
 };
 
@@ -842,51 +879,58 @@ __device__ __forceinline__ void interleave_step(std::integer_sequence<int, kMs..
 
 }  // namespace
 
-template <class Src, bool kOutF32>
+template <class SA, class SB, bool kOutF32>
 __global__ __launch_bounds__(512, 1) void k_gemm_bf16(OpArgs A, OpArgs B, int64_t M, int64_t N,
                                                       int64_t K, void* __restrict__ c, int64_t ldc)
 {
-    typedef typename Src::Row Row;
     __shared__ __attribute__((aligned(16))) uint8_t lds[2][2][kOpBytes];  // [stage][A/B]
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
-    const int g = lane >> 5, lr = lane & 31;
     int64_t tile_m, tile_n;
     tile_of(M, N, tile_m, tile_n);
 
-    // threads 0..255 bring the A tile into LDS, 256..511 the B tile
+    // threads 0..255 (waves 0-3) bring the A tile into LDS, 256..511 the B tile
     const bool is_b = tid >= 256;
     const int rid = tid & 255;
-    const Src src(is_b ? B : A, rid, is_b ? tile_n * kBN : tile_m * kBM, is_b ? N : M, K);
-    auto put = [&](const Row& w, int stage) { src.store(w, lds[stage][is_b ? 1 : 0]); };
+    constexpr bool kSame = std::is_same<SA, SB>::value;
+    const OpArgs& op = is_b ? B : A;
+    const int64_t r0 = is_b ? tile_n * kBN : tile_m * kBM, lim = is_b ? N : M;
+    const Bf16Load src = (kSame || !is_b) ? SA::make(op, rid, r0, lim, K) : SB::make(op, rid, r0, lim, K);
+    auto load_full = [&](int64_t k0, Bf16Row& w) {
+        if (!kSame && is_b) SB::load_full(src, k0, w);
+        else SA::load_full(src, k0, w);
+    };
+    auto load_tail = [&](int64_t k0, Bf16Row& w) {
+        if (!kSame && is_b) SB::load_tail(src, rid & 7, k0, w);
+        else SA::load_tail(src, rid & 7, k0, w);
+    };
+    auto put = [&](const Bf16Row& w, int stage) {
+        if (!kSame && is_b) SB::store(w, rid, lds[stage][1]);
+        else SA::store(w, rid, lds[stage][is_b ? 1 : 0]);
+    };
 
     float16_t acc[4][2];
     zero_acc(acc);
-    const int wm = wave >> 2, wn = wave & 3;
-    // fragment read offsets within a stage: row (32 t + lr) of the wave's
-    // 128-row A slab / 64-row B slab, k = 16 i + 8 g
-    const int a_frag = (wm * 128 + lr) * kRowBytes + 16 * g;
-    const int b_frag = (wn * 64 + lr) * kRowBytes + 16 * g;
+    const int wm = wave >> 2, wn = wave & 3;  // the wave's 128-row A slab and 64-row B slab
+    const int a_off = SA::frag_off(wm * 128, lane), b_off = SB::frag_off(wn * 64, lane);
 
     auto compute = [&](int stage) {
-        const uint8_t* As = lds[stage][0];
-        const uint8_t* Bs = lds[stage][1];
+        const uint8_t* As = lds[stage][0] + a_off;
+        const uint8_t* Bs = lds[stage][1] + b_off;
         bf16x8_t af[2][4], bf[2][2];  // fragments of two sub-steps in flight
 #pragma unroll
-        for (int t = 0; t < 4; ++t) af[0][t] = *reinterpret_cast<const bf16x8_t*>(As + a_frag + t * 32 * kRowBytes);
+        for (int t = 0; t < 4; ++t) af[0][t] = SA::frag(As + t * SA::kRows32);
 #pragma unroll
-        for (int t = 0; t < 2; ++t) bf[0][t] = *reinterpret_cast<const bf16x8_t*>(Bs + b_frag + t * 32 * kRowBytes);
+        for (int t = 0; t < 2; ++t) bf[0][t] = SB::frag(Bs + t * SB::kRows32);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int cur = i & 1, nxt = cur ^ 1;
             if (i < 3) {
 #pragma unroll
-                for (int t = 0; t < 4; ++t)
-                    af[nxt][t] = *reinterpret_cast<const bf16x8_t*>(As + a_frag + t * 32 * kRowBytes + 32 * (i + 1));
+                for (int t = 0; t < 4; ++t) af[nxt][t] = SA::frag(As + t * SA::kRows32 + (i + 1) * SA::kSub);
 #pragma unroll
-                for (int t = 0; t < 2; ++t)
-                    bf[nxt][t] = *reinterpret_cast<const bf16x8_t*>(Bs + b_frag + t * 32 * kRowBytes + 32 * (i + 1));
+                for (int t = 0; t < 2; ++t) bf[nxt][t] = SB::frag(Bs + t * SB::kRows32 + (i + 1) * SB::kSub);
             }
 #pragma unroll
             for (int tm = 0; tm < 4; ++tm)
@@ -895,6 +939,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(OpArgs A, OpArgs B, int64_
                     acc[tm][tn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][tm], bf[cur][tn], acc[tm][tn], 0, 0, 0);
         }
     };
+    // the interleaving hint counts one 16-byte LDS read per fragment
+    constexpr bool kHints = std::is_same<SA, Bf16RowsK>::value && std::is_same<SB, Bf16RowsK>::value;
 
     // One register stage: the loads of step s+1 are issued before the MFMAs
     // of step s (a scheduling barrier keeps them there) and written to LDS
@@ -902,29 +948,29 @@ __global__ __launch_bounds__(512, 1) void k_gemm_bf16(OpArgs A, OpArgs B, int64_
     const int64_t nsteps = (K + kKS - 1) / kKS;
     const int64_t nfull = K / kKS;
     int64_t s = 0;
-    Row g0;
+    Bf16Row g0;
     if (nfull > 0) {
-        src.load_full(0, g0);
+        load_full(0, g0);
         put(g0, 0);
     }
     __syncthreads();
     for (; s + 2 <= nfull; s += 2) {
-        src.load_full((s + 1) * kKS, g0);
+        load_full((s + 1) * kKS, g0);
         __builtin_amdgcn_sched_barrier(0);
         compute(0);
         put(g0, 1);
-        interleave_step(std::make_integer_sequence<int, 32>{});
+        if constexpr (kHints) interleave_step(std::make_integer_sequence<int, 32>{});
         __syncthreads();
-        src.load_full((s + 2 < nfull ? s + 2 : nfull - 1) * kKS, g0);
+        load_full((s + 2 < nfull ? s + 2 : nfull - 1) * kKS, g0);
         __builtin_amdgcn_sched_barrier(0);
         compute(1);
         put(g0, 0);  // harmless on the last pass: stage 0 is not read again
-        interleave_step(std::make_integer_sequence<int, 32>{});
+        if constexpr (kHints) interleave_step(std::make_integer_sequence<int, 32>{});
         __syncthreads();
     }
     if (s < nfull) compute(0);  // odd number of full steps: the last one is in stage 0
     if (nfull < nsteps) {       // partial last step
-        src.load_tail(nfull * kKS, g0);
+        load_tail(nfull * kKS, g0);
         __syncthreads();
         put(g0, 1);
         __syncthreads();
@@ -971,8 +1017,8 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
 {
     if (M == 0 || N == 0) return;
     if (K == 0) return launch_fill_zero(M, N, c, ldc, out_fp32, s);
-    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc, 0};
-    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc, 0};
+    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc};
+    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc};
     if (out_fp32)
         hipLaunchKernelGGL(k_gemm_nv<true>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
     else
@@ -996,8 +1042,8 @@ void launch_gemm_nt_amax(const GemmOperand& a, const GemmOperand& b, int64_t M, 
     hipLaunchKernelGGL(k_zero_amax, dim3(1), dim3(1), 0, s, ab, rb);
     if (M == 0 || N == 0) return;
     if (K == 0) return launch_fill_zero(M, N, c, ldc, false, s);  // maxima stay 0
-    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc, 0};
-    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc, 0};
+    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc};
+    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc};
     if (rb)
         hipLaunchKernelGGL((k_gemm_nv<false, 2>), tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K,
                            static_cast<void*>(c), ldc, ab, rb, mask);
@@ -1011,22 +1057,22 @@ void launch_gemm_mx(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
 {
     if (M == 0 || N == 0) return;
     if (K == 0) return launch_fill_zero(M, N, c, ldc, out_fp32, s);
-    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, 0, nullptr, 0};
-    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, 0, nullptr, 0};
+    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, 0, nullptr};
+    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, 0, nullptr};
     if (out_fp32)
         hipLaunchKernelGGL(k_gemm_mx<true>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
     else
         hipLaunchKernelGGL(k_gemm_mx<false>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
 }
 
-template <class Src>
+template <class SA, class SB>
 static void launch_bf16(const OpArgs& a, const OpArgs& b, int64_t M, int64_t N, int64_t K, void* c,
                         int64_t ldc, bool out_fp32, hipStream_t s)
 {
     if (out_fp32)
-        hipLaunchKernelGGL((k_gemm_bf16<Src, true>), tile_grid(M, N), dim3(512), 0, s, a, b, M, N, K, c, ldc);
+        hipLaunchKernelGGL((k_gemm_bf16<SA, SB, true>), tile_grid(M, N), dim3(512), 0, s, a, b, M, N, K, c, ldc);
     else
-        hipLaunchKernelGGL((k_gemm_bf16<Src, false>), tile_grid(M, N), dim3(512), 0, s, a, b, M, N, K, c, ldc);
+        hipLaunchKernelGGL((k_gemm_bf16<SA, SB, false>), tile_grid(M, N), dim3(512), 0, s, a, b, M, N, K, c, ldc);
 }
 
 void launch_bf16_gemm(const uint16_t* a, int64_t lda, bool a_t, const uint16_t* b, int64_t ldb,
@@ -1035,14 +1081,16 @@ void launch_bf16_gemm(const uint16_t* a, int64_t lda, bool a_t, const uint16_t* 
 {
     if (M == 0 || N == 0) return;
     if (K == 0) return launch_fill_zero(M, N, c, ldc, out_fp32, s);
-    const OpArgs A{a, lda, nullptr, 0, 0, nullptr, a_t ? 1 : 0};
-    const OpArgs B{b, ldb, nullptr, 0, 0, nullptr, b_t ? 1 : 0};
-    if (a_t != b_t)
-        launch_bf16<Bf16Src<2>>(A, B, M, N, K, c, ldc, out_fp32, s);
-    else if (a_t)
-        launch_bf16<Bf16Src<1>>(A, B, M, N, K, c, ldc, out_fp32, s);
+    const OpArgs A{a, lda, nullptr, 0, 0, nullptr};
+    const OpArgs B{b, ldb, nullptr, 0, 0, nullptr};
+    if (!a_t && !b_t)
+        launch_bf16<Bf16RowsK, Bf16RowsK>(A, B, M, N, K, c, ldc, out_fp32, s);
+    else if (!a_t)
+        launch_bf16<Bf16RowsK, Bf16KRows>(A, B, M, N, K, c, ldc, out_fp32, s);
+    else if (b_t)
+        launch_bf16<Bf16KRows, Bf16KRows>(A, B, M, N, K, c, ldc, out_fp32, s);
     else
-        launch_bf16<Bf16Src<0>>(A, B, M, N, K, c, ldc, out_fp32, s);
+        launch_bf16<Bf16KRows, Bf16RowsK>(A, B, M, N, K, c, ldc, out_fp32, s);
 }
 
 }  // namespace nvfp4
