@@ -426,9 +426,9 @@ def main():
                          "the reference that scales hardware byte counters")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(the layer shards by tokens; see the design notes). Run with --gpus 1.",
-              file=sys.stderr)
+        print("bench.py measures one GPU only: the library has no multi-GPU path "
+              "(the layer would shard by tokens, with an all-reduce of dW and of the "
+              "tensor maxima). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     mlp = args.workload == "mlp"
     steps = args.steps if args.steps is not None else (5 if mlp else 20)

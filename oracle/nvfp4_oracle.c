@@ -17,8 +17,8 @@
  *   [P2] "LLM-Pretraining in 4-Bit: NVIDIA stellt NVFP4-Trainingsansatz vor",
  *        section "Das Wichtigste".
  * The pages fix the recipe (which tensor gets which treatment) but not the
- * arithmetic; each reading taken where they are silent is named "reading"
- * below and listed with its justification in the design notes.
+ * arithmetic; each reading taken where they are silent is marked "reading"
+ * below.
  */
 #include <float.h>
 #include <math.h>
