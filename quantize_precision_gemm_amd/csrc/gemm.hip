@@ -222,8 +222,9 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float a
             if (row < M && col < N) {
                 if constexpr (kOutF32) {
                     float* dst = static_cast<float*>(c) + row * ldc + col;
-                    if (col + 4 <= N) {
-                        *reinterpret_cast<float4*>(dst) = v;
+                    if (col + 4 <= N) {  // streaming store: the output is not read back here
+                        typedef float f32x4_t __attribute__((ext_vector_type(4)));
+                        __builtin_nontemporal_store(f32x4_t{v.x, v.y, v.z, v.w}, reinterpret_cast<f32x4_t*>(dst));
                     } else {
                         dst[0] = v.x;
                         if (col + 1 < N) dst[1] = v.y;
@@ -243,9 +244,10 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float a
                         b2 = f32_to_bf16_rne(v.z);
                         b3 = f32_to_bf16_rne(v.w);
                     }
-                    if (col + 4 <= N) {
-                        *reinterpret_cast<uint2*>(dst) =
-                            make_uint2(b0 | ((uint32_t)b1 << 16), b2 | ((uint32_t)b3 << 16));
+                    if (col + 4 <= N) {  // streaming store, as above
+                        typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                        __builtin_nontemporal_store(u32x2_t{b0 | ((uint32_t)b1 << 16), b2 | ((uint32_t)b3 << 16)},
+                                                    reinterpret_cast<u32x2_t*>(dst));
                     } else {
                         dst[0] = b0;
                         if (col + 1 < N) dst[1] = b1;
