@@ -108,25 +108,64 @@ def test_rht_quantize_brute_force():
                 assert codes[16 * b + i] == (sign | c)
 
 
+def _exact_value(q, r, k):
+    """Exact decoded value q * S of element (r, k) of an NVFP4 tensor, read
+    straight from its packed codes and scale bytes through the exact model's
+    value lists (no oracle decode table): code = nibble k % 2 of byte k / 2
+    (low nibble first), scale byte at (r, k / 16) for 1x16 blocks and at
+    (r / 16, k / 16) for 16x16 blocks."""
+    byte = int(q.codes[r, k // 2])
+    c = (byte >> 4) if k % 2 else (byte & 0xF)
+    sb = int(q.scales[r, k // 16] if q.block == oracle.BLOCK_1X16 else q.scales[r // 16, k // 16])
+    mag = ex.E2M1_MAGS[c & 7] * ex.E4M3_VAL[sb]
+    return -mag if c & 8 else mag
+
+
 def _exact_gemm(a, b, dgrad=False):
-    """Exact rational GEMM of dequantised operands (q * S / s_enc)."""
-    A = oracle.dequantize_qs(a)
-    B = oracle.dequantize_qs(b)
-    if dgrad:
-        B = B.T
+    """Exact rational GEMM of the dequantised operands, (q * S) / s_enc.
+    fprop/wgrad: C[m, n] = sum_k A[m, k] B[n, k]; dgrad: C[m, k] = sum_n A[m, n] B[n, k]."""
     alpha = Fraction(1) / (Fraction(a.s_enc) * Fraction(b.s_enc))
-    M, N = A.shape[0], B.shape[0]
+    M = a.rows
+    if dgrad:
+        N, red = b.cols, a.cols
+        term = lambda m, n, j: _exact_value(a, m, j) * _exact_value(b, j, n)
+    else:
+        N, red = b.rows, a.cols
+        term = lambda m, n, j: _exact_value(a, m, j) * _exact_value(b, n, j)
     out = np.empty((M, N))
     for m in range(M):
         for n in range(N):
-            s = sum(Fraction(float(A[m, k])) * Fraction(float(B[n, k])) for k in range(A.shape[1]))
-            out[m, n] = float(s * alpha)
+            out[m, n] = float(sum(term(m, n, j) for j in range(red)) * alpha)
     return out
+
+
+def test_decode_tables_match_exact_model():
+    # The fp64 decode tables every oracle GEMM and dequantisation multiplies by
+    # (Technische Zusammenfassung 2.A: E2M1 elements, E4M3 block scales) equal
+    # the exact model's value lists entry by entry: all 16 E2M1 codes, and all
+    # 127 finite E4M3 bytes of each sign, including the subnormal scale bytes
+    # 0x01-0x07 (m * 2^-9).
+    for c in range(16):
+        want = ex.E2M1_MAGS[c & 7]
+        assert Fraction(float(oracle.E2M1_VALUES[c])) == (-want if c & 8 else want)
+        assert np.signbit(oracle.E2M1_VALUES[c]) == bool(c & 8)
+    for b, v in ex.E4M3_LIST:
+        assert Fraction(float(oracle.E4M3_VALUES[b])) == v, hex(b)
+        assert Fraction(float(oracle.E4M3_VALUES[0x80 | b])) == -v, hex(0x80 | b)
+    assert [float(oracle.E4M3_VALUES[b]) for b in range(1, 8)] == [m / 512 for m in range(1, 8)]
+    assert np.isnan(oracle.E4M3_VALUES[0x7F]) and np.isnan(oracle.E4M3_VALUES[0xFF])
+
+
+def _rows_scaled(rng, shape, factors):
+    """bf16 rows ~N(0, 1) times per-row factors (spans E4M3's subnormal and zero scales)."""
+    x = rng.standard_normal(shape) * np.asarray(factors, np.float64)[:, None]
+    return wl.f32_to_bf16_bits(x.astype(np.float32))
 
 
 def test_gemm_reference_matches_exact_rationals():
     # I-10 (exactness part): the fp64 reference equals the exact product of the
-    # dequantised operands to fp64 rounding, for all three passes.
+    # dequantised operands (decoded independently of the oracle's tables) to
+    # fp64 rounding, for all three passes.
     rng = np.random.default_rng(4)
     x = wl.normal(rng, (4, 32), 1.0)
     w = wl.normal(rng, (16, 32), 0.02)
@@ -143,6 +182,27 @@ def test_gemm_reference_matches_exact_rationals():
     xt = oracle.rht_quantize(wl.normal(rng, (32, 5), 1.0), mask, oracle.RNE)
     dw = oracle.gemm(oracle.WGRAD, dyt, xt)
     np.testing.assert_allclose(dw, _exact_gemm(dyt, xt), rtol=1e-13, atol=0)
+
+
+@pytest.mark.parametrize("rounding", [oracle.RNE, oracle.SR])
+def test_gemm_reference_exact_with_subnormal_block_scales(rounding):
+    # Blocks whose E4M3 scale is subnormal (bytes 0x01-0x07) or zero: rows
+    # 1e-4 .. 1e-7 of the tensor's largest row (block scale ~448 * ratio, so
+    # 2^-9 .. 2^-6 is subnormal, below 2^-10 rounds to zero).  A wrong
+    # subnormal decode entry changes these rows of the product.
+    rng = np.random.default_rng(40)
+    factors = [1.0, 3e-5, 1e-5, 4e-6, 1.5e-6, 1e-7]
+    a = oracle.quantize(_rows_scaled(rng, (6, 48), factors), rounding=rounding, seed=11)
+    b = oracle.quantize(_rows_scaled(rng, (5, 48), [1.0, 2e-5, 7e-6, 1.0, 2e-6]), rounding=rounding, seed=12)
+    sub_a = set(int(v) for v in a.scales.reshape(-1) if 0 < v < 8)
+    sub_b = set(int(v) for v in b.scales.reshape(-1) if 0 < v < 8)
+    assert len(sub_a) >= 3 and len(sub_b) >= 2, (sub_a, sub_b)  # the case is exercised
+    assert (a.scales == 0).any()
+    got = oracle.gemm(oracle.WGRAD, a, b)  # C = A B^T over 1x16 blocks
+    want = _exact_gemm(a, b)
+    np.testing.assert_allclose(got, want, rtol=1e-13, atol=0)
+    # the subnormal-scale rows are not negligible in their own outputs
+    assert np.all(np.abs(want[1:5, 1:3]) > 0)
 
 
 def test_gemm_fp32_accumulation_within_budget():
