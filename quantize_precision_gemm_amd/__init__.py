@@ -193,6 +193,82 @@ def _check_bf16(x):
         raise ValueError("the last dimension must be contiguous")
 
 
+def _check_buf(t, what, device, dtype, min_shape):
+    """A caller-supplied buffer: a 2-D (or, for min_shape of length 1, 1-D)
+    contiguous tensor of `dtype` on `device`, at least `min_shape` large.
+    The C descriptor carries no buffer sizes, so this is the only place an
+    undersized buffer can be caught before a kernel writes past its end."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{what}: expected a tensor")
+    if t.dtype != dtype:
+        raise ValueError(f"{what}: dtype {t.dtype}, expected {dtype}")
+    if t.device != device:
+        raise ValueError(f"{what}: on {t.device}, expected {device}")
+    if t.dim() != len(min_shape):
+        raise ValueError(f"{what}: {t.dim()}-D, expected {len(min_shape)}-D")
+    if not t.is_contiguous():
+        raise ValueError(f"{what}: must be contiguous (its row length is its leading dimension)")
+    if any(have < need for have, need in zip(t.shape, min_shape)):
+        raise ValueError(f"{what}: shape {tuple(t.shape)} smaller than the {tuple(min_shape)} needed")
+
+
+def _same_device(a, b):
+    """torch devices compare unequal for cuda vs cuda:0; normalise the index."""
+    if a.type != b.type:
+        return False
+    ia = a.index if a.index is not None else (torch.cuda.current_device() if a.type == "cuda" else None)
+    ib = b.index if b.index is not None else (torch.cuda.current_device() if b.type == "cuda" else None)
+    return ia == ib
+
+
+def _check_nvfp4_buffers(t, rows, cols, block, device, with_transpose=False, what="out"):
+    """Every buffer of an NVFP4 (or MXFP4) tensor is large enough for a
+    rows x cols tensor with `block` layout, on `device`."""
+    if not isinstance(t, NVFP4Tensor):
+        raise TypeError(f"{what}: expected an NVFP4Tensor")
+    device = t.codes.device if device is None else device
+    if not _same_device(t.codes.device, device):
+        raise ValueError(f"{what}.codes: on {t.codes.device}, expected {device}")
+    device = t.codes.device
+    per = 32 if block == BLOCK_MX32 else 16
+    srows = rows // 16 if block == BLOCK_16X16 else rows
+    _check_buf(t.codes, f"{what}.codes", device, torch.uint8, (rows, _round_up(cols, 32) // 2))
+    _check_buf(t.scales, f"{what}.scales", device, torch.uint8, (srows, cols // per))
+    if block != BLOCK_MX32:
+        _check_buf(t.amax, f"{what}.amax", device, torch.float32, (1,))
+        _check_buf(t.s_enc, f"{what}.s_enc", device, torch.float32, (1,))
+    if with_transpose:
+        if t.codes_t is None or t.scales_t is None:
+            raise ValueError(f"{what}: the transposed copy was asked for but has no buffers")
+        _check_buf(t.codes_t, f"{what}.codes_t", device, torch.uint8, (cols, _round_up(rows, 32) // 2))
+        _check_buf(t.scales_t, f"{what}.scales_t", device, torch.uint8, (cols // 16, rows // 16))
+
+
+def _check_operand(t, what):
+    """A GEMM operand: its buffers hold what its descriptor claims."""
+    _check_nvfp4_buffers(t, t.rows, t.cols, t.block, None, False, what)
+
+
+def _check_gemm_out(out, shape, device, dtypes=(torch.float32, torch.bfloat16)):
+    if not isinstance(out, torch.Tensor):
+        raise TypeError("out: expected a tensor")
+    if out.dtype not in dtypes:
+        raise TypeError(f"output must be one of {dtypes} with a contiguous last dimension")
+    if out.dim() != 2 or tuple(out.shape) != tuple(shape):
+        raise ValueError(f"out: shape {tuple(out.shape)}, expected {tuple(shape)}")
+    if out.numel() > 0 and out.stride(1) != 1:
+        raise TypeError("output must have a contiguous last dimension")
+    if out.numel() > 0 and out.stride(0) < shape[1]:
+        raise ValueError("out: row stride shorter than a row")
+    if not _same_device(out.device, device):
+        raise ValueError(f"out: on {out.device}, expected {device}")
+
+
+def _check_scalar_out(t, what, device):
+    if t is not None:
+        _check_buf(t, what, device, torch.float32, (1,))
+
+
 def nvfp4_quantize(x, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None,
                    with_transpose=False, out=None, stream=None):
     """Quantise a row-major bf16 matrix to NVFP4 (see nvfp4_quantize in nvfp4.h)."""
@@ -200,6 +276,9 @@ def nvfp4_quantize(x, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None,
     rows, cols = x.shape
     if out is None:
         out = alloc_nvfp4(rows, cols, block, with_transpose and block == BLOCK_16X16, x.device)
+    _check_nvfp4_buffers(out, rows, cols, block, x.device,
+                         out.codes_t is not None or out.scales_t is not None)
+    _check_scalar_out(amax_in, "amax_in", x.device)
     d = out.descriptor()
     st = load_library().nvfp4_quantize(_ptr(x), rows, cols, x.stride(0), block, rounding,
                                        seed, _ptr(amax_in), ctypes.byref(d), _stream(stream))
@@ -214,6 +293,8 @@ def nvfp4_rht_quantize(x, sign_mask, rounding=RNE, seed=0, amax_in=None, out=Non
     tokens, channels = x.shape
     if out is None:
         out = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device)
+    _check_nvfp4_buffers(out, channels, tokens, BLOCK_1X16, x.device)
+    _check_scalar_out(amax_in, "amax_in", x.device)
     d = out.descriptor()
     st = load_library().nvfp4_rht_quantize(_ptr(x), tokens, channels, x.stride(0), sign_mask,
                                            rounding, seed, _ptr(amax_in), ctypes.byref(d),
@@ -235,6 +316,10 @@ def nvfp4_quantize_dual(x, sign_mask, rounding=RNE, seed=0, seed_rht=0, amax_in=
         out = alloc_nvfp4(tokens, channels, BLOCK_1X16, False, x.device)
     if out_rht is None:
         out_rht = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device)
+    _check_nvfp4_buffers(out, tokens, channels, BLOCK_1X16, x.device)
+    _check_nvfp4_buffers(out_rht, channels, tokens, BLOCK_1X16, x.device, what="out_rht")
+    _check_scalar_out(amax_in, "amax_in", x.device)
+    _check_scalar_out(amax_rht_in, "amax_rht_in", x.device)
     d, dr = out.descriptor(), out_rht.descriptor()
     ld_x = x.stride(0) if channels > 0 else 0  # no row stride without columns
     st = load_library().nvfp4_quantize_dual(_ptr(x), tokens, channels, ld_x, sign_mask,
@@ -255,6 +340,9 @@ def nvfp4_quantize_rht_rows(x, sign_mask, block=BLOCK_1X16, rounding=RNE, seed=0
     rows, cols = x.shape
     if out is None:
         out = alloc_nvfp4(rows, cols, block, with_transpose and block == BLOCK_16X16, x.device)
+    _check_nvfp4_buffers(out, rows, cols, block, x.device,
+                         out.codes_t is not None or out.scales_t is not None)
+    _check_scalar_out(amax_in, "amax_in", x.device)
     d = out.descriptor()
     st = load_library().nvfp4_quantize_rht_rows(_ptr(x), rows, cols, x.stride(0), block, sign_mask,
                                                 rounding, seed, _ptr(amax_in), ctypes.byref(d),
@@ -272,6 +360,8 @@ def nvfp4_rht_quantize_sized(x, size, signs, rounding=RNE, seed=0, amax_in=None,
     tokens, channels = x.shape
     if out is None:
         out = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device)
+    _check_nvfp4_buffers(out, channels, tokens, BLOCK_1X16, x.device)
+    _check_scalar_out(amax_in, "amax_in", x.device)
     d = out.descriptor()
     st = load_library().nvfp4_rht_quantize_sized(_ptr(x), tokens, channels, x.stride(0), size,
                                                  signs, rounding, seed, _ptr(amax_in),
@@ -294,6 +384,7 @@ def nvfp4_mx_quantize(x, mode=MX_ROWS, sign_mask=0, rounding=RNE, seed=0, out=No
     orows, ocols = (rows, cols) if mode == MX_ROWS else (cols, rows)
     if out is None:
         out = alloc_nvfp4(orows, ocols, BLOCK_MX32, False, x.device)
+    _check_nvfp4_buffers(out, orows, ocols, BLOCK_MX32, x.device)
     d = out.descriptor()
     ld_x = x.stride(0) if cols > 0 else 0
     st = load_library().nvfp4_mx_quantize(_ptr(x), rows, cols, ld_x, mode, sign_mask, rounding,
@@ -306,10 +397,11 @@ def nvfp4_mx_quantize(x, mode=MX_ROWS, sign_mask=0, rounding=RNE, seed=0, out=No
 def nvfp4_mx_gemm(a, b, out_dtype=torch.bfloat16, out=None, stream=None):
     """c = a^ b^T over MXFP4 operands (see nvfp4_mx_gemm in nvfp4.h)."""
     M, N = a.rows, b.rows
+    _check_operand(a, "a")
+    _check_operand(b, "b")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
-    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
-        raise TypeError("output must be float32 or bfloat16 with a contiguous last dimension")
+    _check_gemm_out(out, (M, N), a.codes.device)
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     da, db = a.descriptor(), b.descriptor()
     st = load_library().nvfp4_mx_gemm(ctypes.byref(da), ctypes.byref(db), _ptr(out),
@@ -324,11 +416,14 @@ def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None, fp8
     fp8_blocks=True runs the second datapath (nvfp4_gemm_fp8blk)."""
     M = a.rows
     N = b.cols if pass_ == DGRAD else b.rows
+    _check_operand(a, "a")
+    _check_operand(b, "b")
+    if pass_ == DGRAD:
+        _check_nvfp4_buffers(b, b.rows, b.cols, b.block, a.codes.device, True, "b")
     if out is None:
         out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    _check_gemm_out(out, (M, N), a.codes.device)
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
-    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
-        raise TypeError("output must be float32 or bfloat16 with a contiguous last dimension")
     da, db = a.descriptor(), b.descriptor()
     fn = load_library().nvfp4_gemm_fp8blk if fp8_blocks else load_library().nvfp4_gemm
     st = fn(pass_, ctypes.byref(da), ctypes.byref(db), _ptr(out), out.stride(0), dt,
@@ -348,10 +443,15 @@ def nvfp4_gemm_amax(pass_, a, b, sign_mask=0, rht=True, out=None, amax=None, ama
     M = a.rows
     N = b.cols if pass_ == DGRAD else b.rows
     dev = a.codes.device
+    _check_operand(a, "a")
+    _check_operand(b, "b")
+    if pass_ == DGRAD:
+        _check_nvfp4_buffers(b, b.rows, b.cols, b.block, dev, True, "b")
     if out is None:
         out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
-    if out.dtype != torch.bfloat16 or out.stride(1) != 1:
-        raise TypeError("output must be bfloat16 with a contiguous last dimension")
+    _check_gemm_out(out, (M, N), dev, (torch.bfloat16,))
+    _check_scalar_out(amax, "amax", dev)
+    _check_scalar_out(amax_rht if rht else None, "amax_rht", dev)
     if amax is None:
         amax = torch.empty(1, dtype=torch.float32, device=dev)
     if rht and amax_rht is None:
@@ -388,8 +488,9 @@ def nvfp4_bf16_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None
         raise ValueError(f"unknown pass {pass_}")
     if out is None:
         out = torch.empty(shape, dtype=out_dtype, device=a.device)
-    if out.dtype not in (torch.float32, torch.bfloat16) or out.stride(1) != 1:
-        raise TypeError("output must be float32 or bfloat16 with a contiguous last dimension")
+    _check_gemm_out(out, shape, a.device)
+    if not _same_device(b.device, a.device):
+        raise ValueError(f"b: on {b.device}, expected {a.device}")
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     def ld(t):  # a matrix without columns has no meaningful row stride
         return t.stride(0) if t.shape[1] > 0 else 0
@@ -407,6 +508,8 @@ def nvfp4_amax(x, sign_mask=None, amax=None, amax_rht=None, stream=None):
     """
     _check_bf16(x)
     rows, cols = x.shape
+    _check_scalar_out(amax, "amax", x.device)
+    _check_scalar_out(amax_rht if sign_mask is not None else None, "amax_rht", x.device)
     amax = amax if amax is not None else torch.empty(1, dtype=torch.float32, device=x.device)
     if sign_mask is not None and amax_rht is None:
         amax_rht = torch.empty(1, dtype=torch.float32, device=x.device)

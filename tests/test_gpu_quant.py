@@ -262,3 +262,27 @@ def test_fused_amax_matches_quantisers(env, shape):
         g1 = q.nvfp4_quantize(xd, q.BLOCK_1X16, q.SR, 4, amax_in=a)
         torch.cuda.synchronize()
         assert_same_quant(g1, o1, f"1x16 with fused amax {shape}")
+
+
+def test_binding_rejects_undersized_buffers_before_launch(env):
+    # A 16x16-block buffer (rows/16 scale rows) reused for a 1x16 quantise, a
+    # GEMM output of the wrong shape: the binding raises and nothing is written.
+    torch, oracle, q, wl, dev = env
+    rng = np.random.default_rng(90)
+    x = to_dev(wl.normal(rng, (64, 96), 1.0), dev)
+    print("binding buffer checks", flush=True)
+    out2d = q.alloc_nvfp4(64, 96, q.BLOCK_16X16, False, dev)
+    out2d.scales.fill_(0xAB)
+    with pytest.raises(ValueError):
+        q.nvfp4_quantize(x, q.BLOCK_1X16, q.RNE, out=out2d)
+    torch.cuda.synchronize()
+    assert (out2d.scales == 0xAB).all().item()
+    gx = q.nvfp4_quantize(x)
+    gw = q.nvfp4_quantize(to_dev(wl.normal(rng, (32, 96), 0.02), dev), q.BLOCK_16X16)
+    bad = torch.full((64, 31), 7.0, dtype=torch.float32, device=dev)
+    with pytest.raises(ValueError):
+        q.nvfp4_gemm(q.FPROP, gx, gw, out=bad)
+    with pytest.raises(ValueError):  # dgrad needs the transposed weight copy
+        q.nvfp4_gemm(q.DGRAD, q.nvfp4_quantize(to_dev(wl.normal(rng, (64, 32), 1.0), dev)), gw)
+    torch.cuda.synchronize()
+    assert (bad == 7.0).all().item()
