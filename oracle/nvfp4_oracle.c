@@ -758,7 +758,14 @@ int orc_mx_quantize(const uint16_t* x, int64_t rows, int64_t cols, int mode, uin
  * operands, both stored rows x K with 16-element blocks along K.  Each
  * 16-block partial is exact (integer sum of products of doubled E2M1 values,
  * times two E4M3 scales); the partials are added in fp32 in block order and
- * the sum is multiplied by alpha = (1/s_enc_A) * (1/s_enc_B).  The reference
+ * the sum is multiplied by alpha = (1/s_enc_A) * (1/s_enc_B), the product of
+ * the two FP32 tensor decode scales ("Pretraining Large Language Models with
+ * NVFP4", Technische Zusammenfassung 2.A: one FP32 scale per tensor).  That
+ * product is formed in fp32 while it is a normal number; below fp32's normal
+ * range (tiny tensor maxima) its significand (the rounded product of the two
+ * factors' significands) and its exponent are kept apart, and the output is
+ * ldexp(RN(acc * significand), exponent) -- the value of RN(acc * alpha)
+ * with alpha held to 24 significant bits instead of a subnormal.  The reference
  * GEMM used by the parity tests is the fp64 product of the dequantised
  * matrices; this fp32 variant only bounds how far an fp32-accumulating GEMM
  * may sit from it.
@@ -771,7 +778,15 @@ int orc_gemm_fp32(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_r
 {
     if (M < 0 || N < 0 || K < 0 || K % 16 != 0) return ORC_ERR_SHAPE;
     int64_t nb = K / 16;
-    float alpha = (1.0f / a_s_enc) * (1.0f / b_s_enc);
+    float da = 1.0f / a_s_enc, db = 1.0f / b_s_enc;
+    float alpha = da * db;
+    int alpha_exp = 0;
+    if (!(alpha >= FLT_MIN)) {
+        int ea, eb;
+        float ma = frexpf(da, &ea), mb = frexpf(db, &eb);
+        alpha = ma * mb;
+        alpha_exp = ea + eb;
+    }
 #pragma omp parallel for schedule(static)
     for (int64_t m = 0; m < M; ++m)
         for (int64_t n = 0; n < N; ++n) {
@@ -789,7 +804,8 @@ int orc_gemm_fp32(const uint8_t* a_codes, const uint8_t* a_scales, int a_scale_r
                 float term = ((float)P * 0.25f * SA) * SB;
                 acc += term;
             }
-            c[m * N + n] = acc * alpha;
+            float out = acc * alpha;
+            c[m * N + n] = alpha_exp ? ldexpf(out, alpha_exp) : out;
         }
     return ORC_OK;
 }

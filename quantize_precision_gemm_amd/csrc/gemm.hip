@@ -23,7 +23,8 @@
 // the hardware converts a byte of two codes to an fp16 pair, and one packed
 // fp16 multiply applies the block scale.  The fp16 MFMA accumulates exact
 // products in fp32, and the epilogue multiplies by
-// alpha = (1/s_enc_a) (1/s_enc_b).  The A tile (shared by 4 waves) is
+// alpha = (1/s_enc_a) (1/s_enc_b), kept apart from its exponent when it falls
+// below fp32's normal range (output_scale).  The A tile (shared by 4 waves) is
 // decoded once per workgroup into fp16 LDS rows; the B tile (shared by 2
 // waves) stays raw in LDS -- 48 bytes per row instead of 144 -- and each
 // wave decodes its own B fragments after reading them, trading a little
@@ -483,7 +484,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
         compute((int)(nfull & 1));
     }
 
-    const float alpha = (1.0f / *A.s_enc) * (1.0f / *B.s_enc);
+    float alpha;
+    int alpha_exp;
+    output_scale(*A.s_enc, *B.s_enc, alpha, alpha_exp);
+    if (alpha_exp != 0) {  // (uniform) output scale below fp32's normal range
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) acc[i][j][e] = __builtin_ldexpf(acc[i][j][e] * alpha, alpha_exp);
+        alpha = 1.0f;
+    }
     __syncthreads();  // every wave is done reading the operand stages
     store_tile<kOutF32, kAmax>(acc, alpha, reinterpret_cast<float*>(lds) + wave * 32 * kEpiStride,
                                tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c, ldc,

@@ -200,7 +200,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fp8blk(GemmOperand A, GemmOpera
         __syncthreads();
     }
 
-    float alpha = (1.0f / *A.s_enc) * (1.0f / *B.s_enc);
+    float alpha;
+    int alpha_exp;  // alpha * 2^alpha_exp is the output scale (output_scale)
+    output_scale(*A.s_enc, *B.s_enc, alpha, alpha_exp);
 #pragma unroll
     for (int tm = 0; tm < 2; ++tm)
 #pragma unroll
@@ -210,7 +212,8 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fp8blk(GemmOperand A, GemmOpera
             for (int e = 0; e < 16; ++e) {
                 const int64_t row = tile_m * kT + wm * 64 + 32 * tm + (e >> 2) * 8 + g * 4 + (e & 3);
                 if (row < M && col < N) {
-                    const float v = acc[tm][tn][e] * alpha;
+                    float v = acc[tm][tn][e] * alpha;
+                    if (alpha_exp != 0) v = __builtin_ldexpf(v, alpha_exp);
                     if constexpr (kOutF32)
                         static_cast<float*>(c)[row * ldc + col] = v;
                     else

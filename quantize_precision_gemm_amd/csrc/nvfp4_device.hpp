@@ -34,6 +34,29 @@ __device__ __forceinline__ uint32_t bf16_absmax2(uint32_t w)
     return max(w & 0x7FFFu, (w >> 16) & 0x7FFFu);
 }
 
+// The output scale of a GEMM over two NVFP4 operands: the product of their
+// FP32 tensor decode scales d = 1 / s_enc (format: FP32 per-tensor scale).
+// The product is returned as am * 2^e: when d_a * d_b is a normal fp32
+// number, am is that product and e = 0; below fp32's normal range (both
+// tensor maxima tiny, amax_a * amax_b < ~8.5e-32) am is the rounded product
+// of the two significands and e the sum of the exponents, so that
+// out = ldexp(acc * am, e) keeps 24 significant bits wherever the output
+// itself is a normal number.  A single fp32 product would be subnormal there
+// and lose precision (or reach zero) although every factor and every output
+// is normal.
+__device__ __forceinline__ void output_scale(float s_enc_a, float s_enc_b, float& am, int& e)
+{
+    const float da = 1.0f / s_enc_a, db = 1.0f / s_enc_b;
+    am = da * db;
+    e = 0;
+    if (!(am >= 1.17549435e-38f)) {  // below FLT_MIN: keep the exponent apart
+        int ea, eb;
+        const float ma = __builtin_frexpf(da, &ea), mb = __builtin_frexpf(db, &eb);
+        am = ma * mb;  // in [0.25, 1): normal
+        e = ea + eb;
+    }
+}
+
 // Tensor encode scale: 2688 / amax (2688 = 6 * 448 maps the tensor amax to
 // the largest E2M1 value under the largest E4M3 scale); 1 for amax = 0,
 // FLT_MAX when the quotient overflows.

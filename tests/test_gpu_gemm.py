@@ -213,3 +213,61 @@ def test_padded_leading_dimensions(env, fp8):
     assert rel_fro(g32, want) <= TOL
     b16 = outs[torch.bfloat16].view(torch.int16).cpu().numpy().view(np.uint16)
     np.testing.assert_array_equal(b16, bf16_rne_bits(g32))
+
+
+def _scaled(wl, bits, f):
+    return wl.f32_to_bf16_bits((wl.bf16_bits_to_f32(bits).astype(np.float64) * f).astype(np.float32))
+
+
+# Extreme tensor scales (two-level scaling edges): (a factor, b factor).
+# 1e-17 / 2e-18: the product of the FP32 decode scales falls below fp32's
+# normal range while every output is normal; 1e-36: the tensor scale of A
+# saturates at FLT_MAX (amax < 2688 / FLT_MAX); 0: A all zeros (s_enc = 1);
+# 1e30 / 1e-30: a large and a small tensor scale.
+EXTREME = {"both 1e-17": (1e-17, 1e-17 / 0.02), "both 2e-18": (2e-18, 2e-18 / 0.02),
+           "a at FLT_MAX scale": (1e-36, 1.0 / 0.02), "a zero": (0.0, 1.0),
+           "large and small": (1e30, 1e-30 / 0.02)}
+
+
+@pytest.mark.parametrize("case", list(EXTREME))
+@pytest.mark.parametrize("pass_name", ["fprop", "dgrad", "wgrad"])
+def test_extreme_tensor_scales(env, case, pass_name):
+    # Both datapaths within 1e-5 of the fp64 oracle (bf16 output = RNE of the
+    # fp32 output), and the FP8-per-block datapath equal to the oracle's fp32
+    # block GEMM bit for bit, at the edges of the tensor scale.
+    torch, oracle, q, wl, dev = env
+    fa, fb = EXTREME[case]
+    M, K, N = 96, 272, 80
+    rng = np.random.default_rng(123)
+    print(f"extreme scales {case} {pass_name}", flush=True)
+    if pass_name == "fprop":
+        a = _scaled(wl, wl.normal(rng, (M, K), 1.0), fa)
+        w = _scaled(wl, wl.normal(rng, (N, K), 0.02), fb)
+        ga, gb = q.nvfp4_quantize(to_dev(a, dev)), q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, with_transpose=True)
+        oa, ob = oracle.quantize(a), oracle.quantize(w, oracle.BLOCK_16X16)
+        want, ob_rows, pass_ = oracle.gemm(oracle.FPROP, oa, ob), ob, q.FPROP
+    elif pass_name == "dgrad":
+        a = _scaled(wl, wl.lognormal_rows(rng, (M, N), base=1.0, sigma=0.5), fa)
+        w = _scaled(wl, wl.normal(rng, (N, K), 0.02), fb)
+        ga = q.nvfp4_quantize(to_dev(a, dev), q.BLOCK_1X16, q.SR, 7)
+        gb = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, with_transpose=True)
+        oa, ob = oracle.quantize(a, oracle.BLOCK_1X16, oracle.SR, 7), oracle.quantize(w, oracle.BLOCK_16X16)
+        want, pass_ = oracle.gemm(oracle.DGRAD, oa, ob), q.DGRAD
+        ob_rows = oracle.quantize(np.ascontiguousarray(w.T), oracle.BLOCK_16X16)
+    else:
+        dy = _scaled(wl, wl.lognormal_rows(rng, (K, M), base=1.0, sigma=0.5), fa)
+        x = _scaled(wl, wl.normal(rng, (K, N), 0.02), fb)
+        mask = q.nvfp4_rht_sign_mask(K)
+        ga, gb = q.nvfp4_rht_quantize(to_dev(dy, dev), mask, q.SR, 9), q.nvfp4_rht_quantize(to_dev(x, dev), mask)
+        oa, ob = oracle.rht_quantize(dy, mask, oracle.SR, 9), oracle.rht_quantize(x, mask)
+        want, ob_rows, pass_ = oracle.gemm(oracle.WGRAD, oa, ob), ob, q.WGRAD
+    if fa == 1e-36:
+        assert np.float32(oa.s_enc) == np.finfo(np.float32).max  # the clamp is exercised
+    if fa != 0.0:  # most outputs are normal fp32 numbers (cancellation may leave a few tiny)
+        assert np.median(np.abs(want)) > 1e-36
+    _check_both_dtypes(torch, q, pass_, ga, gb, want)
+    y = q.nvfp4_gemm(pass_, ga, gb, torch.float32, fp8_blocks=True)
+    torch.cuda.synchronize()
+    got, ref = y.cpu().numpy(), oracle.gemm_fp32_blocks(oa, ob_rows)
+    bad = np.argwhere(got.view(np.uint32) != ref.view(np.uint32))
+    assert len(bad) == 0, f"{len(bad)} outputs differ, first {bad[0]}: {got[tuple(bad[0])]} vs {ref[tuple(bad[0])]}"

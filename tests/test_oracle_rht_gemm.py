@@ -293,3 +293,34 @@ def test_bf16_gemm_sampled_rows_match_full(pass_):
     full = oracle.bf16_gemm(pass_, a, b)
     rows = np.array([0, 3, full.shape[0] - 1])
     np.testing.assert_array_equal(oracle.bf16_gemm(pass_, a, b, rows=rows), full[rows])
+
+
+def _scaled_bits(u16, k):
+    """bf16 bit patterns times 2^k (exact: exponent field shift, no under/overflow here)."""
+    return wl.f32_to_bf16_bits((wl.bf16_bits_to_f32(u16).astype(np.float64) * 2.0 ** k).astype(np.float32))
+
+
+@pytest.mark.parametrize("k", [-40, -52, -55])
+def test_gemm_fp32_output_scale_below_normal_range(k):
+    # Both operands times 2^k: codes and scales stay (I-5), each tensor scale
+    # gains 2^-k, so the product of the two FP32 decode scales loses 2^2k and,
+    # for k = -52 / -55, falls below fp32's normal range (amax product <
+    # ~8.5e-32) while every output stays a normal number.  The fp32 block
+    # GEMM's output is then exactly the unscaled output times 2^2k, and within
+    # 1e-6 of the fp64 reference.
+    rng = np.random.default_rng(41)
+    x = wl.normal(rng, (8, 64), 1.0)
+    w = wl.normal(rng, (16, 64), 0.02)
+    a, b = oracle.quantize(x), oracle.quantize(w, oracle.BLOCK_16X16)
+    a2, b2 = oracle.quantize(_scaled_bits(x, k)), oracle.quantize(_scaled_bits(w, k), oracle.BLOCK_16X16)
+    np.testing.assert_array_equal(a2.codes, a.codes)
+    np.testing.assert_array_equal(b2.scales, b.scales)
+    alpha32 = np.float32(np.float32(1) / a2.s_enc) * np.float32(np.float32(1) / b2.s_enc)
+    if k <= -52:
+        assert alpha32 < np.finfo(np.float32).tiny  # the case is exercised
+    base = oracle.gemm_fp32_blocks(a, b).astype(np.float64)
+    got = oracle.gemm_fp32_blocks(a2, b2).astype(np.float64)
+    assert np.all(np.abs(got[got != 0]) >= np.finfo(np.float32).tiny)
+    np.testing.assert_array_equal(got, base * 2.0 ** (2 * k))
+    ref = oracle.gemm(oracle.FPROP, a2, b2)
+    assert np.linalg.norm(got - ref) / np.linalg.norm(ref) < 1e-6
