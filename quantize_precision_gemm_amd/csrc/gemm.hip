@@ -80,9 +80,10 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 // This workgroup's output tile.  Workgroups are dealt round-robin to the 8
 // XCDs; renumbering gives each XCD a contiguous range, walked in groups of 8
 // tile rows, column by column.
+template <int kTM = kBM>
 __device__ __forceinline__ void tile_of(int64_t M, int64_t N, int64_t& tile_m, int64_t& tile_n)
 {
-    const int64_t tiles_m = (M + kBM - 1) / kBM, tiles_n = (N + kBN - 1) / kBN;
+    const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kBN - 1) / kBN;
     const int64_t T = tiles_m * tiles_n;
     const int64_t hw = blockIdx.x;
     const int64_t L = (T % 8 == 0) ? (hw % 8) * (T / 8) + hw / 8 : hw;
@@ -310,68 +311,93 @@ __device__ __forceinline__ half8_t decode8(uint32_t w, half2_t S)
 // ---------------------------------------------------------------------------
 
 constexpr int kBRow = 48;
-constexpr int kAOp = kOpBytes;
 constexpr int kBOp = 256 * kBRow;
-constexpr int kStage = kAOp + kBOp + 256 * 4;
 
-struct NvRow {      // one thread's share of a K step
-    uint4 ca, cb;   // 16 code bytes of its A and B half rows
-    uint32_t sa, sb;  // its 2 A and 2 B scale bytes, as loaded
+// LDS bytes of one stage of a tile with kTM rows of A: A decoded (kTM x
+// 144 B), B raw (256 x 48 B), B scales (256 x 4 B).
+template <int kTM>
+constexpr int nv_stage_bytes() { return kTM * kRowBytes + kBOp + 256 * 4; }
+
+// One thread's share of a K step: half an A row, and kRB half B rows
+// (kRB = 1 for 256-row tiles of 512 threads, 2 for 128-row tiles of 256).
+template <int kRB>
+struct NvRow {
+    uint4 ca, cb[kRB];      // 16 code bytes of its A and B half rows
+    uint32_t sa, sb[kRB];   // its 2 A and 2 B scale bytes per half row, as loaded
 };
 
 }  // namespace
 
-template <bool kOutF32, int kAmax = 0>
-__global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t M, int64_t N,
+// kTM = 256: 8 waves (2 x 4, each a 128 x 64 slab), one workgroup per CU.
+// kTM = 128: 4 waves (1 x 4), 62 KB of LDS, two workgroups per CU -- their
+// phases drift apart, so one workgroup's stores, barriers and epilogue run
+// while the other's waves issue MFMAs.
+template <int kTM, bool kOutF32, int kAmax = 0>
+__global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs B, int64_t M, int64_t N,
                                                     int64_t K, void* __restrict__ c, int64_t ldc,
                                                     uint32_t* amax_bits = nullptr,
                                                     uint32_t* amax_rht_bits = nullptr,
                                                     uint32_t mask = 0u)
 {
+    constexpr int kRB = 256 / kTM;
+    constexpr int kAOp = kTM * kRowBytes;
+    constexpr int kStage = nv_stage_bytes<kTM>();
+    static_assert((2 * kTM / 64) * 32 * kEpiStride * 4 <= 2 * kStage, "epilogue rows fit the stages");
     __shared__ __attribute__((aligned(16))) uint8_t lds[2 * kStage];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, lr = lane & 31;
     int64_t tile_m, tile_n;
-    tile_of(M, N, tile_m, tile_n);
+    tile_of<kTM>(M, N, tile_m, tile_n);
 
-    // half h of tile row `row` (rows past the operand re-read its last row;
-    // they are never stored)
+    // half h of tile row `row` of A and of tile rows row + kTM j of B (rows
+    // past the operand re-read its last row; they are never stored)
     const int row = tid >> 1, h = tid & 1;
-    int64_t ra = tile_m * kBM + row, rb = tile_n * kBN + row;
+    int64_t ra = tile_m * kTM + row;
     ra = ra < M ? ra : M - 1;
-    rb = rb < N ? rb : N - 1;
     const uint8_t* pa = static_cast<const uint8_t*>(A.data) + ra * A.ld + 16 * h;
-    const uint8_t* pb = static_cast<const uint8_t*>(B.data) + rb * B.ld + 16 * h;
     const uint8_t* psa = A.scales + (ra >> A.scale_shift) * A.ld_scales + 2 * h;
-    const uint8_t* psb = B.scales + (rb >> B.scale_shift) * B.ld_scales + 2 * h;
+    const uint8_t* pb[kRB];
+    const uint8_t* psb[kRB];
+#pragma unroll
+    for (int j = 0; j < kRB; ++j) {
+        int64_t rb = tile_n * kBN + row + kTM * j;
+        rb = rb < N ? rb : N - 1;
+        pb[j] = static_cast<const uint8_t*>(B.data) + rb * B.ld + 16 * h;
+        psb[j] = B.scales + (rb >> B.scale_shift) * B.ld_scales + 2 * h;
+    }
     const int64_t nblk = K >> 4;
 
-    auto load_full = [&](int64_t k0, NvRow& w) {
+    auto load_full = [&](int64_t k0, NvRow<kRB>& w) {
         w.ca = *reinterpret_cast<const uint4*>(pa + (k0 >> 1));
-        w.cb = *reinterpret_cast<const uint4*>(pb + (k0 >> 1));
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) w.cb[j] = *reinterpret_cast<const uint4*>(pb[j] + (k0 >> 1));
         w.sa = *reinterpret_cast<const uint16_t*>(psa + (k0 >> 4));
-        w.sb = *reinterpret_cast<const uint16_t*>(psb + (k0 >> 4));
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) w.sb[j] = *reinterpret_cast<const uint16_t*>(psb[j] + (k0 >> 4));
     };
     // partial last step: blocks past K get zero scales, so their codes decode
     // to zero (the 16 code bytes of a half row with one valid block still lie
     // inside the row, whose length is rounded up to 32 codes)
-    auto load_tail = [&](int64_t k0, NvRow& w) {
+    auto load_tail = [&](int64_t k0, NvRow<kRB>& w) {
         const int64_t b0 = (k0 >> 4) + 2 * h;
         w.ca = b0 < nblk ? *reinterpret_cast<const uint4*>(pa + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
-        w.cb = b0 < nblk ? *reinterpret_cast<const uint4*>(pb + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
-        uint32_t sa = 0u, sb = 0u;
-        for (int j = 0; j < 2; ++j)
-            if (b0 + j < nblk) {
-                sa |= (uint32_t)psa[(k0 >> 4) + j] << (8 * j);
-                sb |= (uint32_t)psb[(k0 >> 4) + j] << (8 * j);
-            }
+        uint32_t sa = 0u;
+        for (int i = 0; i < 2; ++i)
+            if (b0 + i < nblk) sa |= (uint32_t)psa[(k0 >> 4) + i] << (8 * i);
         w.sa = sa;
-        w.sb = sb;
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) {
+            w.cb[j] = b0 < nblk ? *reinterpret_cast<const uint4*>(pb[j] + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
+            uint32_t sb = 0u;
+            for (int i = 0; i < 2; ++i)
+                if (b0 + i < nblk) sb |= (uint32_t)psb[j][(k0 >> 4) + i] << (8 * i);
+            w.sb[j] = sb;
+        }
     };
-    // A half row decoded to fp16 q * S in natural k order; B half row stored raw
-    auto put = [&](const NvRow& w, int st) {
+    // A half row decoded to fp16 q * S in natural k order; B half rows stored raw
+    auto put = [&](const NvRow<kRB>& w, int st) {
         uint8_t* base = lds + st * kStage;
         const half2_t pair = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.sa, 1.0f, false);
         const half2_t S0 = __builtin_shufflevector(pair, pair, 0, 0);
@@ -381,8 +407,11 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
         for (int d = 0; d < 4; ++d)  // dword d: k 32h + 8d .. +7, block 2h + d/2
             *reinterpret_cast<half8_t*>(base + row * kRowBytes + 64 * h + 16 * d) =
                 decode8(cw[d], d < 2 ? S0 : S1);
-        *reinterpret_cast<uint4*>(base + kAOp + row * kBRow + 16 * h) = w.cb;
-        *reinterpret_cast<uint16_t*>(base + kAOp + kBOp + row * 4 + 2 * h) = (uint16_t)w.sb;
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) {
+            *reinterpret_cast<uint4*>(base + kAOp + (row + kTM * j) * kBRow + 16 * h) = w.cb[j];
+            *reinterpret_cast<uint16_t*>(base + kAOp + kBOp + (row + kTM * j) * 4 + 2 * h) = (uint16_t)w.sb[j];
+        }
     };
 
     float16_t acc[4][2];
@@ -449,7 +478,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
     const int64_t nsteps = (K + kKS - 1) / kKS;
     const int64_t nfull = K / kKS;
     int64_t s = 0;
-    NvRow g0, g1, g2;
+    NvRow<kRB> g0, g1, g2;
     if (nfull > 0) {
         load_full(0, g0);
         load_full((nfull > 1 ? 1 : 0) * kKS, g1);
@@ -460,8 +489,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
     auto step = [&](auto c3, int64_t t) {
         constexpr int r = decltype(c3)::value;
         const int st = (int)(t & 1);
-        NvRow& done = r == 0 ? g0 : (r == 1 ? g1 : g2);  // step t, already in LDS
-        NvRow& next = r == 0 ? g1 : (r == 1 ? g2 : g0);  // step t + 1
+        NvRow<kRB>& done = r == 0 ? g0 : (r == 1 ? g1 : g2);  // step t, already in LDS
+        NvRow<kRB>& next = r == 0 ? g1 : (r == 1 ? g2 : g0);  // step t + 1
         load_full((t + 3 < nfull ? t + 3 : nfull - 1) * kKS, done);
         compute(st);
         put(next, st ^ 1);  // past the last full step: harmless, never read
@@ -498,7 +527,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_nv(OpArgs A, OpArgs B, int64_t 
     }
     __syncthreads();  // every wave is done reading the operand stages
     store_tile<kOutF32, kAmax>(acc, alpha, reinterpret_cast<float*>(lds) + wave * 32 * kEpiStride,
-                               tile_m * kBM + wm * 128, tile_n * kBN + wn * 64, M, N, c, ldc,
+                               tile_m * kTM + wm * 128, tile_n * kBN + wn * 64, M, N, c, ldc,
                                amax_bits, amax_rht_bits, mask);
 }
 
@@ -1021,10 +1050,16 @@ static void launch_fill_zero(int64_t M, int64_t N, void* c, int64_t ldc, bool ou
         hipLaunchKernelGGL(k_fill_zero<false>, g, dim3(256), 0, s, c, ldc, M, N);
 }
 
-static dim3 tile_grid(int64_t M, int64_t N)
+static dim3 tile_grid(int64_t M, int64_t N, int64_t tm = kBM)
 {
-    return dim3((unsigned)(((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN)));
+    return dim3((unsigned)(((M + tm - 1) / tm) * ((N + kBN - 1) / kBN)));
 }
+
+// Tile height of the NVFP4 GEMM (256: one workgroup per CU; 128: two).
+#ifndef NVFP4_GEMM_TM
+#define NVFP4_GEMM_TM 256
+#endif
+constexpr int kNvTM = NVFP4_GEMM_TM;
 
 void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N, int64_t K,
                     void* c, int64_t ldc, bool out_fp32, hipStream_t s)
@@ -1033,10 +1068,11 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
     if (K == 0) return launch_fill_zero(M, N, c, ldc, out_fp32, s);
     const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc};
     const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc};
+    const dim3 grid = tile_grid(M, N, kNvTM), block(2 * kNvTM);
     if (out_fp32)
-        hipLaunchKernelGGL(k_gemm_nv<true>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
+        hipLaunchKernelGGL((k_gemm_nv<kNvTM, true>), grid, block, 0, s, A, B, M, N, K, c, ldc);
     else
-        hipLaunchKernelGGL(k_gemm_nv<false>, tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K, c, ldc);
+        hipLaunchKernelGGL((k_gemm_nv<kNvTM, false>), grid, block, 0, s, A, B, M, N, K, c, ldc);
 }
 
 // Zeroes the output maxima (a kernel, not a memset, so the sequence can be
@@ -1058,11 +1094,12 @@ void launch_gemm_nt_amax(const GemmOperand& a, const GemmOperand& b, int64_t M, 
     if (K == 0) return launch_fill_zero(M, N, c, ldc, false, s);  // maxima stay 0
     const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc};
     const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc};
+    const dim3 grid = tile_grid(M, N, kNvTM), block(2 * kNvTM);
     if (rb)
-        hipLaunchKernelGGL((k_gemm_nv<false, 2>), tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K,
+        hipLaunchKernelGGL((k_gemm_nv<kNvTM, false, 2>), grid, block, 0, s, A, B, M, N, K,
                            static_cast<void*>(c), ldc, ab, rb, mask);
     else
-        hipLaunchKernelGGL((k_gemm_nv<false, 1>), tile_grid(M, N), dim3(512), 0, s, A, B, M, N, K,
+        hipLaunchKernelGGL((k_gemm_nv<kNvTM, false, 1>), grid, block, 0, s, A, B, M, N, K,
                            static_cast<void*>(c), ldc, ab, rb, mask);
 }
 

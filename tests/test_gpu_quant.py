@@ -231,8 +231,14 @@ def test_error_paths(env):
     w = q.nvfp4_quantize(torch.zeros((16, 32), dtype=torch.bfloat16, device=dev), q.BLOCK_16X16, q.RNE)
     with pytest.raises(RuntimeError, match="status -5"):
         q.nvfp4_gemm(q.FPROP, a, w)                           # K mismatch 48 vs 32
-    with pytest.raises(RuntimeError, match="status -1"):
-        q.nvfp4_gemm(q.DGRAD, a, w)                           # no transposed copy
+    with pytest.raises(ValueError, match="transposed copy"):
+        q.nvfp4_gemm(q.DGRAD, a, w)                           # no transposed copy: the binding
+    import ctypes                                             # ... and the C ABI (-1) refuse it
+    c = torch.empty((32, 32), dtype=torch.bfloat16, device=dev)
+    da, dw = a.descriptor(), w.descriptor()
+    st = q.load_library().nvfp4_gemm(q.DGRAD, ctypes.byref(da), ctypes.byref(dw), c.data_ptr(), 32,
+                                     q.OUT_BF16, torch.cuda.current_stream().cuda_stream)
+    assert st == -1
     torch.cuda.synchronize()
 
 
