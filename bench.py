@@ -291,6 +291,119 @@ def rht_size_study(q, torch, dev, reps=3, rows=40):
             "results": out, "fprop_dgrad_rht": fd}
 
 
+def quantize_cold(q, torch, layer, reps=20):
+    """Each quantisation pass of the layer timed cold: before every rep a
+    1 GiB buffer is written (more than the 256 MB Infinity Cache and the L2s
+    hold), so the pass reads its tensor from HBM.  Events bracket the single
+    launch sequence of the pass on the current stream; median over `reps`.
+
+    kernel_gbps: algorithmic bytes of the pass / its time.
+    op_gbps: the whole quantisation (its amax pass plus its encode pass, both
+    cold) -- 2 B/element for the amax read plus the encode pass's bytes --
+    over the sum of the two times; the headline against the 70 % target.
+    W is reported with the transposed copy the dgrad GEMM reads (the bytes
+    this library moves) and on the plain 16x16 quantisation's bytes (one
+    read for the amax, one read, codes and scales written once)."""
+    dev = layer.x.device
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    aw = torch.empty(1, dtype=torch.float32, device=dev)
+    e_x, e_w, e_dy = layer.M * layer.K, layer.N * layer.K, layer.M * layer.N
+    enc = lambda e: 2 * e + e // 2 + e // 16
+    passes = {
+        "amax_X (plain + RHT maxima)": (lambda: q.nvfp4_amax(layer.x, layer.mask, layer.ax, layer.ax_rht), 2 * e_x),
+        "quant_X (1x16 RNE)": (lambda: q.nvfp4_quantize(layer.x, q.BLOCK_1X16, q.RNE, amax_in=layer.ax,
+                                                        out=layer.gx), enc(e_x)),
+        "rht_X (RHT 1x16 RNE)": (lambda: q.nvfp4_rht_quantize(layer.x, layer.mask, q.RNE,
+                                                             amax_in=layer.ax_rht, out=layer.gxt), enc(e_x)),
+        "amax_W": (lambda: q.nvfp4_amax(layer.w, None, aw), 2 * e_w),
+        "quant_W (16x16 RNE + transposed copy)": (
+            lambda: q.nvfp4_quantize(layer.w, q.BLOCK_16X16, q.RNE, amax_in=aw, out=layer.gw),
+            2 * e_w + 2 * (e_w // 2 + e_w // 256)),
+        "amax_dY (plain + RHT maxima)": (lambda: q.nvfp4_amax(layer.dy, layer.mask, layer.ady, layer.ady_rht), 2 * e_dy),
+        "quant_dY (1x16 SR)": (lambda: q.nvfp4_quantize(layer.dy, q.BLOCK_1X16, q.SR, layer.seed + 100,
+                                                        amax_in=layer.ady, out=layer.gdy), enc(e_dy)),
+        "rht_dY (RHT 1x16 SR)": (lambda: q.nvfp4_rht_quantize(layer.dy, layer.mask, q.SR, layer.seed + 101,
+                                                             amax_in=layer.ady_rht, out=layer.gdyt), enc(e_dy)),
+    }
+    times = {k: [] for k in passes}
+    for _ in range(reps):
+        for k, (f, _) in passes.items():
+            flush.fill_(1)
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            times[k].append((a, b))
+    torch.cuda.synchronize()
+    med = {k: sorted(x.elapsed_time(y) for x, y in v)[len(v) // 2] for k, v in times.items()}
+    del flush
+    kern = {k: {"ms": round(med[k], 4), "gbps": round(passes[k][1] / (med[k] * 1e-3) / 1e9, 1),
+                "frac_of_hbm_peak": round(passes[k][1] / (med[k] * 1e-3) / 1e9 / PEAK_HBM_GBPS, 3)}
+            for k in passes}
+    ops = {  # op: (amax pass, encode pass, bytes of the whole op)
+        "X 1x16 RNE": ("amax_X (plain + RHT maxima)", "quant_X (1x16 RNE)", 2 * e_x + enc(e_x)),
+        "X RHT 1x16 RNE (wgrad)": ("amax_X (plain + RHT maxima)", "rht_X (RHT 1x16 RNE)", 2 * e_x + enc(e_x)),
+        "W 16x16 RNE + transposed copy": ("amax_W", "quant_W (16x16 RNE + transposed copy)",
+                                          2 * e_w + passes["quant_W (16x16 RNE + transposed copy)"][1]),
+        "W 16x16 RNE (bytes without the copy)": ("amax_W", "quant_W (16x16 RNE + transposed copy)",
+                                                 2 * e_w + 2 * e_w + e_w // 2 + e_w // 256),
+        "dY 1x16 SR": ("amax_dY (plain + RHT maxima)", "quant_dY (1x16 SR)", 2 * e_dy + enc(e_dy)),
+        "dY RHT 1x16 SR (wgrad)": ("amax_dY (plain + RHT maxima)", "rht_dY (RHT 1x16 SR)", 2 * e_dy + enc(e_dy)),
+    }
+    op = {}
+    for k, (pa, pe, nbytes) in ops.items():
+        t = med[pa] + med[pe]
+        gbps = nbytes / (t * 1e-3) / 1e9
+        op[k] = {"ms": round(t, 4), "gbps": round(gbps, 1), "frac_of_hbm_peak": round(gbps / PEAK_HBM_GBPS, 3)}
+    return {"method": f"cold: 1 GiB written before every rep; median of {reps} reps; events around "
+                      "each pass's launches", "kernel": kern, "op": op}
+
+
+def small_fprop_latency(q, torch, dev, reps=50):
+    """The 256 x 256 x 256 fprop (X N(0,1) with 0.1 % outliers x 50, W N(0,
+    0.02), seed 0): latency of each call and of the whole path (quantise X,
+    quantise W with its transposed copy, GEMM), median over `reps`.  Too small
+    for a roofline (33.5 MFLOP)."""
+    import numpy as np
+    from quantize_precision_gemm_amd import workloads as wl
+    X, W = wl.small_fprop(seed=0)
+    to_dev = lambda u: torch.from_numpy(u.view(np.int16)).to(dev).view(torch.bfloat16)
+    x, w = to_dev(X), to_dev(W)
+    gx = q.alloc_nvfp4(256, 256, q.BLOCK_1X16, device=dev)
+    gw = q.alloc_nvfp4(256, 256, q.BLOCK_16X16, with_transpose=True, device=dev)
+    y = torch.empty((256, 256), dtype=torch.bfloat16, device=dev)
+    steps = {"quant_X": lambda: q.nvfp4_quantize(x, q.BLOCK_1X16, q.RNE, out=gx),
+             "quant_W": lambda: q.nvfp4_quantize(w, q.BLOCK_16X16, q.RNE, out=gw),
+             "fprop": lambda: q.nvfp4_gemm(q.FPROP, gx, gw, out=y)}
+    steps["whole path"] = lambda: [f() for f in list(steps.values())[:3]]
+    for f in steps.values():
+        f()
+    torch.cuda.synchronize()
+    out = {}
+    for k, f in steps.items():
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            f()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        out[k] = round(sorted(a.elapsed_time(b) for a, b in ts)[reps // 2] * 1e3, 1)
+    return {"workload": "fprop 256 x 256 x 256 (X 1x16 RNE, W 16x16 RNE, bf16 out), seed 0",
+            "latency_us": out, "note": "median of %d event-timed calls each" % reps}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def copy_gbps(torch, dev, reps=5):
     """Device copy of 1 GiB of bf16 (read + write bytes / time), the measured
     stream rate the quantisers are also reported against."""
@@ -352,6 +465,7 @@ def cpu_baseline(data, tokens=M):
     flops = 3 * 2.0 * tokens * N * K
     threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
     return {"value": flops / t / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"{tokens} of {M} tokens through the whole step (all quantisations and "
                       f"the three GEMMs, fp64 numpy GEMM over dequantised operands); W "
                       f"quantised in full ({t_w:.2f} s) and counted at {tokens}/{M}; "
@@ -601,6 +715,8 @@ def main():
         result["quantize_frac_of_copy"] = {
             k: round(qb[k] / (avg[k] * 1e-3) / 1e9 / cgb, 3) for k in qb}
         result["ms_per_op"] = {k: round(v, 4) for k, v in avg.items()}
+        result["quantize_cold"] = quantize_cold(q, torch, step.layers[0])
+        result["config_256_fprop"] = small_fprop_latency(q, torch, dev)
     if mx is not None:
         mx["speedup_vs_nvfp4"] = {k: round(v / result["gemm_tflops"][k], 2)
                                   for k, v in mx["gemm_tflops"].items()}
@@ -620,6 +736,12 @@ def main():
         "timing": "HIP events around each fprop launch in the timed steps, on its stream",
         "dgrad_avg_launch_ms_concurrent": round(mean(live_dgrad), 4) if live_dgrad else None,
         "traffic": None if mlp else counter_traffic()}
+    # every pass of the kernel, each launch serialised (events after every op)
+    result["roofline"]["per_pass_serialised"] = {
+        n: {"ms": round(mean(by_name[n]), 4),
+            "achieved": round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12, 1),
+            "frac": round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
+        for n in ("fprop", "dgrad", "wgrad") if n in by_name}
     result["cpu_baseline"] = None
     if not args.no_cpu_baseline and not mlp:
         print("# timing the CPU oracle on a token slice", file=sys.stderr, flush=True)
