@@ -44,7 +44,9 @@ _lib = None
 
 
 def lib_path() -> str:
-    return os.path.join(_HERE, _LIB_NAME)
+    """libnvfp4.so next to this file, or the build named by NVFP4_LIB (the
+    host-sanitized build of the same sources, for the CPU checks)."""
+    return os.environ.get("NVFP4_LIB") or os.path.join(_HERE, _LIB_NAME)
 
 
 class _Desc(ctypes.Structure):

@@ -39,24 +39,40 @@ def _run(cmd, verbose):
         print(msg)
 
 
-def build(verbose: bool = False, jobs: int = 4) -> str:
-    os.makedirs(BUILD, exist_ok=True)
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build (the C ABI's
+# argument validation and dispatch; device code is built as usual, since GPU
+# sanitizers are not used here): each -fsanitize= applies to the host pass
+# only.  Selected at load time with NVFP4_LIB.
+LIB_SAN = os.path.join(HERE, "libnvfp4_san.so")
+SAN_FLAGS = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+             "-Xarch_host", "-fno-sanitize-recover=undefined", "-Xarch_host", "-fno-omit-frame-pointer",
+             "-Xarch_host", "-g"]
+
+
+def build(verbose: bool = False, jobs: int = 4, sanitize: bool = False) -> str:
+    bdir = BUILD + ("_san" if sanitize else "")
+    out = LIB_SAN if sanitize else LIB
+    os.makedirs(bdir, exist_ok=True)
     objs = []
     procs = []
     for src in SOURCES:
-        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC] + CFLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + CFLAGS + (SAN_FLAGS if sanitize else []) + ["-c", os.path.join(CSRC, src), "-o", obj]
         procs.append(cmd)
     # compile in parallel
     from concurrent.futures import ThreadPoolExecutor
     with ThreadPoolExecutor(max_workers=jobs) as ex:
         list(ex.map(lambda c: _run(c, verbose), procs))
-    tmp = LIB + ".tmp"
-    _run([HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs, verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    tmp = out + ".tmp"
+    link = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs
+    if sanitize:
+        link[1:1] = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                     "-shared-libasan"]
+    _run(link, verbose)
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose="-v" in sys.argv))
+    print(build(verbose="-v" in sys.argv, sanitize="--sanitize" in sys.argv))
