@@ -489,11 +489,12 @@ def as_mxfp4(q, torch, dev, step):
     return TrainingStep(torch, layers, dev)
 
 
-def with_schedule(q, torch, dev, step, fused_quant):
+def with_schedule(q, torch, dev, step, fused_quant, split_tail=False):
     """The same step over the same tensors, with the NVFP4 layers' quantisers
-    fused (nvfp4_quantize_dual) or separate."""
+    fused (nvfp4_quantize_dual) or separate, and dgrad / wgrad through
+    nvfp4_gemm_split (split_tail) or nvfp4_gemm."""
     from quantize_precision_gemm_amd.step import NVFP4Linear, TrainingStep
-    layers = [NVFP4Linear(q, torch, l.x, l.w, l.dy, l.seed, fused_quant)
+    layers = [NVFP4Linear(q, torch, l.x, l.w, l.dy, l.seed, fused_quant, split_tail)
               if isinstance(l, NVFP4Linear) else l for l in step.layers]
     return TrainingStep(torch, layers, dev)
 
@@ -600,6 +601,25 @@ def main():
     torch.cuda.synchronize()
     alt_ms = (time.perf_counter() - t0) * 1e3 / steps
 
+    # the step with dgrad and wgrad through nvfp4_gemm_split, timed the same way
+    spl = with_schedule(q, torch, dev, step, args.fused_quant, split_tail=True)
+    for _ in range(warmup):
+        spl.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        spl.run()
+    torch.cuda.synchronize()
+    split_ms = (time.perf_counter() - t0) * 1e3 / steps
+    split_ops = {}
+    for _ in range(max(3, steps // 2)):  # its GEMMs serialised, events around each
+        ops, ev = spl.run_timed_ops()
+        torch.cuda.synchronize()
+        for j, (i, name, _) in enumerate(ops):
+            if name in ("dgrad", "wgrad"):
+                split_ops.setdefault(name, []).append(ev[j].elapsed_time(ev[j + 1]))
+    del spl
+
     # the same step in the comparison format MXFP4, timed the same way
     mxs = as_mxfp4(q, torch, dev, step)
     for _ in range(warmup):
@@ -677,11 +697,14 @@ def main():
     names = ("separate quantisers", "dual quantisers (nvfp4_quantize_dual)")
     result["schedules_ms_per_step"] = {
         names[int(args.fused_quant)]: round(ms_step, 4),
-        names[int(not args.fused_quant)]: round(alt_ms, 4)}
+        names[int(not args.fused_quant)]: round(alt_ms, 4),
+        names[int(args.fused_quant)] + ", dgrad/wgrad tail split (nvfp4_gemm_split)": round(split_ms, 4)}
     gemm_names = [n for n in ("fprop", "dgrad", "wgrad", "bf16_fprop", "bf16_dgrad", "bf16_wgrad")
                   if n in by_name]
     result["gemm_tflops"] = {n: round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12, 1)
                              for n in gemm_names}
+    result["gemm_split_tflops"] = {
+        n: round(gemm_flop / (mean(v) * 1e-3) / 1e12, 1) for n, v in split_ops.items()}
     if datapaths is not None:
         result["gemm_datapaths_tflops"] = {
             "fp16_decode (nvfp4_gemm)": {n: result["gemm_tflops"][n] for n in datapaths},

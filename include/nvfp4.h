@@ -52,6 +52,7 @@ extern "C" {
 #define NVFP4_ERR_MODE (-4)     /* unknown block, rounding, pass or dtype */
 #define NVFP4_ERR_MISMATCH (-5) /* GEMM operands inconsistent with the pass */
 #define NVFP4_ERR_LAUNCH (-6)   /* the HIP runtime reported a launch error */
+#define NVFP4_ERR_WORKSPACE (-7) /* the workspace is missing or smaller than needed */
 
 /* Block layouts. */
 #define NVFP4_BLOCK_1X16 0      /* one scale per 16 consecutive elements of a row */
@@ -292,6 +293,44 @@ uint32_t nvfp4_rht_sign_mask(uint64_t seed);
  */
 int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
                int64_t ldc, int32_t c_dtype, void* stream);
+
+/*
+ * nvfp4_gemm_split -- nvfp4_gemm (the same passes, operands, output and
+ * validation) with the last wave of output tiles split along the
+ * contraction.  Defines: as nvfp4_gemm ("Pretraining Large Language Models
+ * with NVFP4", Technische Zusammenfassung 2.B.2, 2.B.3); the split is an
+ * order of the fp32 accumulation, which the method leaves free.
+ * The output is cut into 256 x 256 tiles, one per workgroup and compute unit.
+ * When the tile count is not a multiple of the compute units, the tiles of
+ * the last, partial wave are each computed in `split` parts over equal runs
+ * of 64-element K steps (split = min(CUs / leftover tiles, 8), each part at
+ * least 4 steps), the parts' fp32 sums go to the workspace, and a second
+ * kernel adds them in part order, applies alpha and writes c.  The result is
+ * deterministic; it may differ from nvfp4_gemm's in the last bits of the
+ * fp32 accumulation order (both are within the parity bar of the oracle),
+ * and the bf16 output is the round-to-nearest-even of this call's fp32
+ * result.  Without a partial wave (or with too short a contraction) it is
+ * nvfp4_gemm and touches no workspace.
+ *   workspace        device memory, 16-byte aligned, caller-owned, at least
+ *                    the size nvfp4_gemm_split_workspace reports for the
+ *                    same pass, operands and device; NULL is allowed when
+ *                    that size is 0.  Its contents on entry do not matter;
+ *                    calls that share a workspace must not overlap.
+ *   workspace_bytes  its size; NVFP4_ERR_WORKSPACE if smaller than needed.
+ */
+int nvfp4_gemm_split(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                     int64_t ldc, int32_t c_dtype, void* workspace, int64_t workspace_bytes,
+                     void* stream);
+
+/*
+ * nvfp4_gemm_split_workspace -- host query: the workspace bytes
+ * nvfp4_gemm_split needs for this pass and these operands on the current
+ * device (0 when the tiles fill whole waves).  At most 256 KB per compute
+ * unit (64 MiB on 256 CUs).  Validates the operands as nvfp4_gemm does;
+ * *bytes is written only on NVFP4_OK.
+ */
+int nvfp4_gemm_split_workspace(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b,
+                               int64_t* bytes);
 
 /*
  * nvfp4_gemm_fp8blk -- the same GEMM as nvfp4_gemm (same arguments, passes,

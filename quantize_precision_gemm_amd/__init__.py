@@ -21,7 +21,8 @@ __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_gemm",
     "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_mx_quantize",
-    "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "nvfp4_gemm_amax", "lib_path", "load_library",
+    "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "nvfp4_gemm_amax", "nvfp4_gemm_split", "nvfp4_gemm_split_workspace",
+    "lib_path", "load_library",
 ]
 
 BLOCK_1X16 = 0
@@ -93,6 +94,10 @@ def load_library():
         L.nvfp4_gemm.argtypes = [i32, D, D, P, i64, i32, P]
         L.nvfp4_gemm.restype = ctypes.c_int
         L.nvfp4_gemm_fp8blk.argtypes = [i32, D, D, P, i64, i32, P]
+        L.nvfp4_gemm_split.argtypes = [i32, D, D, P, i64, i32, P, i64, P]
+        L.nvfp4_gemm_split.restype = ctypes.c_int
+        L.nvfp4_gemm_split_workspace.argtypes = [i32, D, D, ctypes.POINTER(i64)]
+        L.nvfp4_gemm_split_workspace.restype = ctypes.c_int
         L.nvfp4_gemm_amax.argtypes = [i32, D, D, P, i64, u32, P, P, P]
         L.nvfp4_gemm_amax.restype = ctypes.c_int
         L.nvfp4_gemm_fp8blk.restype = ctypes.c_int
@@ -431,6 +436,44 @@ def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None, fp8
     st = fn(pass_, ctypes.byref(da), ctypes.byref(db), _ptr(out), out.stride(0), dt,
             _stream(stream))
     _check(st, "nvfp4_gemm_fp8blk" if fp8_blocks else "nvfp4_gemm")
+    return out
+
+
+def nvfp4_gemm_split_workspace(pass_, a, b):
+    """Workspace bytes nvfp4_gemm_split needs for this pass and these operands
+    on the current device (0: the tiles fill whole waves)."""
+    _check_operand(a, "a")
+    _check_operand(b, "b")
+    n = ctypes.c_int64(0)
+    da, db = a.descriptor(), b.descriptor()
+    _check(load_library().nvfp4_gemm_split_workspace(pass_, ctypes.byref(da), ctypes.byref(db),
+                                                     ctypes.byref(n)), "nvfp4_gemm_split_workspace")
+    return int(n.value)
+
+
+def nvfp4_gemm_split(pass_, a, b, workspace=None, out_dtype=torch.bfloat16, out=None, stream=None):
+    """nvfp4_gemm with the last partial wave of tiles split along K into
+    `workspace` (a uint8 device tensor of at least nvfp4_gemm_split_workspace
+    bytes; allocated here when None) -- see nvfp4_gemm_split in nvfp4.h."""
+    M = a.rows
+    N = b.cols if pass_ == DGRAD else b.rows
+    need = nvfp4_gemm_split_workspace(pass_, a, b)
+    if pass_ == DGRAD:
+        _check_nvfp4_buffers(b, b.rows, b.cols, b.block, a.codes.device, True, "b")
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=a.codes.device)
+    if workspace is not None:
+        _check_buf(workspace, "workspace", a.codes.device, torch.uint8, (need,))
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    _check_gemm_out(out, (M, N), a.codes.device)
+    dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    da, db = a.descriptor(), b.descriptor()
+    st = load_library().nvfp4_gemm_split(pass_, ctypes.byref(da), ctypes.byref(db), _ptr(out),
+                                         out.stride(0), dt, _ptr(workspace),
+                                         0 if workspace is None else workspace.numel(),
+                                         _stream(stream))
+    _check(st, "nvfp4_gemm_split")
     return out
 
 

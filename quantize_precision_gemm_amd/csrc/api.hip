@@ -368,6 +368,44 @@ int gemm_nvfp4(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void*
     return launch_status();
 }
 
+// Compute units of the current device (the tail split sizes its parts to them).
+int device_cus()
+{
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    return n;
+}
+
+// The tail-split GEMM on a workspace of ws_bytes (or, with ws_bytes < 0, just
+// the size it needs in *need).
+int gemm_split(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t ldc,
+               int32_t c_dtype, void* ws, int64_t ws_bytes, int64_t* need, void* stream)
+{
+    GemmOperand A, B;
+    int64_t M, N, K;
+    int st = resolve_gemm(pass, a, b, A, B, M, N, K);
+    if (st != NVFP4_OK) return st;
+    int64_t full = 0;
+    int split = 1;
+    const int64_t bytes = (M > 0 && N > 0 && K > 0) ? nvfp4::splitk_plan(M, N, K, device_cus(), full, split) : 0;
+    if (need) *need = bytes;
+    if (ws_bytes < 0) return NVFP4_OK;
+    if (c_dtype != NVFP4_OUT_BF16 && c_dtype != NVFP4_OUT_FP32) return NVFP4_ERR_MODE;
+    if (!c && M > 0 && N > 0) return NVFP4_ERR_NULL;
+    if (!aligned(c, c_dtype == NVFP4_OUT_FP32 ? 16 : 8) || ldc % 4 != 0) return NVFP4_ERR_ALIGN;
+    if (ldc < N) return NVFP4_ERR_SHAPE;
+    if (bytes > 0 && (!ws || ws_bytes < bytes)) return NVFP4_ERR_WORKSPACE;
+    if (bytes > 0 && !aligned(ws, 16)) return NVFP4_ERR_ALIGN;
+    const bool f32 = c_dtype == NVFP4_OUT_FP32;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (bytes > 0)
+        nvfp4::launch_gemm_nt_split(A, B, M, N, K, c, ldc, f32, static_cast<float*>(ws), full, split, s);
+    else
+        nvfp4::launch_gemm_nt(A, B, M, N, K, c, ldc, f32, s);
+    return launch_status();
+}
+
 }  // namespace
 
 extern "C" {
@@ -376,6 +414,21 @@ int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void*
                int64_t ldc, int32_t c_dtype, void* stream)
 {
     return gemm_nvfp4(pass, a, b, c, ldc, c_dtype, stream, false);
+}
+
+int nvfp4_gemm_split_workspace(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b,
+                               int64_t* bytes)
+{
+    if (!bytes) return NVFP4_ERR_NULL;
+    return gemm_split(pass, a, b, nullptr, 0, NVFP4_OUT_BF16, nullptr, -1, bytes, nullptr);
+}
+
+int nvfp4_gemm_split(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                     int64_t ldc, int32_t c_dtype, void* workspace, int64_t workspace_bytes,
+                     void* stream)
+{
+    if (workspace_bytes < 0) return NVFP4_ERR_SHAPE;
+    return gemm_split(pass, a, b, c, ldc, c_dtype, workspace, workspace_bytes, nullptr, stream);
 }
 
 int nvfp4_gemm_fp8blk(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
@@ -504,6 +557,7 @@ const char* nvfp4_status_string(int32_t status)
     case NVFP4_ERR_MODE: return "unknown mode";
     case NVFP4_ERR_MISMATCH: return "operands inconsistent with the pass";
     case NVFP4_ERR_LAUNCH: return "kernel launch failed";
+    case NVFP4_ERR_WORKSPACE: return "workspace missing or too small";
     default: return "unknown status";
     }
 }

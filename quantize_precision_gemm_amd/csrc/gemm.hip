@@ -81,11 +81,12 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 // XCDs; renumbering gives each XCD a contiguous range, walked in groups of 8
 // tile rows, column by column.
 template <int kTM = kBM>
-__device__ __forceinline__ void tile_of(int64_t M, int64_t N, int64_t& tile_m, int64_t& tile_n)
+__device__ __forceinline__ void tile_of(int64_t M, int64_t N, int64_t& tile_m, int64_t& tile_n,
+                                        int64_t hw = -1)
 {
     const int64_t tiles_m = (M + kTM - 1) / kTM, tiles_n = (N + kBN - 1) / kBN;
     const int64_t T = tiles_m * tiles_n;
-    const int64_t hw = blockIdx.x;
+    if (hw < 0) hw = blockIdx.x;
     const int64_t L = (T % 8 == 0) ? (hw % 8) * (T / 8) + hw / 8 : hw;
     const int64_t GM = 8;
     const int64_t group = L / (GM * tiles_n);
@@ -332,12 +333,19 @@ struct NvRow {
 // kTM = 128: 4 waves (1 x 4), 62 KB of LDS, two workgroups per CU -- their
 // phases drift apart, so one workgroup's stores, barriers and epilogue run
 // while the other's waves issue MFMAs.
+// Split tail (split > 1): workgroups past `full_tiles` take the remaining
+// tiles `split` ways along K, in whole K steps (the partial last step in the
+// last part), and store their raw fp32 sums (no output scale) into `ws`, one
+// 256 x 256 row-major tile per part; k_splitk_reduce then adds the parts in
+// order and writes the output.  The launch then fills the last, otherwise
+// partial, wave of tiles with parts of equal length.
 template <int kTM, bool kOutF32, int kAmax = 0>
 __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs B, int64_t M, int64_t N,
                                                     int64_t K, void* __restrict__ c, int64_t ldc,
                                                     uint32_t* amax_bits = nullptr,
                                                     uint32_t* amax_rht_bits = nullptr,
-                                                    uint32_t mask = 0u)
+                                                    uint32_t mask = 0u, int64_t full_tiles = 0,
+                                                    int split = 1, float* __restrict__ ws = nullptr)
 {
     constexpr int kRB = 256 / kTM;
     constexpr int kAOp = kTM * kRowBytes;
@@ -348,8 +356,23 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
     const int g = lane >> 5, lr = lane & 31;
+    int64_t hw = blockIdx.x, part = 0;
+    if (split > 1 && hw >= full_tiles) {
+        part = (hw - full_tiles) % split;
+        hw = full_tiles + (hw - full_tiles) / split;
+    }
     int64_t tile_m, tile_n;
-    tile_of<kTM>(M, N, tile_m, tile_n);
+    tile_of<kTM>(M, N, tile_m, tile_n, hw);
+    if (split > 1 && hw >= full_tiles) {  // this part's K steps [s0, s1)
+        const int64_t nst = (K + kKS - 1) / kKS;
+        const int64_t s0 = nst * part / split, s1 = nst * (part + 1) / split;
+        const int64_t k0 = s0 * kKS, k1 = s1 * kKS < K ? s1 * kKS : K;
+        A.data = static_cast<const uint8_t*>(A.data) + (k0 >> 1);
+        B.data = static_cast<const uint8_t*>(B.data) + (k0 >> 1);
+        A.scales += k0 >> 4;
+        B.scales += k0 >> 4;
+        K = k1 - k0;
+    }
 
     // half h of tile row `row` of A and of tile rows row + kTM j of B (rows
     // past the operand re-read its last row; they are never stored)
@@ -513,6 +536,19 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
         compute((int)(nfull & 1));
     }
 
+    if (split > 1 && hw >= full_tiles) {  // one part of a split tile: raw sums into ws
+        float* dst = ws + ((hw - full_tiles) * split + part) * (int64_t)(kTM * kBN);
+#pragma unroll
+        for (int tm = 0; tm < 4; ++tm)
+#pragma unroll
+            for (int tn = 0; tn < 2; ++tn)
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const int r = wm * 128 + tm * 32 + (e >> 2) * 8 + g * 4 + (e & 3);
+                    __builtin_nontemporal_store(acc[tm][tn][e], dst + r * kBN + wn * 64 + tn * 32 + lr);
+                }
+        return;
+    }
     float alpha;
     int alpha_exp;
     output_scale(*A.s_enc, *B.s_enc, alpha, alpha_exp);
@@ -1055,11 +1091,9 @@ static dim3 tile_grid(int64_t M, int64_t N, int64_t tm = kBM)
     return dim3((unsigned)(((M + tm - 1) / tm) * ((N + kBN - 1) / kBN)));
 }
 
-// Tile height of the NVFP4 GEMM (256: one workgroup per CU; 128: two).
-#ifndef NVFP4_GEMM_TM
-#define NVFP4_GEMM_TM 256
-#endif
-constexpr int kNvTM = NVFP4_GEMM_TM;
+// Tile height of the NVFP4 GEMM launches: 256 rows, one workgroup per CU
+// (128-row tiles, two workgroups per CU, measured slower).
+constexpr int kNvTM = kBM;
 
 void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N, int64_t K,
                     void* c, int64_t ldc, bool out_fp32, hipStream_t s)
@@ -1073,6 +1107,115 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
         hipLaunchKernelGGL((k_gemm_nv<kNvTM, true>), grid, block, 0, s, A, B, M, N, K, c, ldc);
     else
         hipLaunchKernelGGL((k_gemm_nv<kNvTM, false>), grid, block, 0, s, A, B, M, N, K, c, ldc);
+}
+
+// The split tiles of a k_gemm_nv launch: output = (sum of the tile's parts,
+// added in part order) * the output scale.  Each workgroup takes 16 rows of
+// one tile (16 workgroups per tile, so that even a few split tiles spread
+// over many CUs); a thread adds 4 groups of 4 consecutive values, all parts'
+// loads of a group in flight together.
+constexpr int kRedRows = 16;
+template <bool kOutF32>
+__global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int64_t full_tiles,
+                                                       int split, const float* __restrict__ s_enc_a,
+                                                       const float* __restrict__ s_enc_b, int64_t M,
+                                                       int64_t N, void* __restrict__ c, int64_t ldc)
+{
+    constexpr int kGroups = kBN / 4;  // float4 groups per tile row
+    const int64_t t = blockIdx.x / (kBM / kRedRows);
+    const int rg = (int)(blockIdx.x % (kBM / kRedRows));
+    int64_t tile_m, tile_n;
+    tile_of<kBM>(M, N, tile_m, tile_n, full_tiles + t);
+    float alpha;
+    int alpha_exp;
+    output_scale(*s_enc_a, *s_enc_b, alpha, alpha_exp);
+    typedef float f32x4_t __attribute__((ext_vector_type(4)));
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(ws + t * split * (int64_t)(kBM * kBN));
+    constexpr int64_t kPart = kBM * kBN / 4;  // float4 per part
+#pragma unroll
+    for (int it = 0; it < kRedRows * kGroups / 256; ++it) {
+        const int i = rg * kRedRows * kGroups + it * 256 + threadIdx.x;
+        const int r = i / kGroups, q = i % kGroups;
+        const int64_t row = tile_m * kBM + r, col = tile_n * kBN + 4 * q;
+        f32x4_t part[8];
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+            if (p < split) part[p] = __builtin_nontemporal_load(src + p * kPart + i);
+        f32x4_t v = part[0];
+#pragma unroll
+        for (int p = 1; p < 8; ++p)
+            if (p < split) v += part[p];
+        if (row >= M || col >= N) continue;
+        float y[4] = {v.x * alpha, v.y * alpha, v.z * alpha, v.w * alpha};
+        if (alpha_exp != 0)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) y[j] = __builtin_ldexpf(y[j], alpha_exp);
+        if constexpr (kOutF32) {
+            float* dst = static_cast<float*>(c) + row * ldc + col;
+            if (col + 4 <= N) {
+                __builtin_nontemporal_store(f32x4_t{y[0], y[1], y[2], y[3]}, reinterpret_cast<f32x4_t*>(dst));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (col + j < N) dst[j] = y[j];
+            }
+        } else {
+            uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
+            const uint16_t b[4] = {f32_to_bf16_rne(y[0]), f32_to_bf16_rne(y[1]), f32_to_bf16_rne(y[2]),
+                                   f32_to_bf16_rne(y[3])};
+            if (col + 4 <= N) {
+                typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+                __builtin_nontemporal_store(u32x2_t{b[0] | ((uint32_t)b[1] << 16), b[2] | ((uint32_t)b[3] << 16)},
+                                            reinterpret_cast<u32x2_t*>(dst));
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j)
+                    if (col + j < N) dst[j] = b[j];
+            }
+        }
+    }
+}
+
+int64_t splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t& full_tiles, int& split)
+{
+    const int64_t T = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int64_t rem = cus > 0 ? T % cus : 0;
+    const int64_t nst = (K + kKS - 1) / kKS;
+    full_tiles = T;
+    split = 1;
+    if (rem == 0) return 0;
+    int64_t s = cus / rem;
+    if (s > 8) s = 8;
+    while (s > 1 && nst / s < 4) --s;  // every part keeps at least 4 K steps
+    if (s < 2) return 0;
+    full_tiles = T - rem;
+    split = (int)s;
+    return rem * s * (int64_t)(kBM * kBN) * (int64_t)sizeof(float);
+}
+
+void launch_gemm_nt_split(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
+                          int64_t K, void* c, int64_t ldc, bool out_fp32, float* ws,
+                          int64_t full_tiles, int split, hipStream_t s)
+{
+    if (split < 2) return launch_gemm_nt(a, b, M, N, K, c, ldc, out_fp32, s);
+    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc};
+    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc};
+    const int64_t T = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
+    const int64_t rem = T - full_tiles;
+    const dim3 grid((unsigned)(full_tiles + rem * split)), block(512);
+    if (out_fp32)
+        hipLaunchKernelGGL((k_gemm_nv<kBM, true>), grid, block, 0, s, A, B, M, N, K, c, ldc, nullptr,
+                           nullptr, 0u, full_tiles, split, ws);
+    else
+        hipLaunchKernelGGL((k_gemm_nv<kBM, false>), grid, block, 0, s, A, B, M, N, K, c, ldc, nullptr,
+                           nullptr, 0u, full_tiles, split, ws);
+    const dim3 rgrid((unsigned)(rem * (kBM / kRedRows)));
+    if (out_fp32)
+        hipLaunchKernelGGL(k_splitk_reduce<true>, rgrid, dim3(256), 0, s, ws, full_tiles, split,
+                           a.s_enc, b.s_enc, M, N, c, ldc);
+    else
+        hipLaunchKernelGGL(k_splitk_reduce<false>, rgrid, dim3(256), 0, s, ws, full_tiles, split,
+                           a.s_enc, b.s_enc, M, N, c, ldc);
 }
 
 // Zeroes the output maxima (a kernel, not a memset, so the sequence can be

@@ -77,6 +77,17 @@ void launch_mx_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, 
 void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
                     int64_t K, void* c, int64_t ldc, bool out_fp32, hipStream_t s);
 
+// Tail split of launch_gemm_nt: when the tile count leaves the last wave of
+// workgroups on `cus` compute units partial, its tiles are split along K so
+// that the parts fill that wave.  splitk_plan gives the workspace bytes the
+// launch needs (0: no split; then full_tiles is every tile and split 1);
+// launch_gemm_nt_split runs the GEMM with that plan and a workspace of at
+// least that size (fp32 partial tiles), then adds the parts in order.
+int64_t splitk_plan(int64_t M, int64_t N, int64_t K, int cus, int64_t& full_tiles, int& split);
+void launch_gemm_nt_split(const GemmOperand& a, const GemmOperand& b, int64_t M, int64_t N,
+                          int64_t K, void* c, int64_t ldc, bool out_fp32, float* ws,
+                          int64_t full_tiles, int split, hipStream_t s);
+
 // launch_gemm_nt with bf16 output whose epilogue also writes the output's
 // tensor amax (max |c|) and, if amax_rht is not null, the amax of its
 // 16-point RHT along the rows (M a multiple of 16); both are zeroed first.

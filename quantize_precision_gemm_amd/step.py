@@ -30,9 +30,10 @@ class NVFP4Linear:
     Outputs: y (M x N, bf16), dx (M x K, bf16), dw (N x K, fp32).
     """
 
-    def __init__(self, q, torch, x, w, dy, seed, fused_quant=False):
+    def __init__(self, q, torch, x, w, dy, seed, fused_quant=False, split_tail=False):
         self.q, self.torch = q, torch
         self.fused_quant = fused_quant
+        self.split_tail = split_tail
         self.x, self.w, self.dy = x, w, dy
         M, K = x.shape
         N = w.shape[0]
@@ -51,6 +52,14 @@ class NVFP4Linear:
         self.mask = q.nvfp4_rht_sign_mask(seed + RHT_SEED)
         f32 = lambda: torch.empty(1, dtype=torch.float32, device=dev)
         self.ax, self.ax_rht, self.ady, self.ady_rht = f32(), f32(), f32(), f32()
+        # with split_tail, dgrad and wgrad run nvfp4_gemm_split (the last,
+        # partial wave of tiles split along K); they run concurrently, so
+        # each has its own workspace
+        self.ws_dgrad = self.ws_wgrad = None
+        if split_tail:
+            ws = lambda n: torch.empty(max(n, 1), dtype=torch.uint8, device=dev)
+            self.ws_dgrad = ws(q.nvfp4_gemm_split_workspace(q.DGRAD, self.gdy, self.gw))
+            self.ws_wgrad = ws(q.nvfp4_gemm_split_workspace(q.WGRAD, self.gdyt, self.gxt))
 
     def flops(self):
         return 3 * 2.0 * self.M * self.N * self.K
@@ -100,11 +109,18 @@ class NVFP4Linear:
 
     def dgrad_ops(self):
         q = self.q
+        if self.split_tail:
+            return [("dgrad", lambda: q.nvfp4_gemm_split(q.DGRAD, self.gdy, self.gw, self.ws_dgrad,
+                                                         out=self.dx))]
         return [("dgrad", lambda: q.nvfp4_gemm(q.DGRAD, self.gdy, self.gw, out=self.dx))]
 
     def wgrad_ops(self):
         q = self.q
-        wgrad = ("wgrad", lambda: q.nvfp4_gemm(q.WGRAD, self.gdyt, self.gxt, out=self.dw))
+        if self.split_tail:
+            wgrad = ("wgrad", lambda: q.nvfp4_gemm_split(q.WGRAD, self.gdyt, self.gxt, self.ws_wgrad,
+                                                         out=self.dw))
+        else:
+            wgrad = ("wgrad", lambda: q.nvfp4_gemm(q.WGRAD, self.gdyt, self.gxt, out=self.dw))
         if self.fused_quant:
             return [wgrad]
         return [

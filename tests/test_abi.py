@@ -47,7 +47,8 @@ def test_library_exports_every_declared_symbol(lib):
 def test_status_strings(lib):
     for st, s in [(0, b"ok"), (-1, b"null pointer"), (-2, b"invalid shape"),
                   (-3, b"misaligned pointer or leading dimension"), (-4, b"unknown mode"),
-                  (-5, b"operands inconsistent with the pass"), (-6, b"kernel launch failed")]:
+                  (-5, b"operands inconsistent with the pass"), (-6, b"kernel launch failed"),
+                  (-7, b"workspace missing or too small")]:
         assert lib.nvfp4_status_string(st) == s
 
 
