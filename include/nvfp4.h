@@ -333,6 +333,24 @@ int nvfp4_gemm_split_workspace(int32_t pass, const nvfp4_tensor* a, const nvfp4_
                                int64_t* bytes);
 
 /*
+ * nvfp4_gemm_split_noalloc -- nvfp4_gemm_split without a workspace argument,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * split parts go to a 64 MiB array of device memory inside the library
+ * (one per GPU, held from the library's load to the end of the process);
+ * nothing is allocated by the call.  Same arguments, results and errors as
+ * nvfp4_gemm_split; NVFP4_ERR_WORKSPACE if the split needs more than 64 MiB
+ * (it needs at most 256 KB per compute unit, 64 MiB on 256 CUs).  The first
+ * call on a device looks up that device's address of the array
+ * (NVFP4_ERR_LAUNCH if the runtime refuses).  All calls on one GPU share the
+ * array: calls that overlap on one GPU (concurrent streams, threads) race
+ * and must be serialised by the caller.  The array needs no clearing: every
+ * part is written before it is read.
+ */
+int nvfp4_gemm_split_noalloc(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                             int64_t ldc, int32_t c_dtype, void* stream);
+
+/*
  * nvfp4_gemm_fp8blk -- the same GEMM as nvfp4_gemm (same arguments, passes,
  * validation and result within the same tolerance) by the second datapath:
  * each NVFP4 block of 16 products is contracted by an FP8 matrix-core

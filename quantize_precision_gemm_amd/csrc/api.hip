@@ -3,6 +3,8 @@
 // enqueued; a failed check returns a negative status and launches nothing.
 #include <stdint.h>
 
+#include <mutex>
+
 #include "nvfp4.h"
 #include "internal.hpp"
 
@@ -429,6 +431,56 @@ int nvfp4_gemm_split(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b,
 {
     if (workspace_bytes < 0) return NVFP4_ERR_SHAPE;
     return gemm_split(pass, a, b, c, ldc, c_dtype, workspace, workspace_bytes, nullptr, stream);
+}
+
+}  // extern "C"
+
+namespace {
+
+// Scratch of nvfp4_gemm_split_noalloc: the split parts' fp32 partial tiles,
+// at most 256 KB per compute unit of a 256-CU device.  Each GPU the library
+// runs on holds its own copy from the load of the library to the end of the
+// process.  On the host `scratch` only names the array: kernels get its
+// device address, looked up once per device.
+constexpr int64_t kScratchBytes = (int64_t)64 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` per device (null: not looked up)
+
+// The current device's address of `scratch`, looked up with that device
+// current on its first use; null on failure.
+void* scratch_ptr()
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+int nvfp4_gemm_split_noalloc(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
+                             int64_t ldc, int32_t c_dtype, void* stream)
+{
+    int64_t need = 0;
+    int st = gemm_split(pass, a, b, nullptr, 0, NVFP4_OUT_BF16, nullptr, -1, &need, nullptr);
+    if (st != NVFP4_OK) return st;
+    if (need > kScratchBytes) return NVFP4_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        ws = scratch_ptr();
+        if (!ws) return NVFP4_ERR_LAUNCH;
+    }
+    return gemm_split(pass, a, b, c, ldc, c_dtype, ws, need > 0 ? kScratchBytes : 0, nullptr, stream);
 }
 
 int nvfp4_gemm_fp8blk(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
