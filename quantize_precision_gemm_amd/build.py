@@ -26,6 +26,12 @@ CFLAGS = [
 ]
 
 
+# Per-source flags.  gemm.hip: the backend's ILP-maximising machine scheduler
+# (measured on the NVFP4 GEMM's three 12B-layer passes: +0.7 % fprop, +1.9 %
+# dgrad, +2.3 % wgrad, bit-identical outputs).
+FILE_FLAGS = {"gemm.hip": ["-mllvm", "--amdgpu-sched-strategy=max-ilp"]}
+
+
 def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
@@ -58,7 +64,8 @@ def build(verbose: bool = False, jobs: int = 4, sanitize: bool = False) -> str:
     for src in SOURCES:
         obj = os.path.join(bdir, src.replace(".hip", ".o"))
         objs.append(obj)
-        cmd = [HIPCC] + CFLAGS + (SAN_FLAGS if sanitize else []) + ["-c", os.path.join(CSRC, src), "-o", obj]
+        cmd = [HIPCC] + CFLAGS + FILE_FLAGS.get(src, []) + (SAN_FLAGS if sanitize else []) + \
+            ["-c", os.path.join(CSRC, src), "-o", obj]
         procs.append(cmd)
     # compile in parallel
     from concurrent.futures import ThreadPoolExecutor
