@@ -489,14 +489,15 @@ def as_mxfp4(q, torch, dev, step):
     return TrainingStep(torch, layers, dev)
 
 
-def with_schedule(q, torch, dev, step, fused_quant, split_tail=False):
+def with_schedule(q, torch, dev, step, fused_quant, split_tail=False, serial_gemms=False):
     """The same step over the same tensors, with the NVFP4 layers' quantisers
-    fused (nvfp4_quantize_dual) or separate, and dgrad / wgrad through
-    nvfp4_gemm_split (split_tail) or nvfp4_gemm."""
+    fused (nvfp4_quantize_dual) or separate, dgrad / wgrad through
+    nvfp4_gemm_split (split_tail) or nvfp4_gemm, and the two backward GEMMs
+    concurrent on two streams or one after the other (serial_gemms)."""
     from quantize_precision_gemm_amd.step import NVFP4Linear, TrainingStep
     layers = [NVFP4Linear(q, torch, l.x, l.w, l.dy, l.seed, fused_quant, split_tail)
               if isinstance(l, NVFP4Linear) else l for l in step.layers]
-    return TrainingStep(torch, layers, dev)
+    return TrainingStep(torch, layers, dev, serial_gemms)
 
 
 def build_mlp_step(q, torch, dev, fused_quant=False):
@@ -619,6 +620,18 @@ def main():
             if name in ("dgrad", "wgrad"):
                 split_ops.setdefault(name, []).append(ev[j].elapsed_time(ev[j + 1]))
     del spl
+    # and with the two split GEMMs one after the other (the wgrad operands'
+    # quantisation beside dgrad)
+    ser = with_schedule(q, torch, dev, step, args.fused_quant, split_tail=True, serial_gemms=True)
+    for _ in range(warmup):
+        ser.run()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        ser.run()
+    torch.cuda.synchronize()
+    serial_ms = (time.perf_counter() - t0) * 1e3 / steps
+    del ser
 
     # the same step in the comparison format MXFP4, timed the same way
     mxs = as_mxfp4(q, torch, dev, step)
@@ -698,7 +711,8 @@ def main():
     result["schedules_ms_per_step"] = {
         names[int(args.fused_quant)]: round(ms_step, 4),
         names[int(not args.fused_quant)]: round(alt_ms, 4),
-        names[int(args.fused_quant)] + ", dgrad/wgrad tail split (nvfp4_gemm_split)": round(split_ms, 4)}
+        names[int(args.fused_quant)] + ", dgrad/wgrad tail split (nvfp4_gemm_split)": round(split_ms, 4),
+        names[int(args.fused_quant)] + ", tail split, dgrad then wgrad on one stream": round(serial_ms, 4)}
     gemm_names = [n for n in ("fprop", "dgrad", "wgrad", "bf16_fprop", "bf16_dgrad", "bf16_wgrad")
                   if n in by_name]
     result["gemm_tflops"] = {n: round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12, 1)

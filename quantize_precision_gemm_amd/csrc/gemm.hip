@@ -1140,7 +1140,7 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
         f32x4_t part[8];
 #pragma unroll
         for (int p = 0; p < 8; ++p)
-            if (p < split) part[p] = __builtin_nontemporal_load(src + p * kPart + i);
+            if (p < split) part[p] = src[p * kPart + i];  // just written: mostly cache hits
         f32x4_t v = part[0];
 #pragma unroll
         for (int p = 1; p < 8; ++p)

@@ -253,10 +253,14 @@ class TrainingStep:
     stream waiting for the second one.
     """
 
-    def __init__(self, torch, layers, device):
+    def __init__(self, torch, layers, device, serial_gemms=False):
         self.torch = torch
         self.layers = list(layers)
         self.side = torch.cuda.Stream(device=device)  # default priority
+        # serial_gemms: dgrad then wgrad on the main stream (each filling its
+        # own partial last wave, e.g. with nvfp4_gemm_split), only the wgrad
+        # operands' quantisation on the second stream beside dgrad
+        self.serial_gemms = serial_gemms
 
     def flops(self):
         return sum(l.flops() for l in self.layers)
@@ -297,11 +301,15 @@ class TrainingStep:
             for n, f in layer.backward_shared_ops():
                 call(n, f)
             self.side.wait_stream(main)
+            wg = layer.wgrad_ops()
             for n, f in layer.backward_quant_ops() + layer.dgrad_ops():
                 call(n, f)
             with torch.cuda.stream(self.side):
-                for n, f in layer.wgrad_ops():
+                for n, f in (wg[:-1] if self.serial_gemms else wg):
                     call(n, f)
+            if self.serial_gemms:
+                main.wait_stream(self.side)
+                call(*wg[-1])
         main.wait_stream(self.side)
 
     def serial_ops(self):
