@@ -21,7 +21,7 @@ __all__ = [
     "BLOCK_1X16", "BLOCK_16X16", "RNE", "SR", "FPROP", "DGRAD", "WGRAD",
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_gemm",
     "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_mx_quantize",
-    "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "nvfp4_gemm_amax", "nvfp4_gemm_split", "nvfp4_gemm_split_workspace",
+    "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "nvfp4_gemm_amax", "nvfp4_gemm_split", "nvfp4_gemm_split_workspace", "nvfp4_gemm_split_noalloc",
     "lib_path", "load_library",
 ]
 
@@ -98,6 +98,8 @@ def load_library():
         L.nvfp4_gemm_split.restype = ctypes.c_int
         L.nvfp4_gemm_split_workspace.argtypes = [i32, D, D, ctypes.POINTER(i64)]
         L.nvfp4_gemm_split_workspace.restype = ctypes.c_int
+        L.nvfp4_gemm_split_noalloc.argtypes = [i32, D, D, P, i64, i32, P]
+        L.nvfp4_gemm_split_noalloc.restype = ctypes.c_int
         L.nvfp4_gemm_amax.argtypes = [i32, D, D, P, i64, u32, P, P, P]
         L.nvfp4_gemm_amax.restype = ctypes.c_int
         L.nvfp4_gemm_fp8blk.restype = ctypes.c_int
@@ -474,6 +476,27 @@ def nvfp4_gemm_split(pass_, a, b, workspace=None, out_dtype=torch.bfloat16, out=
                                          0 if workspace is None else workspace.numel(),
                                          _stream(stream))
     _check(st, "nvfp4_gemm_split")
+    return out
+
+
+def nvfp4_gemm_split_noalloc(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None):
+    """nvfp4_gemm_split with the library's own device array as its workspace
+    (see nvfp4_gemm_split_noalloc in nvfp4.h: nothing is allocated by the
+    call when `out` is given; calls that overlap on one GPU race)."""
+    M = a.rows
+    N = b.cols if pass_ == DGRAD else b.rows
+    _check_operand(a, "a")
+    _check_operand(b, "b")
+    if pass_ == DGRAD:
+        _check_nvfp4_buffers(b, b.rows, b.cols, b.block, a.codes.device, True, "b")
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+    _check_gemm_out(out, (M, N), a.codes.device)
+    dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
+    da, db = a.descriptor(), b.descriptor()
+    st = load_library().nvfp4_gemm_split_noalloc(pass_, ctypes.byref(da), ctypes.byref(db),
+                                                 _ptr(out), out.stride(0), dt, _stream(stream))
+    _check(st, "nvfp4_gemm_split_noalloc")
     return out
 
 

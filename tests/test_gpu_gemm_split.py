@@ -163,3 +163,17 @@ def test_split_workspace_errors(env):
                               q.OUT_FP32, None, 0, s) == -7
     torch.cuda.synchronize()
     assert (c == 5.0).all().item()  # nothing was launched
+
+
+def test_binding_noalloc_equals_split(env):
+    # the binding's nvfp4_gemm_split_noalloc runs the same kernels as
+    # nvfp4_gemm_split with a caller workspace: identical output
+    torch, oracle, q, wl, dev = env
+    rng = np.random.default_rng(21)
+    x, w = wl.normal(rng, (300, 4112), 1.0), wl.normal(rng, (528, 4112), 0.02)
+    ga, gb = q.nvfp4_quantize(to_dev(x, dev)), q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16)
+    print("binding noalloc", flush=True)
+    a = q.nvfp4_gemm_split_noalloc(q.FPROP, ga, gb, torch.float32)
+    b = q.nvfp4_gemm_split(q.FPROP, ga, gb, None, torch.float32)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(torch.int32), b.view(torch.int32))
