@@ -473,12 +473,27 @@ def cpu_baseline(data, tokens=M):
             "seconds": t}
 
 
-def build_layer_step(q, torch, dev, fused_quant=False):
+# Backward schedule of each workload's headline step: (split_tail,
+# serial_gemms).  The layer step runs dgrad and the wgrad branch concurrently
+# with nvfp4_gemm (each fills the other's partial last wave); the 8-layer MLP
+# step runs them one after the other with nvfp4_gemm_split, which measured
+# 2-3 % faster there (concurrent pairs of GEMMs from consecutive layers share
+# the L2s).  Every bench line times the other schedules beside it.
+HEADLINE_SCHEDULE = {"layer": (False, False), "mlp": (True, True)}
+
+
+def schedule_name(fused_quant, split_tail, serial_gemms):
+    return ("dual quantisers (nvfp4_quantize_dual)" if fused_quant else "separate quantisers") + \
+        (", dgrad then wgrad on one stream" if serial_gemms else ", dgrad || wgrad branch") + \
+        (", tail split (nvfp4_gemm_split)" if split_tail else "")
+
+
+def build_layer_step(q, torch, dev, fused_quant=False, split_tail=False, serial_gemms=False):
     """The 12B-layer step: one NVFP4 linear layer, numpy-drawn inputs."""
     from quantize_precision_gemm_amd.step import NVFP4Linear, TrainingStep
     data, t = make_inputs(dev)
-    layer = NVFP4Linear(q, torch, t["X"], t["W"], t["dY"], SEED, fused_quant)
-    return data, TrainingStep(torch, [layer], dev)
+    layer = NVFP4Linear(q, torch, t["X"], t["W"], t["dY"], SEED, fused_quant, split_tail)
+    return data, TrainingStep(torch, [layer], dev, serial_gemms)
 
 
 def as_mxfp4(q, torch, dev, step):
@@ -500,7 +515,7 @@ def with_schedule(q, torch, dev, step, fused_quant, split_tail=False, serial_gem
     return TrainingStep(torch, layers, dev, serial_gemms)
 
 
-def build_mlp_step(q, torch, dev, fused_quant=False):
+def build_mlp_step(q, torch, dev, fused_quant=False, split_tail=True, serial_gemms=True):
     """The 4-block MLP step: 8 linear layers (3 NVFP4 blocks, the last block
     in bf16), each with its own inputs drawn on the GPU."""
     from quantize_precision_gemm_amd import workloads as wl
@@ -512,11 +527,11 @@ def build_mlp_step(q, torch, dev, fused_quant=False):
         seed = wl.layer_seed(wl.MLP_SEED, i)
         d = wl.layer_inputs_device(torch, dev, sh, seed)
         cls = BF16Linear if i >= len(shapes) - 2 else NVFP4Linear
-        layers.append(NVFP4Linear(q, torch, d["X"], d["W"], d["dY"], seed, fused_quant)
+        layers.append(NVFP4Linear(q, torch, d["X"], d["W"], d["dY"], seed, fused_quant, split_tail)
                       if cls is NVFP4Linear else cls(q, torch, d["X"], d["W"], d["dY"], seed))
     torch.cuda.synchronize()
     print(f"# MLP inputs generated in {time.time() - t0:.1f}s", file=sys.stderr, flush=True)
-    return TrainingStep(torch, layers, dev)
+    return TrainingStep(torch, layers, dev, serial_gemms)
 
 
 def main():
@@ -569,10 +584,11 @@ def main():
     if args.rht_study:
         print(json.dumps(rht_size_study(q, torch, dev)), flush=True)
         return
+    head_split, head_serial = HEADLINE_SCHEDULE[args.workload]
     if mlp:
-        data, step = None, build_mlp_step(q, torch, dev, args.fused_quant)
+        data, step = None, build_mlp_step(q, torch, dev, args.fused_quant, head_split, head_serial)
     else:
-        data, step = build_layer_step(q, torch, dev, args.fused_quant)
+        data, step = build_layer_step(q, torch, dev, args.fused_quant, head_split, head_serial)
 
     for _ in range(warmup):
         step.run()
@@ -591,47 +607,39 @@ def main():
     live = [s.elapsed_time(e) for s, e in marks["fprop"]]
     live_dgrad = [s.elapsed_time(e) for s, e in marks["dgrad"]]
 
-    # the other quantiser schedule over the same tensors, timed the same way
-    alt = with_schedule(q, torch, dev, step, not args.fused_quant)
-    for _ in range(warmup):
-        alt.run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        alt.run()
-    torch.cuda.synchronize()
-    alt_ms = (time.perf_counter() - t0) * 1e3 / steps
+    # the other schedules over the same tensors, timed the same way: the other
+    # quantiser form, and the backward GEMMs concurrent or one after the other,
+    # with or without the tail split
+    def timed_steps(st):
+        for _ in range(warmup):
+            st.run()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            st.run()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) * 1e3 / steps
 
-    # the step with dgrad and wgrad through nvfp4_gemm_split, timed the same way
-    spl = with_schedule(q, torch, dev, step, args.fused_quant, split_tail=True)
-    for _ in range(warmup):
-        spl.run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        spl.run()
-    torch.cuda.synchronize()
-    split_ms = (time.perf_counter() - t0) * 1e3 / steps
+    head_name = schedule_name(args.fused_quant, head_split, head_serial)
+    sched_ms = {head_name: None}
+    alt = with_schedule(q, torch, dev, step, not args.fused_quant, head_split, head_serial)
+    sched_ms[schedule_name(not args.fused_quant, head_split, head_serial)] = timed_steps(alt)
+    for sp, se in ((False, False), (True, False), (True, True)):
+        if (sp, se) == (head_split, head_serial):
+            continue
+        other = with_schedule(q, torch, dev, step, args.fused_quant, sp, se)
+        sched_ms[schedule_name(args.fused_quant, sp, se)] = timed_steps(other)
+        del other
+    # the GEMMs of the tail-split step serialised, events around each
+    spl = with_schedule(q, torch, dev, step, args.fused_quant, True, False)
     split_ops = {}
-    for _ in range(max(3, steps // 2)):  # its GEMMs serialised, events around each
+    for _ in range(max(3, steps // 2)):
         ops, ev = spl.run_timed_ops()
         torch.cuda.synchronize()
         for j, (i, name, _) in enumerate(ops):
             if name in ("dgrad", "wgrad"):
                 split_ops.setdefault(name, []).append(ev[j].elapsed_time(ev[j + 1]))
     del spl
-    # and with the two split GEMMs one after the other (the wgrad operands'
-    # quantisation beside dgrad)
-    ser = with_schedule(q, torch, dev, step, args.fused_quant, split_tail=True, serial_gemms=True)
-    for _ in range(warmup):
-        ser.run()
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(steps):
-        ser.run()
-    torch.cuda.synchronize()
-    serial_ms = (time.perf_counter() - t0) * 1e3 / steps
-    del ser
 
     # the same step in the comparison format MXFP4, timed the same way
     mxs = as_mxfp4(q, torch, dev, step)
@@ -707,12 +715,9 @@ def main():
         "data": "synthetic",
         "device": device_info(torch, dev),
     }
-    names = ("separate quantisers", "dual quantisers (nvfp4_quantize_dual)")
-    result["schedules_ms_per_step"] = {
-        names[int(args.fused_quant)]: round(ms_step, 4),
-        names[int(not args.fused_quant)]: round(alt_ms, 4),
-        names[int(args.fused_quant)] + ", dgrad/wgrad tail split (nvfp4_gemm_split)": round(split_ms, 4),
-        names[int(args.fused_quant)] + ", tail split, dgrad then wgrad on one stream": round(serial_ms, 4)}
+    sched_ms[head_name] = ms_step
+    result["schedule"] = head_name
+    result["schedules_ms_per_step"] = {k: round(v, 4) for k, v in sched_ms.items()}
     gemm_names = [n for n in ("fprop", "dgrad", "wgrad", "bf16_fprop", "bf16_dgrad", "bf16_wgrad")
                   if n in by_name]
     result["gemm_tflops"] = {n: round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12, 1)
