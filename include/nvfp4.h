@@ -289,7 +289,10 @@ uint32_t nvfp4_rht_sign_mask(uint64_t seed);
  *   c_dtype   NVFP4_OUT_BF16 (fp32 result rounded to nearest even) or
  *             NVFP4_OUT_FP32.
  * The descriptors must be the ones filled by the quantisers (shapes, block
- * and the device amax/s_enc buffers).  Returns NVFP4_OK or a negative status.
+ * and the device amax/s_enc buffers).  Each operand's codes (rows x
+ * ld_codes bytes, for DGRAD's b those of codes_t) and scales span at most
+ * 4 GiB (NVFP4_ERR_SHAPE otherwise; the kernels address them with 32-bit
+ * offsets).  Returns NVFP4_OK or a negative status.
  */
 int nvfp4_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, void* c,
                int64_t ldc, int32_t c_dtype, void* stream);

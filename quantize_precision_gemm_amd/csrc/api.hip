@@ -347,6 +347,12 @@ int resolve_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, Gem
                         b->block == NVFP4_BLOCK_16X16 ? 4 : 0, b->s_enc};
         N = b->rows;
     }
+    // the kernels address an operand's codes and scales with 32-bit offsets
+    const int64_t span = int64_t(1) << 32;
+    const int64_t b_scale_rows = B.scale_row_shift ? (N + 15) >> 4 : N;
+    if (M * A.ld_codes > span || N * B.ld_codes > span || M * A.ld_scales > span ||
+        b_scale_rows * B.ld_scales > span)
+        return NVFP4_ERR_SHAPE;
     return NVFP4_OK;
 }
 

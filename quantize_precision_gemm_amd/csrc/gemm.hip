@@ -379,50 +379,68 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
     const int row = tid >> 1, h = tid & 1;
     int64_t ra = tile_m * kTM + row;
     ra = ra < M ? ra : M - 1;
-    const uint8_t* pa = static_cast<const uint8_t*>(A.data) + ra * A.ld + 16 * h;
-    const uint8_t* psa = A.scales + (ra >> A.scale_shift) * A.ld_scales + 2 * h;
-    const uint8_t* pb[kRB];
-    const uint8_t* psb[kRB];
+    // Addresses are a uniform base (SGPRs; the K offset of a step is added
+    // there) plus a 32-bit per-thread byte offset: an operand's codes and
+    // scales each span less than 4 GiB (the ABI checks it).
+    const uint8_t* const Ad = static_cast<const uint8_t*>(A.data);
+    const uint8_t* const Bd = static_cast<const uint8_t*>(B.data);
+    const uint32_t oa = (uint32_t)(ra * A.ld) + 16u * h;           // codes of the half row
+    const uint32_t qa = (uint32_t)((ra >> A.scale_shift) * A.ld_scales);  // the row's scales
+    uint32_t ob[kRB], qb[kRB];
 #pragma unroll
     for (int j = 0; j < kRB; ++j) {
         int64_t rb = tile_n * kBN + row + kTM * j;
         rb = rb < N ? rb : N - 1;
-        pb[j] = static_cast<const uint8_t*>(B.data) + rb * B.ld + 16 * h;
-        psb[j] = B.scales + (rb >> B.scale_shift) * B.ld_scales + 2 * h;
+        ob[j] = (uint32_t)(rb * B.ld) + 16u * h;
+        qb[j] = (uint32_t)((rb >> B.scale_shift) * B.ld_scales);
     }
     const int64_t nblk = K >> 4;
 
     auto load_full = [&](int64_t k0, NvRow<kRB>& w) {
-        w.ca = *reinterpret_cast<const uint4*>(pa + (k0 >> 1));
+        w.ca = *reinterpret_cast<const uint4*>(Ad + (k0 >> 1) + oa);
 #pragma unroll
-        for (int j = 0; j < kRB; ++j) w.cb[j] = *reinterpret_cast<const uint4*>(pb[j] + (k0 >> 1));
-        w.sa = *reinterpret_cast<const uint16_t*>(psa + (k0 >> 4));
+        for (int j = 0; j < kRB; ++j) w.cb[j] = *reinterpret_cast<const uint4*>(Bd + (k0 >> 1) + ob[j]);
+        w.sa = *reinterpret_cast<const uint16_t*>(A.scales + (k0 >> 4) + (qa + 2u * h));
 #pragma unroll
-        for (int j = 0; j < kRB; ++j) w.sb[j] = *reinterpret_cast<const uint16_t*>(psb[j] + (k0 >> 4));
+        for (int j = 0; j < kRB; ++j)
+            w.sb[j] = *reinterpret_cast<const uint16_t*>(B.scales + (k0 >> 4) + (qb[j] + 2u * h));
     };
     // partial last step: blocks past K get zero scales, so their codes decode
     // to zero (the 16 code bytes of a half row with one valid block still lie
     // inside the row, whose length is rounded up to 32 codes)
     auto load_tail = [&](int64_t k0, NvRow<kRB>& w) {
         const int64_t b0 = (k0 >> 4) + 2 * h;
-        w.ca = b0 < nblk ? *reinterpret_cast<const uint4*>(pa + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
+        w.ca = b0 < nblk ? *reinterpret_cast<const uint4*>(Ad + (k0 >> 1) + oa) : make_uint4(0, 0, 0, 0);
         uint32_t sa = 0u;
         for (int i = 0; i < 2; ++i)
-            if (b0 + i < nblk) sa |= (uint32_t)psa[(k0 >> 4) + i] << (8 * i);
+            if (b0 + i < nblk) sa |= (uint32_t)A.scales[b0 + i + qa] << (8 * i);
         w.sa = sa;
 #pragma unroll
         for (int j = 0; j < kRB; ++j) {
-            w.cb[j] = b0 < nblk ? *reinterpret_cast<const uint4*>(pb[j] + (k0 >> 1)) : make_uint4(0, 0, 0, 0);
+            w.cb[j] = b0 < nblk ? *reinterpret_cast<const uint4*>(Bd + (k0 >> 1) + ob[j]) : make_uint4(0, 0, 0, 0);
             uint32_t sb = 0u;
             for (int i = 0; i < 2; ++i)
-                if (b0 + i < nblk) sb |= (uint32_t)psb[j][(k0 >> 4) + i] << (8 * i);
+                if (b0 + i < nblk) sb |= (uint32_t)B.scales[b0 + i + qb[j]] << (8 * i);
             w.sb[j] = sb;
         }
     };
-    // A half row decoded to fp16 q * S in natural k order; B half rows stored raw
-    auto put = [&](const NvRow<kRB>& w, int st) {
+    // A half row decoded to fp16 q * S in natural k order; B half rows stored
+    // raw.  Scale words: bits [sh, sh + 16) of sa (and of each sb) are the
+    // half row's two scale bytes.  kPin: the words come from a load of three
+    // steps' scales; an empty asm keeps their shifts here (hoisted next to
+    // that load, a shift would wait for the loads issued with it).
+    auto put_s = [&](auto pin, const NvRow<kRB>& w, int st, uint32_t sa, const uint32_t (&sbw)[kRB], int sh) {
+        constexpr bool kPin = decltype(pin)::value;
+        uint32_t sb[kRB];
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) sb[j] = sbw[j];
+        if constexpr (kPin) {
+            asm volatile("" : "+v"(sa));
+#pragma unroll
+            for (int j = 0; j < kRB; ++j) asm volatile("" : "+v"(sb[j]));
+        }
         uint8_t* base = lds + st * kStage;
-        const half2_t pair = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w.sa, 1.0f, false);
+        const half2_t pair = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(sa >> sh, 1.0f, false);
         const half2_t S0 = __builtin_shufflevector(pair, pair, 0, 0);
         const half2_t S1 = __builtin_shufflevector(pair, pair, 1, 1);
         const uint32_t cw[4] = {w.ca.x, w.ca.y, w.ca.z, w.ca.w};
@@ -433,9 +451,10 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
 #pragma unroll
         for (int j = 0; j < kRB; ++j) {
             *reinterpret_cast<uint4*>(base + kAOp + (row + kTM * j) * kBRow + 16 * h) = w.cb[j];
-            *reinterpret_cast<uint16_t*>(base + kAOp + kBOp + (row + kTM * j) * 4 + 2 * h) = (uint16_t)w.sb[j];
+            *reinterpret_cast<uint16_t*>(base + kAOp + kBOp + (row + kTM * j) * 4 + 2 * h) = (uint16_t)(sb[j] >> sh);
         }
     };
+    auto put = [&](const NvRow<kRB>& w, int st) { put_s(std::false_type{}, w, st, w.sa, w.sb, 0); };
 
     float16_t acc[4][2];
     zero_acc(acc);
@@ -522,6 +541,61 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
     using I0 = std::integral_constant<int, 0>;
     using I1 = std::integral_constant<int, 1>;
     using I2 = std::integral_constant<int, 2>;
+    // Scale loads three steps at a time.  A step needs 4 scale bytes of a
+    // row; a 2-byte load per thread, operand and step costs the memory
+    // pipeline as much as a 16-byte code load (both touch one cache line per
+    // row), so while whole steps remain, one 12-byte load (4-byte aligned:
+    // the ABI requires it of scale rows) brings the scales of three steps.
+    // Register sets P and Q alternate: on entry to a 6-step round P holds
+    // steps s .. s+2; Q is loaded with s+3 .. s+5 at step s, P with
+    // s+6 .. s+8 at step s+3.
+    if (nfull >= 9) {
+        uint3 Pa = *reinterpret_cast<const uint3*>(A.scales + qa), Qa;
+        uint3 Pb[kRB], Qb[kRB];
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) Pb[j] = *reinterpret_cast<const uint3*>(B.scales + qb[j]);
+        const int sh = 16 * h;
+        auto gstep = [&](auto c6, int64_t t, uint3& Ca, uint3 (&Cb)[kRB], uint3& Na, uint3 (&Nb)[kRB]) {
+            constexpr int r = decltype(c6)::value % 3;
+            const int st = (int)(t & 1);
+            NvRow<kRB>& done = r == 0 ? g0 : (r == 1 ? g1 : g2);  // step t, already in LDS
+            NvRow<kRB>& next = r == 0 ? g1 : (r == 1 ? g2 : g0);  // step t + 1
+            const int64_t k3 = (t + 3) * kKS;  // a whole step: t + 3 < nfull
+            done.ca = *reinterpret_cast<const uint4*>(Ad + (k3 >> 1) + oa);
+#pragma unroll
+            for (int j = 0; j < kRB; ++j) done.cb[j] = *reinterpret_cast<const uint4*>(Bd + (k3 >> 1) + ob[j]);
+            if constexpr (r == 0) {
+                Na = *reinterpret_cast<const uint3*>(A.scales + 4 * (t + 3) + qa);
+#pragma unroll
+                for (int j = 0; j < kRB; ++j) Nb[j] = *reinterpret_cast<const uint3*>(B.scales + 4 * (t + 3) + qb[j]);
+            }
+            compute(st);
+            uint32_t wb[kRB];
+#pragma unroll
+            for (int j = 0; j < kRB; ++j) wb[j] = r == 0 ? Cb[j].y : (r == 1 ? Cb[j].z : Nb[j].x);
+            put_s(std::true_type{}, next, st ^ 1, r == 0 ? Ca.y : (r == 1 ? Ca.z : Na.x), wb, sh);
+            __syncthreads();
+        };
+        using I3 = std::integral_constant<int, 3>;
+        using I4 = std::integral_constant<int, 4>;
+        using I5 = std::integral_constant<int, 5>;
+        for (; s + 9 <= nfull; s += 6) {
+            gstep(I0{}, s, Pa, Pb, Qa, Qb);
+            gstep(I1{}, s + 1, Pa, Pb, Qa, Qb);
+            gstep(I2{}, s + 2, Pa, Pb, Qa, Qb);
+            gstep(I3{}, s + 3, Qa, Qb, Pa, Pb);
+            gstep(I4{}, s + 4, Qa, Qb, Pa, Pb);
+            gstep(I5{}, s + 5, Qa, Qb, Pa, Pb);
+        }
+        // steps s+1, s+2 (in flight) continue with one scale load per step
+        g1.sa = Pa.y >> sh;
+        g2.sa = Pa.z >> sh;
+#pragma unroll
+        for (int j = 0; j < kRB; ++j) {
+            g1.sb[j] = Pb[j].y >> sh;
+            g2.sb[j] = Pb[j].z >> sh;
+        }
+    }
     for (; s + 3 <= nfull; s += 3) {
         step(I0{}, s);
         step(I1{}, s + 1);

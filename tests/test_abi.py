@@ -209,6 +209,10 @@ def test_gemm_validation(lib, fn):
     assert gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 66, 0, None) == -3
     assert gemm(0, ctypes.byref(a), ctypes.byref(w), FAKE, 16, 0, None) == -2
     assert gemm(0, ctypes.byref(a), ctypes.byref(op(40, 64, 1)), FAKE, 64, 0, None) == -2
+    # an operand's codes or scales spanning more than 4 GiB (32-bit offsets in the kernels)
+    assert gemm(0, ctypes.byref(op((1 << 27) + 16, 64)), ctypes.byref(w), FAKE, 64, 0, None) == -2
+    assert gemm(0, ctypes.byref(a), ctypes.byref(op(48, 64, 1, ld_scales=1 << 31)), FAKE, 64, 0,
+                None) == -2
 
 
 def test_gemm_amax_validation(lib):

@@ -98,6 +98,31 @@ def test_wgrad(env, shape):
     _check_both_dtypes(torch, q, q.WGRAD, gdyt, gxt, want)
 
 
+# Contraction lengths around the kernel's switch between one scale load per
+# 64-element K step and one per three steps (taken while 9 or more whole
+# steps remain): 8 to 16 whole steps, with and without a partial last step.
+@pytest.mark.parametrize("K", [512, 528, 576, 592, 640, 704, 768, 960, 976, 1024])
+def test_scale_load_switch(env, K):
+    torch, oracle, q, wl, dev = env
+    M, N = 264, 272
+    rng = np.random.default_rng(K)
+    x = wl.student_t_unit_var(rng, (M, K), 4)
+    w = wl.normal(rng, (N, K), 0.02)
+    dy = wl.lognormal_rows(rng, (M, K))
+    print(f"scale-load switch K={K}", flush=True)
+    gx = q.nvfp4_quantize(to_dev(x, dev), q.BLOCK_1X16, q.RNE)
+    gw = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, q.RNE, with_transpose=True)
+    want = oracle.gemm(oracle.FPROP, oracle.quantize(x), oracle.quantize(w, oracle.BLOCK_16X16))
+    _check_both_dtypes(torch, q, q.FPROP, gx, gw, want)
+    # dgrad contracts over W's rows: here dY is M x K and W^T is read (K rows)
+    w2 = wl.normal(rng, (K, N), 0.02)
+    gdy = q.nvfp4_quantize(to_dev(dy, dev), q.BLOCK_1X16, q.SR, 5)
+    gw2 = q.nvfp4_quantize(to_dev(w2, dev), q.BLOCK_16X16, q.RNE, with_transpose=True)
+    want = oracle.gemm(oracle.DGRAD, oracle.quantize(dy, oracle.BLOCK_1X16, oracle.SR, 5),
+                       oracle.quantize(w2, oracle.BLOCK_16X16))
+    _check_both_dtypes(torch, q, q.DGRAD, gdy, gw2, want)
+
+
 def test_wgrad_rht_cancels(env):
     # With the same sign mask on both operands the transform cancels in the
     # product: the NVFP4 wgrad stays close to the unquantised dY^T X.
