@@ -228,18 +228,21 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
 }
 
 // ---------------------------------------------------------------------------
-// 16x16 quantiser (weights).  A workgroup covers 128 rows x 128 columns
-// (8 x 8 tiles).  Thread t takes tile column t % 8 and rows 4*(t/8) .. +3, so
-// the 4 threads sharing one tile sit in lanes 8 apart of the same wave and
-// the tile amax is two lane shuffles.  The transposed copy is assembled in
-// LDS and written as 64-byte rows.
+// 16x16 quantiser (weights).  A workgroup of 512 threads covers 128 rows x
+// 256 columns (8 x 16 tiles).  Thread t takes tile column t % 16 and rows
+// 4*(t/16) .. +3, so the 4 threads sharing one tile sit in lanes 16 apart
+// of the same wave and the tile amax is two lane shuffles; a row's codes
+// leave as 128 contiguous bytes.  The transposed copy and its scales are
+// assembled in LDS and written as 64-byte code rows and 8-byte scale rows.
+// (128 x 128 tiles of 256 threads, with the transposed scales written byte
+// by byte, ran 4 % slower on the 12B-layer weight.)
 // ---------------------------------------------------------------------------
 
-constexpr int kW2Rows = 128, kW2Cols = 128;
+constexpr int kW2TC = 16, kW2RG = 32;  // tile columns x row groups of 4 per workgroup
+constexpr int kW2Rows = 4 * kW2RG, kW2Cols = 16 * kW2TC;
 
-// kRht: the 16-point RHT of every tile row first (fprop / dgrad ablation).
 template <bool kSR, bool kRht = false>
-__global__ __launch_bounds__(256) void k_quant_16x16(
+__global__ __launch_bounds__(kW2TC * kW2RG) void k_quant_16x16(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
     int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
@@ -247,13 +250,15 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
     int64_t ld_scales_t, float* __restrict__ amax_out, float* __restrict__ s_enc_out,
     uint32_t mask = 0u)
 {
+    constexpr int kTR = kW2RG / 4;  // tile rows per workgroup
     __shared__ __attribute__((aligned(16))) uint8_t tcodes[kW2Cols][kW2Rows / 2 + 16];  // [col][row/2]
+    __shared__ uint8_t tsc[kW2TC][kTR];
 
     const int t = threadIdx.x;
-    const int tcl = t & 7, rg = t >> 3;            // tile column in block, row group (4 rows)
+    const int tcl = t % kW2TC, rg = t / kW2TC;
     const int64_t col0 = (int64_t)blockIdx.x * kW2Cols + tcl * 16;
     const int64_t row0 = (int64_t)blockIdx.y * kW2Rows + rg * 4;
-    const bool valid = col0 < cols && row0 < rows;  // rows, cols are multiples of 16
+    const bool valid = col0 < cols && row0 < rows;
     const float amax = *amax_src;
     const float s_enc = tensor_scale(amax);
     if (blockIdx.x == 0 && blockIdx.y == 0 && t == 0) {
@@ -275,10 +280,9 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
         }
         m = __builtin_fmaxf(m, absmax16(v[i]));
     }
-    // the tile's four row groups are lanes l, l^8, l^16, l^24 of this wave
     uint32_t mb = __float_as_uint(m);
-    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 8, 64));
-    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 16, 64));
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, kW2TC, 64));
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 2 * kW2TC, 64));
     const uint32_t sb = block_scale(__uint_as_float(mb), s_enc);
     const float f = block_factor(sb, s_enc);
 
@@ -294,12 +298,11 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
     const int64_t tr = row0 >> 4, tc = col0 >> 4;
     if (valid && (rg & 3) == 0) {
         scales[tr * ld_scales + tc] = (uint8_t)sb;
-        if (scales_t) scales_t[tc * ld_scales_t + tr] = (uint8_t)sb;
+        tsc[tcl][rg >> 2] = (uint8_t)sb;
+        if (scales_t && codes_t == nullptr) scales_t[tc * ld_scales_t + tr] = (uint8_t)sb;
     }
     if (codes_t == nullptr) return;
 
-    // column k of this thread's 16 columns: rows 4rg..4rg+3 -> two bytes of the
-    // transposed row k (rows 4rg, 4rg+1 in the first, 4rg+2, 4rg+3 in the second)
 #pragma unroll
     for (int k = 0; k < 16; ++k) {
         const int sh = 4 * (k & 7);
@@ -311,19 +314,24 @@ __global__ __launch_bounds__(256) void k_quant_16x16(
         *reinterpret_cast<uint16_t*>(&tcodes[tcl * 16 + k][rg * 2]) = two;
     }
     __syncthreads();
-    // 128 transposed rows x 64 bytes: 4 threads per row, 16 bytes each
+    if (scales_t && t < kW2TC * kTR) {  // one byte per thread, consecutive along a row of scales_t
+        const int c = t / kTR, r = t % kTR;
+        const int64_t tcg = (int64_t)blockIdx.x * kW2TC + c, trg = (int64_t)blockIdx.y * kTR + r;
+        if (tcg * 16 < cols && trg * 16 < rows) scales_t[tcg * ld_scales_t + trg] = tsc[c][r];
+    }
+    constexpr int kPieces = kW2Rows / 32;  // 16-byte pieces per transposed row
 #pragma unroll
     for (int it = 0; it < 2; ++it) {
-        const int idx = it * 256 + t;
-        const int kr = idx >> 2, q = idx & 3;
-        const int64_t kcol = (int64_t)blockIdx.x * kW2Cols + kr;          // row of W^T
-        const int64_t nrow = (int64_t)blockIdx.y * kW2Rows + q * 32;      // first W row of the piece
+        const int idx = it * kW2TC * kW2RG + t;
+        const int kr = idx / kPieces, q = idx % kPieces;
+        const int64_t kcol = (int64_t)blockIdx.x * kW2Cols + kr;
+        const int64_t nrow = (int64_t)blockIdx.y * kW2Rows + q * 32;
         if (kcol < cols && nrow < rows) {
             const uint4 val = *reinterpret_cast<const uint4*>(&tcodes[kr][q * 16]);
             uint8_t* dst = codes_t + kcol * ld_codes_t + (nrow >> 1);
             if (nrow + 32 <= rows) {
                 *reinterpret_cast<uint4*>(dst) = val;
-            } else {  // rows end inside this 32-row piece (rows is a multiple of 16)
+            } else {
                 *reinterpret_cast<uint2*>(dst) = make_uint2(val.x, val.y);
             }
         }
@@ -916,11 +924,11 @@ void launch_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int
     } else {
         dim3 g((unsigned)((cols + kW2Cols - 1) / kW2Cols), (unsigned)((rows + kW2Rows - 1) / kW2Rows));
         if (sr)
-            hipLaunchKernelGGL(k_quant_16x16<true>, g, dim3(256), 0, s, x, rows, cols, ld,
+            hipLaunchKernelGGL(k_quant_16x16<true>, g, dim3(kW2TC * kW2RG), 0, s, x, rows, cols, ld,
                                amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales,
                                o.codes_t, o.ld_codes_t, o.scales_t, o.ld_scales_t, o.amax, o.s_enc);
         else
-            hipLaunchKernelGGL(k_quant_16x16<false>, g, dim3(256), 0, s, x, rows, cols, ld,
+            hipLaunchKernelGGL(k_quant_16x16<false>, g, dim3(kW2TC * kW2RG), 0, s, x, rows, cols, ld,
                                amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales,
                                o.codes_t, o.ld_codes_t, o.scales_t, o.ld_scales_t, o.amax, o.s_enc);
     }
@@ -1080,7 +1088,7 @@ void launch_quant_rht_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_
     } else {
         dim3 g((unsigned)((cols + kW2Cols - 1) / kW2Cols), (unsigned)((rows + kW2Rows - 1) / kW2Rows));
         auto go = [&](auto kern) {
-            hipLaunchKernelGGL(kern, g, dim3(256), 0, s, x, rows, cols, ld, amax_src, seed, o.codes,
+            hipLaunchKernelGGL(kern, g, dim3(kW2TC * kW2RG), 0, s, x, rows, cols, ld, amax_src, seed, o.codes,
                                o.ld_codes, o.scales, o.ld_scales, o.codes_t, o.ld_codes_t, o.scales_t,
                                o.ld_scales_t, o.amax, o.s_enc, mask);
         };
