@@ -694,6 +694,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t 
     __shared__ __attribute__((aligned(16))) uint8_t lds0[kMxStage];
     __shared__ __attribute__((aligned(16))) uint8_t lds1[kMxStage];
     __shared__ __attribute__((aligned(16))) uint8_t lds2[kMxStage];
+    // scales of three steps (12 bytes per row; A rows, then B rows), two sets;
+    // a 12-byte LDS load lands each lane's bytes 16 bytes apart
+    __shared__ __attribute__((aligned(16))) uint8_t sg0[2 * 256 * 16];
+    __shared__ __attribute__((aligned(16))) uint8_t sg1[2 * 256 * 16];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -731,14 +735,26 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t 
     }
     const int sdst = kMxS + (wb ? 1024 : 0) + 256 * (wave & 3);
 
-    auto issue = [&](int64_t k0, uint8_t* st) {
+    auto issue_codes = [&](int64_t k0, uint8_t* st) {
         const uint8_t* gb = gbase + (k0 >> 1);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             __builtin_amdgcn_global_load_lds((glb_void_t*)(gb + goff[i]),
                                              (lds_void_t*)(st + cdst + 1024 * i), 16, 0, 0);
+    };
+    auto issue_scales1 = [&](int64_t k0, uint8_t* st) {
         __builtin_amdgcn_global_load_lds((glb_void_t*)(sbase + (k0 >> 5) + soff),
                                          (lds_void_t*)(st + sdst), 4, 0, 0);
+    };
+    auto issue = [&](int64_t k0, uint8_t* st) {
+        issue_codes(k0, st);
+        issue_scales1(k0, st);
+    };
+    // the scales of steps k0 / 128 .. +2 of this wave's 64 rows
+    const int gdst = (wb ? 4096 : 0) + 1024 * (wave & 3);
+    auto issue_scales3 = [&](int64_t k0, uint8_t* sg) {
+        __builtin_amdgcn_global_load_lds((glb_void_t*)(sbase + (k0 >> 5) + soff),
+                                         (lds_void_t*)(sg + gdst), 12, 0, 0);
     };
 
     float16_t acc[4][2];
@@ -754,9 +770,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t 
         boff[sub] = kMxB + b_row * 64 + 16 * ((2 * sub + g) ^ sw);
     }
 
-    auto compute = [&](const uint8_t* st) {
-        const uint32_t* Sa = reinterpret_cast<const uint32_t*>(st + kMxS);
-        const uint32_t* Sb = Sa + 256;
+    // scale words: row r's at sc + pos(r) (A), sc + bofs + pos(r) (B); per-step
+    // stage areas: pos(r) = 4 r; groups: 16 bytes a row
+    auto compute_s = [&](const uint8_t* st, const uint8_t* sc, bool grp) {
+        auto pos = [&](int r) { return grp ? 16 * r : 4 * r; };
+        const uint8_t* Sa8 = sc;
+        const uint8_t* Sb8 = sc + (grp ? 4096 : 1024);
         v8i_t af[2][4], bf[2][2];
         uint32_t sa[4], sb[2];
 #pragma unroll
@@ -767,9 +786,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t 
             for (int tn = 0; tn < 2; ++tn) bf[sub][tn] = mx_frag(st + boff[sub] + tn * 2048);
         }
 #pragma unroll
-        for (int tm = 0; tm < 4; ++tm) sa[tm] = Sa[a_row + 32 * tm];
+        for (int tm = 0; tm < 4; ++tm) sa[tm] = *reinterpret_cast<const uint32_t*>(Sa8 + pos(a_row + 32 * tm));
 #pragma unroll
-        for (int tn = 0; tn < 2; ++tn) sb[tn] = Sb[b_row + 32 * tn];
+        for (int tn = 0; tn < 2; ++tn) sb[tn] = *reinterpret_cast<const uint32_t*>(Sb8 + pos(b_row + 32 * tn));
 #pragma unroll
         for (int sub = 0; sub < 2; ++sub) {
             const int blk = 2 * sub + g;
@@ -782,6 +801,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t 
                         (int)((sa[tm] >> (8 * blk)) & 0xFFu), 0, (int)((sb[tn] >> (8 * blk)) & 0xFFu));
         }
     };
+    auto compute = [&](const uint8_t* st) { compute_s(st, st + kMxS, false); };
 
     // Partial last step, through registers: blocks past K get zero codes
     // (they add zero whatever their scale).  Thread t writes half t % 2 of
@@ -824,6 +844,49 @@ __global__ __launch_bounds__(512, 1) void k_gemm_mx(OpArgs A, OpArgs B, int64_t 
         __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
     };
     int64_t t = 0;
+    // While nine more whole steps follow, the scales come three steps per
+    // load into sg0 / sg1 (steps 6i .. 6i+2 in sg0, 6i+3 .. 6i+5 in sg1): a
+    // 4-byte scale load per row and step touched as many cache lines as all
+    // the code loads of the step.  A wave's loads per step: 4 code pieces,
+    // plus one scale piece at the first step of each three.
+    if (nfull >= 9) {
+        issue_scales3(0, sg0);
+        __builtin_amdgcn_s_waitcnt(0x0f70);  // vmcnt(0): the prologue's loads
+        for (; t + 9 <= nfull; t += 6) {  // scales read up to step t + 8
+            __builtin_amdgcn_s_waitcnt(0x0f74);  // vmcnt(4)
+            sync();
+            issue_codes((t + 2) * kMxKS, lds2);
+            issue_scales3((t + 3) * kMxKS, sg1);
+            compute_s(lds0, sg0, true);
+            __builtin_amdgcn_s_waitcnt(0x0f75);  // vmcnt(5)
+            sync();
+            issue_codes((t + 3) * kMxKS, lds0);
+            compute_s(lds1, sg0 + 4, true);
+            __builtin_amdgcn_s_waitcnt(0x0f74);
+            sync();
+            issue_codes((t + 4) * kMxKS, lds1);
+            compute_s(lds2, sg0 + 8, true);
+            __builtin_amdgcn_s_waitcnt(0x0f74);
+            sync();
+            issue_codes((t + 5) * kMxKS, lds2);
+            issue_scales3((t + 6) * kMxKS, sg0);
+            compute_s(lds0, sg1, true);
+            __builtin_amdgcn_s_waitcnt(0x0f75);
+            sync();
+            issue_codes((t + 6) * kMxKS, lds0);
+            compute_s(lds1, sg1 + 4, true);
+            __builtin_amdgcn_s_waitcnt(0x0f74);
+            sync();
+            issue_codes((t + 7) * kMxKS, lds1);
+            compute_s(lds2, sg1 + 8, true);
+        }
+        // steps t, t + 1 (codes in flight) get their scales in their stages
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+        sync();
+        issue_scales1(t * kMxKS, lds0);
+        issue_scales1((t + 1) * kMxKS, lds1);
+        __builtin_amdgcn_s_waitcnt(0x0f70);
+    }
     for (; t + 4 < nfull; t += 3) {
         __builtin_amdgcn_s_waitcnt(0x0f75);  // vmcnt(5)
         sync();

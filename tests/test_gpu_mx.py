@@ -165,6 +165,26 @@ def test_mx_gemm(env, MNK, rounding):
     _check_gemm(env, qa, qb, oa, ob, None, f"gemm {MNK}")
 
 
+# Contraction lengths around the kernel's switch to loading three steps'
+# scales at once (taken while 9 or more whole 128-element steps remain):
+# 8 to 16 whole steps, with and without a partial last step.
+@pytest.mark.parametrize("K", [1024, 1056, 1152, 1184, 1280, 1536, 1920, 2048, 2080])
+def test_mx_gemm_scale_load_switch(env, K):
+    torch, oracle, q, wl, dev = env
+    M, N = 264, 520
+    rng = np.random.default_rng(K)
+    a = wl.lognormal_rows(rng, (M, K))
+    b = wl.normal(rng, (N, K), 0.05)
+    print(f"mx gemm scale-load switch K={K}", flush=True)
+    qa = q.nvfp4_mx_quantize(to_dev(a, dev), q.MX_ROWS, 0, 1, 4)
+    qb = q.nvfp4_mx_quantize(to_dev(b, dev))
+    oa = oracle.mx_quantize(a, oracle.MX_ROWS, 0, 1, 4)
+    ob = oracle.mx_quantize(b)
+    _same(qa, oa, "a")
+    _same(qb, ob, "b")
+    _check_gemm(env, qa, qb, oa, ob, None, f"gemm K={K}")
+
+
 def test_mx_gemm_padded_leading_dimensions(env):
     torch, oracle, q, wl, dev = env
     rng = np.random.default_rng(12)
