@@ -482,8 +482,9 @@ def cpu_baseline(data, tokens=M):
 HEADLINE_SCHEDULE = {"layer": (False, False), "mlp": (True, True)}
 
 
-def schedule_name(fused_quant, split_tail, serial_gemms):
+def schedule_name(fused_quant, split_tail, serial_gemms, rht_x_forward=False):
     return ("dual quantisers (nvfp4_quantize_dual)" if fused_quant else "separate quantisers") + \
+        (", RHT(X) encoded before fprop" if rht_x_forward and not fused_quant else "") + \
         (", dgrad then wgrad on one stream" if serial_gemms else ", dgrad || wgrad branch") + \
         (", tail split (nvfp4_gemm_split)" if split_tail else "")
 
@@ -504,13 +505,15 @@ def as_mxfp4(q, torch, dev, step):
     return TrainingStep(torch, layers, dev)
 
 
-def with_schedule(q, torch, dev, step, fused_quant, split_tail=False, serial_gemms=False):
+def with_schedule(q, torch, dev, step, fused_quant, split_tail=False, serial_gemms=False,
+                  rht_x_forward=False):
     """The same step over the same tensors, with the NVFP4 layers' quantisers
     fused (nvfp4_quantize_dual) or separate, dgrad / wgrad through
-    nvfp4_gemm_split (split_tail) or nvfp4_gemm, and the two backward GEMMs
-    concurrent on two streams or one after the other (serial_gemms)."""
+    nvfp4_gemm_split (split_tail) or nvfp4_gemm, the two backward GEMMs
+    concurrent on two streams or one after the other (serial_gemms), and X's
+    RHT operand encoded in the forward part or in the wgrad branch."""
     from quantize_precision_gemm_amd.step import NVFP4Linear, TrainingStep
-    layers = [NVFP4Linear(q, torch, l.x, l.w, l.dy, l.seed, fused_quant, split_tail)
+    layers = [NVFP4Linear(q, torch, l.x, l.w, l.dy, l.seed, fused_quant, split_tail, rht_x_forward)
               if isinstance(l, NVFP4Linear) else l for l in step.layers]
     return TrainingStep(torch, layers, dev, serial_gemms)
 
@@ -629,6 +632,10 @@ def main():
             continue
         other = with_schedule(q, torch, dev, step, args.fused_quant, sp, se)
         sched_ms[schedule_name(args.fused_quant, sp, se)] = timed_steps(other)
+        del other
+    if not args.fused_quant:  # X's RHT operand encoded before fprop instead
+        other = with_schedule(q, torch, dev, step, False, head_split, head_serial, True)
+        sched_ms[schedule_name(False, head_split, head_serial, True)] = timed_steps(other)
         del other
     # the GEMMs of the tail-split step serialised, events around each
     spl = with_schedule(q, torch, dev, step, args.fused_quant, True, False)
