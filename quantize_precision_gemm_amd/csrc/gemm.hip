@@ -77,6 +77,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
     return (uint16_t)(u >> 16);
 }
 
+// Two fp32 values -> two bf16 (round to nearest even), a in the low half:
+// one v_cvt_pk_bf16_f32.  An exhaustive in-bounds probe over every non-NaN
+// fp32 bit pattern (subnormals and infinities included) found it equal to
+// f32_to_bf16_rne; the outputs here are never NaN.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b)
+{
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t{a, b}), bf16x2_t));
+}
+
 // This workgroup's output tile.  Workgroups are dealt round-robin to the 8
 // XCDs; renumbering gives each XCD a contiguous range, walked in groups of 8
 // tile rows, column by column.
@@ -147,7 +158,7 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float a
             for (int e = 0; e < 16; ++e) {
                 const int r = (e >> 2) * 8 + g * 4 + (e & 3);
                 float v = acc[tm][tn][e] * alpha;
-                if constexpr (kAmax > 0) v = __uint_as_float((uint32_t)f32_to_bf16_rne(v) << 16);
+                if constexpr (kAmax > 0) v = __uint_as_float(bf16x2_rne(v, v) << 16);
                 y[tn][e] = v;
                 stage_out[r * kEpiStride + 32 * tn + lr] = v;
             }
@@ -235,26 +246,21 @@ __device__ __forceinline__ void store_tile(const float16_t (&acc)[4][2], float a
                     }
                 } else {
                     uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
-                    uint16_t b0, b1, b2, b3;
+                    uint32_t w01, w23;  // bf16 pairs (columns col, col + 1 and col + 2, col + 3)
                     if constexpr (kAmax > 0) {  // staged values are bf16 already
-                        b0 = (uint16_t)(__float_as_uint(v.x) >> 16);
-                        b1 = (uint16_t)(__float_as_uint(v.y) >> 16);
-                        b2 = (uint16_t)(__float_as_uint(v.z) >> 16);
-                        b3 = (uint16_t)(__float_as_uint(v.w) >> 16);
+                        w01 = __builtin_amdgcn_perm(__float_as_uint(v.y), __float_as_uint(v.x), 0x07060302u);
+                        w23 = __builtin_amdgcn_perm(__float_as_uint(v.w), __float_as_uint(v.z), 0x07060302u);
                     } else {
-                        b0 = f32_to_bf16_rne(v.x);
-                        b1 = f32_to_bf16_rne(v.y);
-                        b2 = f32_to_bf16_rne(v.z);
-                        b3 = f32_to_bf16_rne(v.w);
+                        w01 = bf16x2_rne(v.x, v.y);
+                        w23 = bf16x2_rne(v.z, v.w);
                     }
                     if (col + 4 <= N) {  // streaming store, as above
                         typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
-                        __builtin_nontemporal_store(u32x2_t{b0 | ((uint32_t)b1 << 16), b2 | ((uint32_t)b3 << 16)},
-                                                    reinterpret_cast<u32x2_t*>(dst));
+                        __builtin_nontemporal_store(u32x2_t{w01, w23}, reinterpret_cast<u32x2_t*>(dst));
                     } else {
-                        dst[0] = b0;
-                        if (col + 1 < N) dst[1] = b1;
-                        if (col + 2 < N) dst[2] = b2;
+                        dst[0] = (uint16_t)w01;
+                        if (col + 1 < N) dst[1] = (uint16_t)(w01 >> 16);
+                        if (col + 2 < N) dst[2] = (uint16_t)w23;
                     }
                 }
             }
@@ -1299,8 +1305,8 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
             }
         } else {
             uint16_t* dst = static_cast<uint16_t*>(c) + row * ldc + col;
-            const uint16_t b[4] = {f32_to_bf16_rne(y[0]), f32_to_bf16_rne(y[1]), f32_to_bf16_rne(y[2]),
-                                   f32_to_bf16_rne(y[3])};
+            const uint32_t w01 = bf16x2_rne(y[0], y[1]), w23 = bf16x2_rne(y[2], y[3]);
+            const uint16_t b[4] = {(uint16_t)w01, (uint16_t)(w01 >> 16), (uint16_t)w23, (uint16_t)(w23 >> 16)};
             if (col + 4 <= N) {
                 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
                 __builtin_nontemporal_store(u32x2_t{b[0] | ((uint32_t)b[1] << 16), b[2] | ((uint32_t)b[3] << 16)},
