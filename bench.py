@@ -308,6 +308,7 @@ def quantize_cold(q, torch, layer, reps=20):
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     aw = torch.empty(1, dtype=torch.float32, device=dev)
     e_x, e_w, e_dy = layer.M * layer.K, layer.N * layer.K, layer.M * layer.N
+    dy_rne = q.alloc_nvfp4(layer.M, layer.N, q.BLOCK_1X16, device=dev)
     enc = lambda e: 2 * e + e // 2 + e // 16
     passes = {
         "amax_X (plain + RHT maxima)": (lambda: q.nvfp4_amax(layer.x, layer.mask, layer.ax, layer.ax_rht), 2 * e_x),
@@ -324,6 +325,10 @@ def quantize_cold(q, torch, layer, reps=20):
                                                         amax_in=layer.ady, out=layer.gdy), enc(e_dy)),
         "rht_dY (RHT 1x16 SR)": (lambda: q.nvfp4_rht_quantize(layer.dy, layer.mask, q.SR, layer.seed + 101,
                                                              amax_in=layer.ady_rht, out=layer.gdyt), enc(e_dy)),
+        # not a pass of the step: the 1x16 RNE encoder on the largest tensor
+        # (336 MB), where its launch and drain weigh less than on X (84 MB)
+        "quant_dY_rne (1x16 RNE on dY, encoder characterisation)": (
+            lambda: q.nvfp4_quantize(layer.dy, q.BLOCK_1X16, q.RNE, amax_in=layer.ady, out=dy_rne), enc(e_dy)),
     }
     times = {k: [] for k in passes}
     for _ in range(reps):
