@@ -29,8 +29,10 @@
 // waves) stays raw in LDS -- 48 bytes per row instead of 144 -- and each
 // wave decodes its own B fragments after reading them, trading a little
 // VALU work for a third less LDS traffic, the resource that bounds this
-// loop.  Each thread loads half an A row and half a B row per step; the
-// loads run three steps ahead of the MFMAs in three register stages.
+// loop.  Each thread loads half an A row and half a B row per step, and
+// the scales of its rows three steps at a time; the loads run three steps
+// ahead of the MFMAs in three register stages.  The epilogue converts to
+// bf16 with the packed hardware conversion.
 // NVFP4 operands are "rows x K" with K contiguous (the dgrad weight operand
 // is the transposed 16x16-block copy written by the quantiser).
 //
