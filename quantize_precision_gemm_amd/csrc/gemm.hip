@@ -1259,14 +1259,18 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
 // one tile (64 workgroups per tile, so that even a few split tiles spread
 // over every CU; 16 rows per workgroup ran the 12B-layer reduces about 20 us
 // slower); a thread adds one group of 4 consecutive values, all parts' loads
-// in flight together.
+// in flight together.  The part count is a template parameter: with it a
+// runtime bound, the conditional loads of an 8-entry array compiled into
+// hundreds of register copies (196 VGPRs, two waves per SIMD) and the
+// reduces ran at about 2 TB/s.
 constexpr int kRedRows = 4;
-template <bool kOutF32>
+template <bool kOutF32, int kSplit>
 __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__ ws, int64_t full_tiles,
-                                                       int split, const float* __restrict__ s_enc_a,
+                                                       const float* __restrict__ s_enc_a,
                                                        const float* __restrict__ s_enc_b, int64_t M,
                                                        int64_t N, void* __restrict__ c, int64_t ldc)
 {
+    constexpr int split = kSplit;
     constexpr int kGroups = kBN / 4;  // float4 groups per tile row
     const int64_t t = blockIdx.x / (kBM / kRedRows);
     const int rg = (int)(blockIdx.x % (kBM / kRedRows));
@@ -1283,14 +1287,12 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
         const int i = rg * kRedRows * kGroups + it * 256 + threadIdx.x;
         const int r = i / kGroups, q = i % kGroups;
         const int64_t row = tile_m * kBM + r, col = tile_n * kBN + 4 * q;
-        f32x4_t part[8];
+        f32x4_t part[kSplit];
 #pragma unroll
-        for (int p = 0; p < 8; ++p)
-            if (p < split) part[p] = src[p * kPart + i];  // just written: mostly cache hits
+        for (int p = 0; p < kSplit; ++p) part[p] = src[p * kPart + i];
         f32x4_t v = part[0];
 #pragma unroll
-        for (int p = 1; p < 8; ++p)
-            if (p < split) v += part[p];
+        for (int p = 1; p < kSplit; ++p) v += part[p];
         if (row >= M || col >= N) continue;
         float y[4] = {v.x * alpha, v.y * alpha, v.z * alpha, v.w * alpha};
         if (alpha_exp != 0)
@@ -1319,6 +1321,23 @@ __global__ __launch_bounds__(256) void k_splitk_reduce(const float* __restrict__
                     if (col + j < N) dst[j] = b[j];
             }
         }
+    }
+}
+
+// Launches the reduce for `split` parts (splitk_plan keeps it in 2 .. 8).
+template <bool kOutF32, int kS = 2>
+void launch_splitk_reduce(int split, dim3 grid, hipStream_t s, const float* ws, int64_t full_tiles,
+                          const float* s_enc_a, const float* s_enc_b, int64_t M, int64_t N, void* c,
+                          int64_t ldc)
+{
+    if constexpr (kS <= 8) {
+        if (split == kS) {
+            hipLaunchKernelGGL((k_splitk_reduce<kOutF32, kS>), grid, dim3(256), 0, s, ws, full_tiles,
+                               s_enc_a, s_enc_b, M, N, c, ldc);
+            return;
+        }
+        launch_splitk_reduce<kOutF32, kS + 1>(split, grid, s, ws, full_tiles, s_enc_a, s_enc_b, M, N, c,
+                                              ldc);
     }
 }
 
@@ -1357,11 +1376,9 @@ void launch_gemm_nt_split(const GemmOperand& a, const GemmOperand& b, int64_t M,
                            nullptr, 0u, full_tiles, split, ws);
     const dim3 rgrid((unsigned)(rem * (kBM / kRedRows)));
     if (out_fp32)
-        hipLaunchKernelGGL(k_splitk_reduce<true>, rgrid, dim3(256), 0, s, ws, full_tiles, split,
-                           a.s_enc, b.s_enc, M, N, c, ldc);
+        launch_splitk_reduce<true>(split, rgrid, s, ws, full_tiles, a.s_enc, b.s_enc, M, N, c, ldc);
     else
-        hipLaunchKernelGGL(k_splitk_reduce<false>, rgrid, dim3(256), 0, s, ws, full_tiles, split,
-                           a.s_enc, b.s_enc, M, N, c, ldc);
+        launch_splitk_reduce<false>(split, rgrid, s, ws, full_tiles, a.s_enc, b.s_enc, M, N, c, ldc);
 }
 
 // Zeroes the output maxima (a kernel, not a memset, so the sequence can be

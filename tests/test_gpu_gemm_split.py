@@ -90,6 +90,26 @@ def test_split_small(env, case):
         assert ws > 0  # the split path ran
 
 
+# K for 6 output tiles (300 x 528) whose step counts (13, 21, 26 with a K
+# tail, 29) leave 3, 5, 6 and 7 parts of at least 4 steps on 256 CUs: with
+# 2, 4 and 8 above, every part count the plan can choose
+PARTS = [(832, 3), (1344, 5), (1616, 6), (1856, 7)]
+
+
+@pytest.mark.parametrize("K,parts", PARTS)
+def test_split_part_counts(env, K, parts):
+    torch, oracle, q, wl, dev = env
+    M, N = 300, 528
+    print(f"split parts K={K}", flush=True)
+    rng = np.random.default_rng(K)
+    x, w = wl.student_t_unit_var(rng, (M, K), 4), wl.normal(rng, (N, K), 0.02)
+    ga, gb = q.nvfp4_quantize(to_dev(x, dev)), q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16)
+    want = oracle.gemm(oracle.FPROP, oracle.quantize(x), oracle.quantize(w, oracle.BLOCK_16X16))
+    ws, _ = _check(torch, q, q.FPROP, ga, gb, want)
+    if _cus(torch, dev) == 256:  # 6 leftover tiles, `parts` parts of 256 x 256 fp32 each
+        assert ws == 6 * parts * 256 * 256 * 4
+
+
 @pytest.fixture(scope="module")
 def layer(env):
     torch, oracle, q, wl, dev = env
