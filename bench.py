@@ -409,6 +409,27 @@ def cpu_model():
     return None
 
 
+def mfma_sustained(q, torch, dev, blocks=1024, iters=16000, reps=3):
+    """fp16 matrix throughput the GPU sustains on register-resident operands
+    (nvfp4_mfma_sustain: the GEMM's MFMA instruction with nothing else in the
+    loop), with decoded-NVFP4-like and with random fp16 operands.  Launches of
+    ~0.15 s, one untimed first, so the clock has settled where the power
+    limit holds it: the ceiling the published peak does not show."""
+    out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    res = {}
+    for name, ops in (("decoded_nvfp4_operands", q.MFMA_SUSTAIN_DECODED),
+                      ("random_fp16_operands", q.MFMA_SUSTAIN_RANDOM)):
+        _, flops = q.nvfp4_mfma_sustain(blocks, iters, ops, out=out)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            q.nvfp4_mfma_sustain(blocks, iters, ops, out=out)
+        e1.record()
+        torch.cuda.synchronize()
+        res[name] = round(flops / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12, 1)
+    return res
+
+
 def copy_gbps(torch, dev, reps=5):
     """Device copy of 1 GiB of bf16 (read + write bytes / time), the measured
     stream rate the quantisers are also reported against."""
@@ -790,6 +811,9 @@ def main():
         "timing": "HIP events around each fprop launch in the timed steps, on its stream",
         "dgrad_avg_launch_ms_concurrent": round(mean(live_dgrad), 4) if live_dgrad else None,
         "traffic": None if mlp else counter_traffic()}
+    sus = mfma_sustained(q, torch, dev)
+    result["roofline"]["sustained_mfma_tflops"] = sus
+    result["roofline"]["frac_of_sustained"] = round(achieved / sus["decoded_nvfp4_operands"], 4)
     # every pass of the kernel, each launch serialised (events after every op)
     result["roofline"]["per_pass_serialised"] = {
         n: {"ms": round(mean(by_name[n]), 4),

@@ -470,6 +470,28 @@ int nvfp4_mx_quantize(const void* x, int64_t rows, int64_t cols, int64_t ld_x, i
 int nvfp4_mx_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t ldc,
                   int32_t c_dtype, void* stream);
 
+/*
+ * nvfp4_mfma_sustain -- measurement aid for the GEMMs' roofline, not a pass
+ * of the method: a register-only stream of v_mfma_f32_32x32x16_f16, the
+ * matrix instruction nvfp4_gemm contracts with (Technische Zusammenfassung
+ * 2.B.2 defines the GEMMs; the instruction is this library's choice).  A
+ * caller times it to learn the fp16 matrix throughput the GPU sustains under
+ * load, beside the published peak.
+ *   blocks    workgroups of 512 threads (8 waves, two per SIMD), 1 .. 2^20.
+ *   iters     rounds per wave, 1 .. 2^20; one round is 64 instructions on a
+ *             pool of 8 A and 8 B fragments, a different pair each time.
+ *             FLOPs of one call: 2 * 32 * 32 * 16 * 64 * 8 * iters * blocks.
+ *   operands  0: exact fp16 values e2m1 x e4m3 / 64 with random signs (the
+ *             kind of value the GEMM's decode produces); 1: random fp16 in
+ *             [-1, 1).
+ *   out       device float[blocks * 512], 4-byte aligned: one checksum per
+ *             thread (the sum of its accumulators).
+ * Returns NVFP4_OK, NVFP4_ERR_NULL (out), NVFP4_ERR_SHAPE (blocks or iters
+ * out of range), NVFP4_ERR_MODE (operands) or NVFP4_ERR_ALIGN; nothing is
+ * enqueued on failure.
+ */
+int nvfp4_mfma_sustain(int64_t blocks, int64_t iters, int32_t operands, float* out, void* stream);
+
 /* Human-readable name of a status code (static string). */
 const char* nvfp4_status_string(int32_t status);
 

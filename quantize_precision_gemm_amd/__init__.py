@@ -22,6 +22,7 @@ __all__ = [
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_gemm",
     "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_mx_quantize",
     "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "nvfp4_gemm_amax", "nvfp4_gemm_split", "nvfp4_gemm_split_workspace", "nvfp4_gemm_split_noalloc",
+    "nvfp4_mfma_sustain", "MFMA_SUSTAIN_DECODED", "MFMA_SUSTAIN_RANDOM",
     "lib_path", "load_library",
 ]
 
@@ -109,6 +110,8 @@ def load_library():
         L.nvfp4_bf16_gemm.restype = ctypes.c_int
         L.nvfp4_rht_sign_mask.argtypes = [u64]
         L.nvfp4_rht_sign_mask.restype = u32
+        L.nvfp4_mfma_sustain.argtypes = [i64, i64, i32, P, P]
+        L.nvfp4_mfma_sustain.restype = ctypes.c_int
         L.nvfp4_status_string.argtypes = [i32]
         L.nvfp4_status_string.restype = ctypes.c_char_p
         _lib = L
@@ -566,6 +569,23 @@ def nvfp4_bf16_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None
                                         _ptr(out), ld(out), dt, _stream(stream))
     _check(st, "nvfp4_bf16_gemm")
     return out
+
+
+MFMA_SUSTAIN_DECODED, MFMA_SUSTAIN_RANDOM = 0, 1
+
+
+def nvfp4_mfma_sustain(blocks, iters, operands=MFMA_SUSTAIN_DECODED, out=None, device=None,
+                       stream=None):
+    """Register-only stream of the GEMM's fp16 matrix instruction (see
+    nvfp4_mfma_sustain in nvfp4.h), a measurement aid: time it to learn the
+    matrix throughput the GPU sustains.  Returns (out, flops of the call)."""
+    dev = device if device is not None else (out.device if out is not None else torch.device("cuda"))
+    if out is None:
+        out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
+    _check_buf(out, "out", out.device, torch.float32, (blocks * 512,))
+    st = load_library().nvfp4_mfma_sustain(blocks, iters, operands, _ptr(out), _stream(stream))
+    _check(st, "nvfp4_mfma_sustain")
+    return out, 2.0 * 32 * 32 * 16 * 64 * 8 * iters * blocks
 
 
 def nvfp4_amax(x, sign_mask=None, amax=None, amax_rht=None, stream=None):

@@ -605,6 +605,17 @@ int nvfp4_bf16_gemm(int32_t pass, const void* a, int64_t lda, const void* b, int
     return launch_status();
 }
 
+int nvfp4_mfma_sustain(int64_t blocks, int64_t iters, int32_t operands, float* out, void* stream)
+{
+    if (!out) return NVFP4_ERR_NULL;
+    if (blocks < 1 || blocks > (int64_t(1) << 20) || iters < 1 || iters > (int64_t(1) << 20))
+        return NVFP4_ERR_SHAPE;
+    if (operands != 0 && operands != 1) return NVFP4_ERR_MODE;
+    if (!aligned(out, 4)) return NVFP4_ERR_ALIGN;
+    nvfp4::launch_mfma_sustain(blocks, iters, operands, out, static_cast<hipStream_t>(stream));
+    return launch_status();
+}
+
 const char* nvfp4_status_string(int32_t status)
 {
     switch (status) {

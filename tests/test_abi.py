@@ -265,3 +265,16 @@ def test_bf16_gemm_validation(lib):
     assert f(0, FAKE, 56, FAKE, 64, 16, 16, 64, FAKE, 64, 0, None) == -2      # lda < K
     assert f(1, FAKE, 8, FAKE, 64, 16, 16, 64, FAKE, 64, 0, None) == -2       # dgrad: lda < N
     assert f(2, FAKE, 16, FAKE, 64, 16, 16, 64, FAKE, 8, 0, None) == -2       # wgrad: ldc < K
+
+
+def test_mfma_sustain_validation(lib):
+    f = lib.nvfp4_mfma_sustain
+    f.argtypes = [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    # blocks, iters, operands, out
+    assert f(4, 8, 0, None, None) == -1             # null out
+    assert f(0, 8, 0, FAKE, None) == -2             # no workgroup
+    assert f(4, 0, 0, FAKE, None) == -2             # no round
+    assert f((1 << 20) + 1, 8, 0, FAKE, None) == -2  # too many workgroups
+    assert f(4, (1 << 20) + 1, 0, FAKE, None) == -2  # too many rounds
+    assert f(4, 8, 2, FAKE, None) == -4             # unknown operand kind
+    assert f(4, 8, 1, FAKE + 2, None) == -3         # misaligned out
