@@ -18,11 +18,14 @@ X Student-t(4) at unit variance, W ~ N(0, 0.02), dY with log-normal row
 magnitudes.  They are resident in HBM before timing starts.
 
 value = 3 * 2*M*N*K / (wall time of one step), in TFLOP/s, quantisation
-included; dgrad and wgrad run concurrently on two streams.  Per-operation
+included; W's quantisation and the wgrad operands' run on a second stream
+beside the other work, dgrad and wgrad one after the other with their last
+partial wave of tiles split along K (nvfp4_gemm_split).  Per-operation
 times come from separate serialised passes with HIP events on the stream
 the library launches on.  The roofline entry is for the dominant kernel, the
-bf16-output GEMM (fprop and dgrad launches).  The CPU baseline is the
-oracle run on a token slice of the same step.
+NVFP4 GEMM k_gemm_nv (its fprop launches), beside the throughput the matrix
+instruction alone sustains.  The CPU baseline is the oracle run on a token
+slice of the same step.
 
 --workload mlp times the 4-block MLP training step instead (tokens 16384,
 hidden 5120, FFN 20480; 8 linear layers, the last block's two in bf16; all
@@ -410,20 +413,23 @@ def cpu_model():
 
 
 def mfma_sustained(q, torch, dev, blocks=1024, iters=16000, reps=3):
-    """fp16 matrix throughput the GPU sustains on register-resident operands
-    (nvfp4_mfma_sustain: the GEMM's MFMA instruction with nothing else in the
-    loop), with decoded-NVFP4-like and with random fp16 operands.  Launches of
-    ~0.15 s, one untimed first, so the clock has settled where the power
-    limit holds it: the ceiling the published peak does not show."""
+    """Matrix throughput the GPU sustains on register-resident operands
+    (nvfp4_mfma_sustain: a GEMM's matrix instruction with nothing else in the
+    loop): the fp16 instruction of nvfp4_gemm on decoded-NVFP4-like and on
+    random fp16 operands, and the block-scaled FP4 instruction of
+    nvfp4_mx_gemm.  Launches of ~0.15 s, one untimed first, so the clock has
+    settled where the power limit holds it: the ceiling the published peak
+    does not show."""
     out = torch.empty(blocks * 512, dtype=torch.float32, device=dev)
     res = {}
-    for name, ops in (("decoded_nvfp4_operands", q.MFMA_SUSTAIN_DECODED),
-                      ("random_fp16_operands", q.MFMA_SUSTAIN_RANDOM)):
-        _, flops = q.nvfp4_mfma_sustain(blocks, iters, ops, out=out)
+    for name, ops, it in (("decoded_nvfp4_operands", q.MFMA_SUSTAIN_DECODED, iters),
+                          ("random_fp16_operands", q.MFMA_SUSTAIN_RANDOM, iters),
+                          ("fp4_block_scaled_e2m1", q.MFMA_SUSTAIN_FP4, iters)):
+        _, flops = q.nvfp4_mfma_sustain(blocks, it, ops, out=out)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record()
         for _ in range(reps):
-            q.nvfp4_mfma_sustain(blocks, iters, ops, out=out)
+            q.nvfp4_mfma_sustain(blocks, it, ops, out=out)
         e1.record()
         torch.cuda.synchronize()
         res[name] = round(flops / (e0.elapsed_time(e1) / reps * 1e-3) / 1e12, 1)
@@ -500,12 +506,14 @@ def cpu_baseline(data, tokens=M):
 
 
 # Backward schedule of each workload's headline step: (split_tail,
-# serial_gemms).  The layer step runs dgrad and the wgrad branch concurrently
-# with nvfp4_gemm (each fills the other's partial last wave); the 8-layer MLP
-# step runs them one after the other with nvfp4_gemm_split, which measured
-# 2-3 % faster there (concurrent pairs of GEMMs from consecutive layers share
-# the L2s).  Every bench line times the other schedules beside it.
-HEADLINE_SCHEDULE = {"layer": (False, False), "mlp": (True, True)}
+# serial_gemms).  Both run dgrad and then wgrad on the main stream through
+# nvfp4_gemm_split (each GEMM fills its own last, partial wave of tiles),
+# with only the wgrad operands' quantisation on the second stream beside
+# dgrad.  On the layer step that measured 2 % faster than dgrad and the
+# wgrad branch concurrently through nvfp4_gemm (4.327 against 4.414 ms, one
+# run); on the 8-layer MLP step 2-3 % faster.  Every bench line times the
+# other schedules beside it.
+HEADLINE_SCHEDULE = {"layer": (True, True), "mlp": (True, True)}
 
 
 def schedule_name(fused_quant, split_tail, serial_gemms, rht_x_forward=False):
@@ -623,22 +631,22 @@ def main():
         step.run()
     torch.cuda.synchronize()
 
-    # timed steps: the step itself, with timing events around the launches of
-    # the bf16-output NVFP4 GEMM (fprop and dgrad) only.  The roofline takes
-    # the fprop launches: nothing else runs on the GPU meanwhile, while dgrad
-    # shares it with the concurrent wgrad branch
-    marks = {"fprop": [], "dgrad": []}
+    # timed steps: the step itself, with timing events around the fprop
+    # launches only (the roofline's kernel; nothing else runs on the GPU
+    # meanwhile).  A timing event is a barrier in the stream: the kernel
+    # after fprop cannot start during fprop's last wave, which costs the step
+    # a little; schedules_ms_per_step times every schedule without events
+    marks = {"fprop": []}
     t0 = time.perf_counter()
     for _ in range(steps):
         step.run(marks)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     live = [s.elapsed_time(e) for s, e in marks["fprop"]]
-    live_dgrad = [s.elapsed_time(e) for s, e in marks["dgrad"]]
 
-    # the other schedules over the same tensors, timed the same way: the other
-    # quantiser form, and the backward GEMMs concurrent or one after the other,
-    # with or without the tail split
+    # every schedule over the same tensors, timed the same way (no events):
+    # the headline's, the other quantiser form, and the backward GEMMs
+    # concurrent or one after the other, with or without the tail split
     def timed_steps(st):
         for _ in range(warmup):
             st.run()
@@ -650,7 +658,7 @@ def main():
         return (time.perf_counter() - t0) * 1e3 / steps
 
     head_name = schedule_name(args.fused_quant, head_split, head_serial)
-    sched_ms = {head_name: None}
+    sched_ms = {head_name: timed_steps(step)}
     alt = with_schedule(q, torch, dev, step, not args.fused_quant, head_split, head_serial)
     sched_ms[schedule_name(not args.fused_quant, head_split, head_serial)] = timed_steps(alt)
     for sp, se in ((False, False), (True, False), (True, True)):
@@ -686,10 +694,13 @@ def main():
     mx_ms = (time.perf_counter() - t0) * 1e3 / steps
     del mxs
 
-    # per-operation times: separate, serialised passes with events
+    # per-operation times: separate, serialised passes with events; for the
+    # layer through nvfp4_gemm (the kernel the roofline describes; the split
+    # calls are timed above)
+    opstep = step if mlp or not head_split else with_schedule(q, torch, dev, step, args.fused_quant)
     times = {}
     for _ in range(max(3, steps // 2)):
-        ops, ev = step.run_timed_ops()
+        ops, ev = opstep.run_timed_ops()
         torch.cuda.synchronize()
         for j, (i, name, _) in enumerate(ops):
             times.setdefault((i, name), []).append(ev[j].elapsed_time(ev[j + 1]))
@@ -748,7 +759,6 @@ def main():
         "data": "synthetic",
         "device": device_info(torch, dev),
     }
-    sched_ms[head_name] = ms_step
     result["schedule"] = head_name
     result["schedules_ms_per_step"] = {k: round(v, 4) for k, v in sched_ms.items()}
     gemm_names = [n for n in ("fprop", "dgrad", "wgrad", "bf16_fprop", "bf16_dgrad", "bf16_wgrad")
@@ -792,7 +802,10 @@ def main():
         result["ms_per_op"] = {k: round(v, 4) for k, v in avg.items()}
         result["quantize_cold"] = quantize_cold(q, torch, step.layers[0])
         result["config_256_fprop"] = small_fprop_latency(q, torch, dev)
+    sus = mfma_sustained(q, torch, dev)
     if mx is not None:
+        mx["frac_of_sustained_fp4"] = {k: round(v / sus["fp4_block_scaled_e2m1"], 3)
+                                       for k, v in mx["gemm_tflops"].items()}
         mx["speedup_vs_nvfp4"] = {k: round(v / result["gemm_tflops"][k], 2)
                                   for k, v in mx["gemm_tflops"].items()}
         result["mxfp4_comparison"] = mx
@@ -809,9 +822,8 @@ def main():
         "frac": round(achieved / PEAK_F16_TFLOPS, 4), "avg_launch_ms": round(gemm_bf16_ms, 4),
         "launches": len(live),
         "timing": "HIP events around each fprop launch in the timed steps, on its stream",
-        "dgrad_avg_launch_ms_concurrent": round(mean(live_dgrad), 4) if live_dgrad else None,
+
         "traffic": None if mlp else counter_traffic()}
-    sus = mfma_sustained(q, torch, dev)
     result["roofline"]["sustained_mfma_tflops"] = sus
     result["roofline"]["frac_of_sustained"] = round(achieved / sus["decoded_nvfp4_operands"], 4)
     # every pass of the kernel, each launch serialised (events after every op)

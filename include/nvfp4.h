@@ -472,18 +472,22 @@ int nvfp4_mx_gemm(const nvfp4_tensor* a, const nvfp4_tensor* b, void* c, int64_t
 
 /*
  * nvfp4_mfma_sustain -- measurement aid for the GEMMs' roofline, not a pass
- * of the method: a register-only stream of v_mfma_f32_32x32x16_f16, the
- * matrix instruction nvfp4_gemm contracts with (Technische Zusammenfassung
- * 2.B.2 defines the GEMMs; the instruction is this library's choice).  A
- * caller times it to learn the fp16 matrix throughput the GPU sustains under
- * load, beside the published peak.
+ * of the method: a register-only stream of the matrix instruction a GEMM of
+ * this library contracts with (Technische Zusammenfassung 2.B.2 defines the
+ * GEMMs, 2.A the MXFP4 comparison; the instructions are this library's
+ * choice).  A caller times it to learn the matrix throughput the GPU
+ * sustains under load, beside the published peak.
  *   blocks    workgroups of 512 threads (8 waves, two per SIMD), 1 .. 2^20.
  *   iters     rounds per wave, 1 .. 2^20; one round is 64 instructions on a
  *             pool of 8 A and 8 B fragments, a different pair each time.
- *             FLOPs of one call: 2 * 32 * 32 * 16 * 64 * 8 * iters * blocks.
- *   operands  0: exact fp16 values e2m1 x e4m3 / 64 with random signs (the
- *             kind of value the GEMM's decode produces); 1: random fp16 in
- *             [-1, 1).
+ *             FLOPs of one call: 2 * 32 * 32 * Kinst * 64 * 8 * iters *
+ *             blocks, Kinst = 16 for operands 0 and 1, 64 for operands 2.
+ *   operands  0: nvfp4_gemm's v_mfma_f32_32x32x16_f16 on exact fp16 values
+ *             e2m1 x e4m3 / 64 with random signs (the kind of value the
+ *             GEMM's decode produces); 1: the same instruction on random fp16
+ *             in [-1, 1); 2: nvfp4_mx_gemm's block-scaled FP4 instruction
+ *             v_mfma_scale_f32_32x32x64_f8f6f4 on random E2M1 codes with
+ *             unit scales.
  *   out       device float[blocks * 512], 4-byte aligned: one checksum per
  *             thread (the sum of its accumulators).
  * Returns NVFP4_OK, NVFP4_ERR_NULL (out), NVFP4_ERR_SHAPE (blocks or iters

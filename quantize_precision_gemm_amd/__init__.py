@@ -22,7 +22,7 @@ __all__ = [
     "NVFP4Tensor", "alloc_nvfp4", "nvfp4_quantize", "nvfp4_rht_quantize", "nvfp4_quantize_dual", "nvfp4_gemm",
     "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_mx_quantize",
     "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "nvfp4_gemm_amax", "nvfp4_gemm_split", "nvfp4_gemm_split_workspace", "nvfp4_gemm_split_noalloc",
-    "nvfp4_mfma_sustain", "MFMA_SUSTAIN_DECODED", "MFMA_SUSTAIN_RANDOM",
+    "nvfp4_mfma_sustain", "MFMA_SUSTAIN_DECODED", "MFMA_SUSTAIN_RANDOM", "MFMA_SUSTAIN_FP4",
     "lib_path", "load_library",
 ]
 
@@ -571,12 +571,12 @@ def nvfp4_bf16_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None
     return out
 
 
-MFMA_SUSTAIN_DECODED, MFMA_SUSTAIN_RANDOM = 0, 1
+MFMA_SUSTAIN_DECODED, MFMA_SUSTAIN_RANDOM, MFMA_SUSTAIN_FP4 = 0, 1, 2
 
 
 def nvfp4_mfma_sustain(blocks, iters, operands=MFMA_SUSTAIN_DECODED, out=None, device=None,
                        stream=None):
-    """Register-only stream of the GEMM's fp16 matrix instruction (see
+    """Register-only stream of a GEMM's matrix instruction (see
     nvfp4_mfma_sustain in nvfp4.h), a measurement aid: time it to learn the
     matrix throughput the GPU sustains.  Returns (out, flops of the call)."""
     dev = device if device is not None else (out.device if out is not None else torch.device("cuda"))
@@ -585,7 +585,8 @@ def nvfp4_mfma_sustain(blocks, iters, operands=MFMA_SUSTAIN_DECODED, out=None, d
     _check_buf(out, "out", out.device, torch.float32, (blocks * 512,))
     st = load_library().nvfp4_mfma_sustain(blocks, iters, operands, _ptr(out), _stream(stream))
     _check(st, "nvfp4_mfma_sustain")
-    return out, 2.0 * 32 * 32 * 16 * 64 * 8 * iters * blocks
+    k_inst = 64 if operands == MFMA_SUSTAIN_FP4 else 16
+    return out, 2.0 * 32 * 32 * k_inst * 64 * 8 * iters * blocks
 
 
 def nvfp4_amax(x, sign_mask=None, amax=None, amax_rht=None, stream=None):

@@ -610,7 +610,7 @@ int nvfp4_mfma_sustain(int64_t blocks, int64_t iters, int32_t operands, float* o
     if (!out) return NVFP4_ERR_NULL;
     if (blocks < 1 || blocks > (int64_t(1) << 20) || iters < 1 || iters > (int64_t(1) << 20))
         return NVFP4_ERR_SHAPE;
-    if (operands != 0 && operands != 1) return NVFP4_ERR_MODE;
+    if (operands < 0 || operands > 2) return NVFP4_ERR_MODE;
     if (!aligned(out, 4)) return NVFP4_ERR_ALIGN;
     nvfp4::launch_mfma_sustain(blocks, iters, operands, out, static_cast<hipStream_t>(stream));
     return launch_status();

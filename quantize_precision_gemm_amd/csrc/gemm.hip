@@ -1452,14 +1452,17 @@ void launch_bf16_gemm(const uint16_t* a, int64_t lda, bool a_t, const uint16_t* 
 
 // ---------------------------------------------------------------------------
 // Sustained matrix-core throughput (a measurement aid, not a pass): 8 waves
-// per workgroup (two per SIMD) run rounds of 64 v_mfma_f32_32x32x16_f16 on a
+// per workgroup (two per SIMD) run rounds of 64 matrix instructions on a
 // pool of 8 A and 8 B register fragments, a different pair for every
 // instruction, into 8 accumulators each (every accumulator is reused 8
-// instructions later, so no instruction waits on another).  kOps = 0: exact
-// fp16 values E2M1 x E4M3 / 64 with a random sign, as the GEMM's decoded
-// operands; 1: random fp16 in [-1, 1).  With every operand in registers the
-// loop measures what the matrix cores sustain at the clock the chip holds
-// under that load, which the power limit sets below the nominal 2.4 GHz.
+// instructions later, so no instruction waits on another).  kOps = 0: the
+// GEMM's v_mfma_f32_32x32x16_f16 on exact fp16 values E2M1 x E4M3 / 64 with
+// a random sign, as the decoded operands; 1: the same instruction on random
+// fp16 in [-1, 1); 2: the block-scaled FP4 instruction of the MXFP4 GEMM,
+// v_mfma_scale_f32_32x32x64_f8f6f4, on random E2M1 codes with unit scales.
+// With every operand in registers the loop measures what the matrix cores
+// sustain at the clock the chip holds under that load, which the power
+// limit sets below the nominal 2.4 GHz.
 // ---------------------------------------------------------------------------
 
 namespace {
@@ -1482,31 +1485,49 @@ __global__ __launch_bounds__(512, 1) void k_mfma_sustain(float* __restrict__ out
     for (int j = 0; j < 8; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[j][e] = 0.0f;
-    half8_t fa[8], fb[8];
     const uint32_t tid = (uint32_t)(blockIdx.x * blockDim.x + threadIdx.x);
-    const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+    if constexpr (kOps == 2) {
+        v8i_t fa[8], fb[8];  // 32 E2M1 codes (4 dwords) per lane; the upper half unused
 #pragma unroll
-    for (int p = 0; p < 8; ++p)
+        for (int p = 0; p < 8; ++p)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const uint32_t h1 = mix32(tid * 131u + 17u * p + e), h2 = mix32(h1 + 0x9e3779b9u);
-            float va, vb;
-            if constexpr (kOps == 0) {
-                const float sa = (1.0f + (float)(h1 >> 29) * 0.125f) * (float)(1u << ((h1 >> 20) & 3u)) * 0.015625f;
-                const float sb = (1.0f + (float)(h2 >> 29) * 0.125f) * (float)(1u << ((h2 >> 20) & 3u)) * 0.015625f;
-                va = (h1 & 8u) ? -mag[h1 & 7u] * sa : mag[h1 & 7u] * sa;
-                vb = (h2 & 8u) ? -mag[h2 & 7u] * sb : mag[h2 & 7u] * sb;
-            } else {
-                va = (float)(h1 & 0xFFFFu) * (1.0f / 32768.0f) - 1.0f;
-                vb = (float)(h2 & 0xFFFFu) * (1.0f / 32768.0f) - 1.0f;
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t h1 = mix32(tid * 131u + 17u * p + e), h2 = mix32(h1 + 0x9e3779b9u);
+                fa[p][e] = e < 4 ? (int)h1 : 0;
+                fb[p][e] = e < 4 ? (int)h2 : 0;
             }
-            fa[p][e] = (_Float16)va;
-            fb[p][e] = (_Float16)vb;
-        }
-    for (int64_t it = 0; it < iters; ++it) {
+        for (int64_t it = 0; it < iters; ++it) {
 #pragma unroll
-        for (int j = 0; j < 64; ++j)
-            acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[j & 7], fb[((j >> 3) + j) & 7], acc[j & 7], 0, 0, 0);
+            for (int j = 0; j < 64; ++j)
+                acc[j & 7] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                    fa[j & 7], fb[((j >> 3) + j) & 7], acc[j & 7], 4, 4, 0, 127, 0, 127);
+        }
+    } else {
+        half8_t fa[8], fb[8];
+        const float mag[8] = {0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f};
+#pragma unroll
+        for (int p = 0; p < 8; ++p)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t h1 = mix32(tid * 131u + 17u * p + e), h2 = mix32(h1 + 0x9e3779b9u);
+                float va, vb;
+                if constexpr (kOps == 0) {
+                    const float sa = (1.0f + (float)(h1 >> 29) * 0.125f) * (float)(1u << ((h1 >> 20) & 3u)) * 0.015625f;
+                    const float sb = (1.0f + (float)(h2 >> 29) * 0.125f) * (float)(1u << ((h2 >> 20) & 3u)) * 0.015625f;
+                    va = (h1 & 8u) ? -mag[h1 & 7u] * sa : mag[h1 & 7u] * sa;
+                    vb = (h2 & 8u) ? -mag[h2 & 7u] * sb : mag[h2 & 7u] * sb;
+                } else {
+                    va = (float)(h1 & 0xFFFFu) * (1.0f / 32768.0f) - 1.0f;
+                    vb = (float)(h2 & 0xFFFFu) * (1.0f / 32768.0f) - 1.0f;
+                }
+                fa[p][e] = (_Float16)va;
+                fb[p][e] = (_Float16)vb;
+            }
+        for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+            for (int j = 0; j < 64; ++j)
+                acc[j & 7] = __builtin_amdgcn_mfma_f32_32x32x16_f16(fa[j & 7], fb[((j >> 3) + j) & 7], acc[j & 7], 0, 0, 0);
+        }
     }
     float r = 0.0f;
 #pragma unroll
@@ -1518,10 +1539,13 @@ __global__ __launch_bounds__(512, 1) void k_mfma_sustain(float* __restrict__ out
 
 void launch_mfma_sustain(int64_t blocks, int64_t iters, int operands, float* out, hipStream_t s)
 {
+    const dim3 g((unsigned)blocks), b(512);
     if (operands == 0)
-        hipLaunchKernelGGL(k_mfma_sustain<0>, dim3((unsigned)blocks), dim3(512), 0, s, out, iters);
+        hipLaunchKernelGGL(k_mfma_sustain<0>, g, b, 0, s, out, iters);
+    else if (operands == 1)
+        hipLaunchKernelGGL(k_mfma_sustain<1>, g, b, 0, s, out, iters);
     else
-        hipLaunchKernelGGL(k_mfma_sustain<1>, dim3((unsigned)blocks), dim3(512), 0, s, out, iters);
+        hipLaunchKernelGGL(k_mfma_sustain<2>, g, b, 0, s, out, iters);
 }
 
 }  // namespace nvfp4

@@ -112,9 +112,11 @@ void launch_bf16_gemm(const uint16_t* a, int64_t lda, bool a_t, const uint16_t* 
                       bool b_t, int64_t M, int64_t N, int64_t K, void* c, int64_t ldc,
                       bool out_fp32, hipStream_t s);
 
-// Register-only stream of fp16 32x32x16 MFMAs: `blocks` workgroups of 512
-// threads, `iters` rounds of 64 instructions per wave; operands 0 = exact
-// E2M1 x E4M3 fp16 values, 1 = random fp16; one float per thread into out.
+// Register-only stream of matrix instructions: `blocks` workgroups of 512
+// threads, `iters` rounds of 64 instructions per wave; operands 0 = fp16
+// 32x32x16 on exact E2M1 x E4M3 fp16 values, 1 = the same on random fp16,
+// 2 = block-scaled FP4 32x32x64 on random E2M1 codes; one float per thread
+// into out.
 void launch_mfma_sustain(int64_t blocks, int64_t iters, int operands, float* out, hipStream_t s);
 
 }  // namespace nvfp4

@@ -276,5 +276,6 @@ def test_mfma_sustain_validation(lib):
     assert f(4, 0, 0, FAKE, None) == -2             # no round
     assert f((1 << 20) + 1, 8, 0, FAKE, None) == -2  # too many workgroups
     assert f(4, (1 << 20) + 1, 0, FAKE, None) == -2  # too many rounds
-    assert f(4, 8, 2, FAKE, None) == -4             # unknown operand kind
+    assert f(4, 8, 3, FAKE, None) == -4             # unknown operand kind
+    assert f(4, 8, -1, FAKE, None) == -4
     assert f(4, 8, 1, FAKE + 2, None) == -3         # misaligned out
