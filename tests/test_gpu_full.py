@@ -1,4 +1,4 @@
-"""Parity at the full 12B-layer sizes, in the launch configuration bench.py times.
+"""Parity at the full 12B-layer sizes, in the launch configurations bench.py times.
 
 Workload: tokens M = 8192, in K = 5120, out N = 20480 (the bench step), plus
 the 256^3 fprop with outliers.  Every quantised tensor is compared with the
@@ -104,6 +104,51 @@ def test_full_wgrad(full):
     ob = oracle.rht_quantize(data["X"], step.mask, oracle.RNE)
     y32 = _sampled_gemm(torch, oracle, q, q.WGRAD, step.gdyt, step.gxt, oa, ob, _rows(bench.N, seed=2))
     assert torch.equal(y32, step.dw)
+
+
+def test_full_headline_schedule(full):
+    """The step in the schedule bench.py times (its headline: dgrad, then
+    wgrad, through nvfp4_gemm_split) over the same inputs: every quantised
+    operand and the fprop output are bit-identical to the step verified
+    above; dX and dW equal nvfp4_gemm_split called on those operands (bf16
+    dX = RNE of its fp32 result), within the oracle tolerance on sampled rows."""
+    import types
+    torch, oracle, q, bench, data, step = full
+    split, serial = bench.HEADLINE_SCHEDULE["layer"]
+    dev = step.y.device
+    print(f"headline schedule split={split} serial={serial}", flush=True)
+    head = bench.with_schedule(q, torch, dev, types.SimpleNamespace(layers=[step]), False, split, serial)
+    head.run()
+    torch.cuda.synchronize()
+    h = head.layers[0]
+    for name in ("gx", "gw", "gdy", "gdyt", "gxt"):
+        a, b = getattr(h, name), getattr(step, name)
+        for f in ("codes", "scales", "codes_t", "scales_t", "amax", "s_enc"):
+            x, y = getattr(a, f), getattr(b, f)
+            assert (x is None) == (y is None), f"{name}.{f}"
+            if x is not None:
+                assert torch.equal(x, y), f"{name}.{f} differs"
+    assert torch.equal(h.y, step.y)
+    passes = [(q.DGRAD, step.gdy, step.gw, h.dx, _rows(bench.M, seed=3),
+               lambda rows: oracle.gemm(oracle.DGRAD, oracle.quantize(data["dY"], oracle.BLOCK_1X16, oracle.SR,
+                                                                      bench.SEED + 100),
+                                        oracle.quantize(data["W"], oracle.BLOCK_16X16), rows=rows)),
+              (q.WGRAD, step.gdyt, step.gxt, h.dw, _rows(bench.N, seed=4),
+               lambda rows: oracle.gemm(oracle.WGRAD, oracle.rht_quantize(data["dY"], step.mask, oracle.SR,
+                                                                          bench.SEED + 101),
+                                        oracle.rht_quantize(data["X"], step.mask, oracle.RNE), rows=rows))]
+    for pass_, a, b, got, rows, want in passes:
+        ws = q.nvfp4_gemm_split_workspace(pass_, a, b)
+        buf = torch.empty(max(ws, 1), dtype=torch.uint8, device=dev)
+        y32 = q.nvfp4_gemm_split(pass_, a, b, buf, torch.float32)
+        torch.cuda.synchronize()
+        if got.dtype == torch.bfloat16:
+            assert torch.equal(y32.to(torch.bfloat16), got)
+        else:
+            assert torch.equal(y32, got)
+        g = y32[torch.as_tensor(rows, device=dev)].double().cpu().numpy()
+        err = rel_fro(g, want(rows))
+        assert err <= TOL, f"pass {pass_}: relative Frobenius error {err:.3e}"
 
 
 def test_small_fprop_with_outliers():
