@@ -832,6 +832,13 @@ def main():
             "achieved": round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12, 1),
             "frac": round(gemm_flop / (mean(by_name[n]) * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
         for n in ("fprop", "dgrad", "wgrad") if n in by_name}
+    # the calls the headline step makes for dgrad and wgrad (k_gemm_nv with
+    # the last partial wave split along K, then k_splitk_reduce)
+    for n, v in split_ops.items():
+        result["roofline"]["per_pass_serialised"][n + " (nvfp4_gemm_split)"] = {
+            "ms": round(mean(v), 4),
+            "achieved": round(gemm_flop / (mean(v) * 1e-3) / 1e12, 1),
+            "frac": round(gemm_flop / (mean(v) * 1e-3) / 1e12 / PEAK_F16_TFLOPS, 4)}
     result["cpu_baseline"] = None
     if not args.no_cpu_baseline and not mlp:
         print("# timing the CPU oracle on a token slice", file=sys.stderr, flush=True)
