@@ -51,10 +51,16 @@ PEAK_FP4_TFLOPS = 10100.0  # MI355X dense fp4/fp6 MFMA
 
 
 def gemm_source_hash():
+    """Hash of the GEMM kernels' code (comments and blank lines removed, so
+    that a comment edit does not invalidate the committed counter summary)."""
     h = hashlib.sha256()
     for f in ["gemm.hip", "nvfp4_device.hpp"]:
-        with open(os.path.join(ROOT, "quantize_precision_gemm_amd", "csrc", f), "rb") as fh:
-            h.update(fh.read())
+        with open(os.path.join(ROOT, "quantize_precision_gemm_amd", "csrc", f)) as fh:
+            text = re.sub(r"/\*.*?\*/", "", fh.read(), flags=re.S)
+        for line in text.splitlines():
+            code = line.split("//", 1)[0].rstrip()
+            if code:
+                h.update(code.encode() + b"\n")
     return h.hexdigest()[:16]
 
 

@@ -42,6 +42,11 @@
 // into LDS, where a layout-T tile stays K-major and its MFMA fragments come
 // from gfx950's transposing LDS reads; the loads run one step ahead.
 //
+// Also here: the MXFP4 comparison GEMM (k_gemm_mx, block-scaled FP4 MFMA),
+// the reduce of the tail-split launches (k_splitk_reduce), and a
+// register-only stream of the matrix instructions (k_mfma_sustain) that the
+// bench times for the throughput the chip sustains under load.
+//
 // Lane layout of v_mfma_f32_32x32x16_{f16,bf16}: lane l supplies row (A) or
 // column (B) l % 32 and 8 consecutive k (the "half" l / 32 of the 16-wide
 // step); accumulator j of lane l is row (j/4)*8 + (l/32)*4 + j%4, column l % 32.
