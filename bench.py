@@ -180,8 +180,10 @@ def epilogue_amax_comparison(q, torch, layer, reps=5, rounds=5):
     for name, P, a, out_t, rnd in (("fprop (Y, next X: RNE)", q.FPROP, layer.gx, layer.y, q.RNE),
                                    ("dgrad (dX, previous dY: SR)", q.DGRAD, layer.gdy, layer.dx, q.SR)):
         rows, cols = out_t.shape
-        ops = [q.alloc_nvfp4(rows, cols, q.BLOCK_1X16, device=dev) for _ in range(2)]
-        opsr = [q.alloc_nvfp4(cols, rows, q.BLOCK_1X16, device=dev) for _ in range(2)]
+        ops = [q.alloc_nvfp4(rows, cols, q.BLOCK_1X16, device=dev, layout=layer.layout)
+               for _ in range(2)]
+        opsr = [q.alloc_nvfp4(cols, rows, q.BLOCK_1X16, device=dev, layout=layer.layout)
+                for _ in range(2)]
         am, ar = f32(), f32()
         gemm = lambda: q.nvfp4_gemm(P, a, layer.gw, out=out_t)
         gemm_amax = lambda: q.nvfp4_gemm_amax(P, a, layer.gw, layer.mask, out=out_t, amax=am,
@@ -317,7 +319,7 @@ def quantize_cold(q, torch, layer, reps=20):
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
     aw = torch.empty(1, dtype=torch.float32, device=dev)
     e_x, e_w, e_dy = layer.M * layer.K, layer.N * layer.K, layer.M * layer.N
-    dy_rne = q.alloc_nvfp4(layer.M, layer.N, q.BLOCK_1X16, device=dev)
+    dy_rne = q.alloc_nvfp4(layer.M, layer.N, q.BLOCK_1X16, device=dev, layout=layer.layout)
     enc = lambda e: 2 * e + e // 2 + e // 16
     passes = {
         "amax_X (plain + RHT maxima)": (lambda: q.nvfp4_amax(layer.x, layer.mask, layer.ax, layer.ax_rht), 2 * e_x),
@@ -383,8 +385,9 @@ def small_fprop_latency(q, torch, dev, reps=50):
     X, W = wl.small_fprop(seed=0)
     to_dev = lambda u: torch.from_numpy(u.view(np.int16)).to(dev).view(torch.bfloat16)
     x, w = to_dev(X), to_dev(W)
-    gx = q.alloc_nvfp4(256, 256, q.BLOCK_1X16, device=dev)
-    gw = q.alloc_nvfp4(256, 256, q.BLOCK_16X16, with_transpose=True, device=dev)
+    gx = q.alloc_nvfp4(256, 256, q.BLOCK_1X16, device=dev, layout=q.LAYOUT_INTERLEAVED)
+    gw = q.alloc_nvfp4(256, 256, q.BLOCK_16X16, with_transpose=True, device=dev,
+                       layout=q.LAYOUT_INTERLEAVED)
     y = torch.empty((256, 256), dtype=torch.bfloat16, device=dev)
     steps = {"quant_X": lambda: q.nvfp4_quantize(x, q.BLOCK_1X16, q.RNE, out=gx),
              "quant_W": lambda: q.nvfp4_quantize(w, q.BLOCK_16X16, q.RNE, out=gw),
@@ -522,11 +525,12 @@ def cpu_baseline(data, tokens=M):
 HEADLINE_SCHEDULE = {"layer": (True, True), "mlp": (True, True)}
 
 
-def schedule_name(fused_quant, split_tail, serial_gemms, rht_x_forward=False):
+def schedule_name(fused_quant, split_tail, serial_gemms, rht_x_forward=False, row_major=False):
     return ("dual quantisers (nvfp4_quantize_dual)" if fused_quant else "separate quantisers") + \
         (", RHT(X) encoded before fprop" if rht_x_forward and not fused_quant else "") + \
         (", dgrad then wgrad on one stream" if serial_gemms else ", dgrad || wgrad branch") + \
-        (", tail split (nvfp4_gemm_split)" if split_tail else "")
+        (", tail split (nvfp4_gemm_split)" if split_tail else "") + \
+        (", row-major codes" if row_major else "")
 
 
 def build_layer_step(q, torch, dev, fused_quant=False, split_tail=False, serial_gemms=False):
@@ -546,14 +550,16 @@ def as_mxfp4(q, torch, dev, step):
 
 
 def with_schedule(q, torch, dev, step, fused_quant, split_tail=False, serial_gemms=False,
-                  rht_x_forward=False):
+                  rht_x_forward=False, layout=None):
     """The same step over the same tensors, with the NVFP4 layers' quantisers
     fused (nvfp4_quantize_dual) or separate, dgrad / wgrad through
     nvfp4_gemm_split (split_tail) or nvfp4_gemm, the two backward GEMMs
-    concurrent on two streams or one after the other (serial_gemms), and X's
-    RHT operand encoded in the forward part or in the wgrad branch."""
+    concurrent on two streams or one after the other (serial_gemms), X's
+    RHT operand encoded in the forward part or in the wgrad branch, and the
+    codes in the given layout (default: the layers' own, interleaved)."""
     from quantize_precision_gemm_amd.step import NVFP4Linear, TrainingStep
-    layers = [NVFP4Linear(q, torch, l.x, l.w, l.dy, l.seed, fused_quant, split_tail, rht_x_forward)
+    layers = [NVFP4Linear(q, torch, l.x, l.w, l.dy, l.seed, fused_quant, split_tail, rht_x_forward,
+                          layout)
               if isinstance(l, NVFP4Linear) else l for l in step.layers]
     return TrainingStep(torch, layers, dev, serial_gemms)
 
@@ -677,6 +683,13 @@ def main():
         other = with_schedule(q, torch, dev, step, False, head_split, head_serial, True)
         sched_ms[schedule_name(False, head_split, head_serial, True)] = timed_steps(other)
         del other
+    # the headline schedule with every NVFP4 tensor's codes row-major (the
+    # GEMMs then touch a quarter of a cache line per row and K step)
+    other = with_schedule(q, torch, dev, step, args.fused_quant, head_split, head_serial,
+                          layout=q.LAYOUT_ROW_MAJOR)
+    sched_ms[schedule_name(args.fused_quant, head_split, head_serial, row_major=True)] = \
+        timed_steps(other)
+    del other
     # the GEMMs of the tail-split step serialised, events around each
     spl = with_schedule(q, torch, dev, step, args.fused_quant, True, False)
     split_ops = {}

@@ -29,7 +29,9 @@
  *   - Inputs must be finite; NaN or Inf inputs give unspecified codes.
  *   - bf16 data is passed as its 16-bit patterns (uint16).
  *   - Packed codes: element (r, c) of a rows x cols NVFP4 matrix is the
- *     4-bit code in byte codes[r * ld_codes + c / 2], low nibble for even c.
+ *     4-bit code in byte j = c / 2 of code row r, low nibble for even c;
+ *     where that byte lies is the tensor's code layout (nvfp4_tensor.layout:
+ *     codes[r * ld_codes + j] in the row-major layout).
  *     Code = sign << 3 | exponent << 1 | mantissa (OCP E2M1: values 0, 0.5,
  *     1, 1.5, 2, 3, 4, 6).  Scales are OCP E4M3 bytes (bias 7, max 448).
  *   - The value an NVFP4 element stands for is  e2m1(code) * e4m3(scale) /
@@ -77,6 +79,10 @@ extern "C" {
 #define NVFP4_OUT_BF16 0
 #define NVFP4_OUT_FP32 1
 
+/* Code layouts (nvfp4_tensor.layout; the scales are row-major in both). */
+#define NVFP4_LAYOUT_ROW_MAJOR 0   /* byte j of code row r at r * ld + j */
+#define NVFP4_LAYOUT_INTERLEAVED 1 /* rows interleaved by 4 in 32-byte pieces (below) */
+
 /*
  * Descriptor of an NVFP4 tensor (rows x cols, blocks along cols).
  * The caller allocates the buffers and fills the pointer and leading
@@ -95,6 +101,22 @@ extern "C" {
  *             at least rows / 16).  Needed by the DGRAD GEMM.
  *   amax      1 float: max |x| over the tensor as quantised.
  *   s_enc     1 float: the tensor's FP32 encode scale.
+ *   layout    where the bytes of codes and codes_t lie (the caller sets it;
+ *             the quantisers write that layout and the GEMMs read it):
+ *             NVFP4_LAYOUT_ROW_MAJOR: byte j of code row r at
+ *               codes[r * ld_codes + j];
+ *             NVFP4_LAYOUT_INTERLEAVED: code rows in groups of 4, each
+ *               128-byte piece holding 32 bytes (64 codes) of the 4 rows in
+ *               turn: byte j of row r at codes[(r / 4) * 4 * ld_codes +
+ *               (j / 32) * 128 + (r % 4) * 32 + j % 32].  ld_codes (and
+ *               ld_codes_t) must be a multiple of 32, and codes must hold
+ *               round_up(rows, 4) rows (codes_t round_up(cols, 4)); the
+ *               padding rows are neither written nor read.  A 64-element K
+ *               step of 4 rows is then one 128-byte cache line, which the
+ *               NVFP4 GEMMs read whole (the row-major layout makes them touch
+ *               a quarter of a line per row and step).
+ *             Any other value: NVFP4_ERR_MODE.  The MXFP4 entry points take
+ *             the row-major layout only.
  */
 typedef struct nvfp4_tensor {
     uint8_t* codes;
@@ -110,7 +132,7 @@ typedef struct nvfp4_tensor {
     int64_t ld_codes_t;
     int64_t ld_scales_t;
     int32_t block;
-    int32_t reserved;
+    int32_t layout;
 } nvfp4_tensor;
 
 /*

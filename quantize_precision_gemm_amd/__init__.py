@@ -23,6 +23,7 @@ __all__ = [
     "nvfp4_rht_sign_mask", "nvfp4_amax", "nvfp4_bf16_gemm", "nvfp4_mx_quantize",
     "nvfp4_mx_gemm", "nvfp4_rht_quantize_sized", "nvfp4_rht_signs64", "nvfp4_quantize_rht_rows", "BLOCK_MX32", "MX_ROWS", "MX_COLS", "MX_COLS_RHT", "nvfp4_gemm_fp8blk", "nvfp4_gemm_amax", "nvfp4_gemm_split", "nvfp4_gemm_split_workspace", "nvfp4_gemm_split_noalloc",
     "nvfp4_mfma_sustain", "MFMA_SUSTAIN_DECODED", "MFMA_SUSTAIN_RANDOM", "MFMA_SUSTAIN_FP4",
+    "LAYOUT_ROW_MAJOR", "LAYOUT_INTERLEAVED", "interleave_codes", "deinterleave_codes",
     "lib_path", "load_library",
 ]
 
@@ -32,6 +33,10 @@ BLOCK_MX32 = 2     # MXFP4 comparison format: 32-element blocks, UE8M0 scales
 MX_ROWS = 0        # nvfp4_mx_quantize layouts
 MX_COLS = 1
 MX_COLS_RHT = 2
+# Code layouts (nvfp4_tensor.layout): row-major, or code rows interleaved by 4
+# in 32-byte pieces, so that one 64-element K step of 4 rows is a 128-byte line.
+LAYOUT_ROW_MAJOR = 0
+LAYOUT_INTERLEAVED = 1
 RNE = 0
 SR = 1
 FPROP = 0
@@ -60,7 +65,7 @@ class _Desc(ctypes.Structure):
         ("rows", ctypes.c_int64), ("cols", ctypes.c_int64),
         ("ld_codes", ctypes.c_int64), ("ld_scales", ctypes.c_int64),
         ("ld_codes_t", ctypes.c_int64), ("ld_scales_t", ctypes.c_int64),
-        ("block", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("block", ctypes.c_int32), ("layout", ctypes.c_int32),
     ]
 
 
@@ -140,17 +145,21 @@ def _stream(stream=None):
 class NVFP4Tensor:
     """Device buffers of an NVFP4 tensor (rows x cols, blocks along cols).
 
-    codes  uint8 [rows, ld_codes]     two E2M1 codes per byte, low nibble first
-    scales uint8 [rows or rows/16, ld_scales]   E4M3 block scales
-    codes_t / scales_t  (16x16 only, optional) the transposed copy used by dgrad
+    codes  uint8 [rows, ld_codes]     two E2M1 codes per byte, low nibble first;
+           row-major, or (layout LAYOUT_INTERLEAVED) [round_up(rows, 4), ld_codes]
+           bytes holding the code rows interleaved by 4 (interleave_codes)
+    scales uint8 [rows or rows/16, ld_scales]   E4M3 block scales (row-major)
+    codes_t / scales_t  (16x16 only, optional) the transposed copy used by dgrad,
+           codes_t in the same layout as codes
     amax, s_enc  float32 [1]  tensor amax and FP32 encode scale (device)
     """
 
     def __init__(self, codes, scales, amax, s_enc, rows, cols, block, codes_t=None,
-                 scales_t=None):
+                 scales_t=None, layout=LAYOUT_ROW_MAJOR):
         self.codes, self.scales, self.amax, self.s_enc = codes, scales, amax, s_enc
         self.codes_t, self.scales_t = codes_t, scales_t
         self.rows, self.cols, self.block = rows, cols, block
+        self.layout = layout
 
     def descriptor(self) -> _Desc:
         d = _Desc()
@@ -163,39 +172,82 @@ class NVFP4Tensor:
         d.ld_codes_t = self.codes_t.shape[1] if self.codes_t is not None else 0
         d.ld_scales_t = self.scales_t.shape[1] if self.scales_t is not None else 0
         d.block = self.block
+        d.layout = self.layout
         return d
 
-    # --- host copies in the tight layout (for checks) ---
+    # --- host copies in the tight row-major layout (for checks) ---
     def codes_host(self):
-        return self.codes[:, : self.cols // 2].cpu().numpy()
+        c = self.codes.cpu().numpy()
+        if self.layout == LAYOUT_INTERLEAVED:
+            c = deinterleave_codes(c, self.rows)
+        return c[: self.rows, : self.cols // 2]
 
     def scales_host(self):
         per = 32 if self.block == BLOCK_MX32 else 16
         return self.scales[:, : self.cols // per].cpu().numpy()
 
     def codes_t_host(self):
-        return self.codes_t[:, : self.rows // 2].cpu().numpy()
+        c = self.codes_t.cpu().numpy()
+        if self.layout == LAYOUT_INTERLEAVED:
+            c = deinterleave_codes(c, self.cols)
+        return c[: self.cols, : self.rows // 2]
 
     def scales_t_host(self):
         return self.scales_t[:, : self.rows // 16].cpu().numpy()
 
 
-def alloc_nvfp4(rows, cols, block=BLOCK_1X16, with_transpose=False, device=None):
+def _code_buf_shape(rows, cols, layout):
+    """(buffer rows, ld bytes) of the codes of a rows x cols tensor."""
+    if layout == LAYOUT_INTERLEAVED:
+        return _round_up(rows, 4), _round_up(cols, 64) // 2
+    return rows, _round_up(cols, 32) // 2
+
+
+def alloc_nvfp4(rows, cols, block=BLOCK_1X16, with_transpose=False, device=None,
+                layout=LAYOUT_ROW_MAJOR):
     """Allocate the device buffers of a rows x cols NVFP4 tensor (padded leading dims)."""
     device = device or torch.device("cuda", torch.cuda.current_device())
-    ld_c = _round_up(cols, 32) // 2
+    if layout not in (LAYOUT_ROW_MAJOR, LAYOUT_INTERLEAVED):
+        raise ValueError(f"unknown code layout {layout}")
+    if block == BLOCK_MX32 and layout != LAYOUT_ROW_MAJOR:
+        raise ValueError("MXFP4 tensors are row-major")
     ld_s = _round_up(max(cols // (32 if block == BLOCK_MX32 else 16), 1), 4)
     srows = rows // 16 if block == BLOCK_16X16 else rows
-    codes = torch.empty((rows, ld_c), dtype=torch.uint8, device=device)
+    codes = torch.empty(_code_buf_shape(rows, cols, layout), dtype=torch.uint8, device=device)
     scales = torch.empty((srows, ld_s), dtype=torch.uint8, device=device)
     amax = torch.empty(1, dtype=torch.float32, device=device)
     s_enc = torch.empty(1, dtype=torch.float32, device=device)
     ct = st = None
     if with_transpose:
-        ct = torch.empty((cols, _round_up(rows, 32) // 2), dtype=torch.uint8, device=device)
+        ct = torch.empty(_code_buf_shape(cols, rows, layout), dtype=torch.uint8, device=device)
         st = torch.empty((cols // 16, _round_up(max(rows // 16, 1), 4)), dtype=torch.uint8,
                          device=device)
-    return NVFP4Tensor(codes, scales, amax, s_enc, rows, cols, block, ct, st)
+    return NVFP4Tensor(codes, scales, amax, s_enc, rows, cols, block, ct, st, layout)
+
+
+def interleave_codes(codes):
+    """Row-major code rows (numpy uint8 [rows, ld], ld a multiple of 32) in the
+    interleaved layout: [round_up(rows, 4), ld] bytes in which byte j of row r
+    lies at flat offset (r // 4) * 4 * ld + (j // 32) * 128 + (r % 4) * 32 + j % 32
+    (padding rows zero)."""
+    import numpy as np
+    rows, ld = codes.shape
+    if ld % 32:
+        raise ValueError("interleaved code rows are a multiple of 32 bytes")
+    pad = np.zeros((_round_up(rows, 4), ld), dtype=np.uint8)
+    pad[:rows] = codes
+    g = pad.reshape(-1, 4, ld // 32, 32).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(g).reshape(-1, ld)
+
+
+def deinterleave_codes(buf, rows):
+    """The inverse of interleave_codes: the first `rows` code rows, row-major."""
+    import numpy as np
+    n, ld = buf.shape
+    if n % 4 or ld % 32:
+        raise ValueError("an interleaved codes buffer has whole 4-row groups of 32-byte pieces")
+    g = np.ascontiguousarray(buf).reshape(-1, ld // 32, 4, 32).transpose(0, 2, 1, 3)
+    return np.ascontiguousarray(g).reshape(-1, ld)[:rows]
 
 
 def _check_bf16(x):
@@ -244,7 +296,16 @@ def _check_nvfp4_buffers(t, rows, cols, block, device, with_transpose=False, wha
     device = t.codes.device
     per = 32 if block == BLOCK_MX32 else 16
     srows = rows // 16 if block == BLOCK_16X16 else rows
-    _check_buf(t.codes, f"{what}.codes", device, torch.uint8, (rows, _round_up(cols, 32) // 2))
+    layout = getattr(t, "layout", LAYOUT_ROW_MAJOR)
+    if layout not in (LAYOUT_ROW_MAJOR, LAYOUT_INTERLEAVED):
+        raise ValueError(f"{what}: unknown code layout {layout}")
+    if block == BLOCK_MX32 and layout != LAYOUT_ROW_MAJOR:
+        raise ValueError(f"{what}: MXFP4 tensors are row-major")
+    il = layout == LAYOUT_INTERLEAVED
+    if il and t.codes.dim() == 2 and t.codes.shape[1] % 32:
+        raise ValueError(f"{what}.codes: interleaved code rows must be a multiple of 32 bytes")
+    _check_buf(t.codes, f"{what}.codes", device, torch.uint8,
+               (_round_up(rows, 4) if il else rows, _round_up(cols, 32) // 2))
     _check_buf(t.scales, f"{what}.scales", device, torch.uint8, (srows, cols // per))
     if block != BLOCK_MX32:
         _check_buf(t.amax, f"{what}.amax", device, torch.float32, (1,))
@@ -252,7 +313,10 @@ def _check_nvfp4_buffers(t, rows, cols, block, device, with_transpose=False, wha
     if with_transpose:
         if t.codes_t is None or t.scales_t is None:
             raise ValueError(f"{what}: the transposed copy was asked for but has no buffers")
-        _check_buf(t.codes_t, f"{what}.codes_t", device, torch.uint8, (cols, _round_up(rows, 32) // 2))
+        if il and t.codes_t.dim() == 2 and t.codes_t.shape[1] % 32:
+            raise ValueError(f"{what}.codes_t: interleaved code rows must be a multiple of 32 bytes")
+        _check_buf(t.codes_t, f"{what}.codes_t", device, torch.uint8,
+                   (_round_up(cols, 4) if il else cols, _round_up(rows, 32) // 2))
         _check_buf(t.scales_t, f"{what}.scales_t", device, torch.uint8, (cols // 16, rows // 16))
 
 
@@ -282,12 +346,13 @@ def _check_scalar_out(t, what, device):
 
 
 def nvfp4_quantize(x, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None,
-                   with_transpose=False, out=None, stream=None):
+                   with_transpose=False, out=None, layout=LAYOUT_ROW_MAJOR, stream=None):
     """Quantise a row-major bf16 matrix to NVFP4 (see nvfp4_quantize in nvfp4.h)."""
     _check_bf16(x)
     rows, cols = x.shape
     if out is None:
-        out = alloc_nvfp4(rows, cols, block, with_transpose and block == BLOCK_16X16, x.device)
+        out = alloc_nvfp4(rows, cols, block, with_transpose and block == BLOCK_16X16, x.device,
+                          layout)
     _check_nvfp4_buffers(out, rows, cols, block, x.device,
                          out.codes_t is not None or out.scales_t is not None)
     _check_scalar_out(amax_in, "amax_in", x.device)
@@ -299,12 +364,13 @@ def nvfp4_quantize(x, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None,
     return out
 
 
-def nvfp4_rht_quantize(x, sign_mask, rounding=RNE, seed=0, amax_in=None, out=None, stream=None):
+def nvfp4_rht_quantize(x, sign_mask, rounding=RNE, seed=0, amax_in=None, out=None,
+                       layout=LAYOUT_ROW_MAJOR, stream=None):
     """RHT along tokens + transpose + 1x16 quantisation (see nvfp4_rht_quantize)."""
     _check_bf16(x)
     tokens, channels = x.shape
     if out is None:
-        out = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device)
+        out = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device, layout)
     _check_nvfp4_buffers(out, channels, tokens, BLOCK_1X16, x.device)
     _check_scalar_out(amax_in, "amax_in", x.device)
     d = out.descriptor()
@@ -317,7 +383,8 @@ def nvfp4_rht_quantize(x, sign_mask, rounding=RNE, seed=0, amax_in=None, out=Non
 
 
 def nvfp4_quantize_dual(x, sign_mask, rounding=RNE, seed=0, seed_rht=0, amax_in=None,
-                        amax_rht_in=None, out=None, out_rht=None, stream=None):
+                        amax_rht_in=None, out=None, out_rht=None, layout=LAYOUT_ROW_MAJOR,
+                        stream=None):
     """Both operands of one tensor from one read (see nvfp4_quantize_dual).
 
     Returns (the 1x16 tokens x channels operand, the RHT-transposed
@@ -325,9 +392,9 @@ def nvfp4_quantize_dual(x, sign_mask, rounding=RNE, seed=0, seed_rht=0, amax_in=
     _check_bf16(x)
     tokens, channels = x.shape
     if out is None:
-        out = alloc_nvfp4(tokens, channels, BLOCK_1X16, False, x.device)
+        out = alloc_nvfp4(tokens, channels, BLOCK_1X16, False, x.device, layout)
     if out_rht is None:
-        out_rht = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device)
+        out_rht = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device, layout)
     _check_nvfp4_buffers(out, tokens, channels, BLOCK_1X16, x.device)
     _check_nvfp4_buffers(out_rht, channels, tokens, BLOCK_1X16, x.device, what="out_rht")
     _check_scalar_out(amax_in, "amax_in", x.device)
@@ -345,13 +412,13 @@ def nvfp4_quantize_dual(x, sign_mask, rounding=RNE, seed=0, seed_rht=0, amax_in=
 
 
 def nvfp4_quantize_rht_rows(x, sign_mask, block=BLOCK_1X16, rounding=RNE, seed=0, amax_in=None,
-                            with_transpose=False, out=None, stream=None):
+                            with_transpose=False, out=None, layout=LAYOUT_ROW_MAJOR, stream=None):
     """nvfp4_quantize after the 16-point RHT along the rows (see
     nvfp4_quantize_rht_rows in nvfp4.h)."""
     _check_bf16(x)
     rows, cols = x.shape
     if out is None:
-        out = alloc_nvfp4(rows, cols, block, with_transpose and block == BLOCK_16X16, x.device)
+        out = alloc_nvfp4(rows, cols, block, with_transpose and block == BLOCK_16X16, x.device, layout)
     _check_nvfp4_buffers(out, rows, cols, block, x.device,
                          out.codes_t is not None or out.scales_t is not None)
     _check_scalar_out(amax_in, "amax_in", x.device)
@@ -365,13 +432,13 @@ def nvfp4_quantize_rht_rows(x, sign_mask, block=BLOCK_1X16, rounding=RNE, seed=0
 
 
 def nvfp4_rht_quantize_sized(x, size, signs, rounding=RNE, seed=0, amax_in=None, out=None,
-                             stream=None):
+                             layout=LAYOUT_ROW_MAJOR, stream=None):
     """Wgrad operand with a `size`-token transform: 1 (none), 4, 16 or 64
     (see nvfp4_rht_quantize_sized in nvfp4.h)."""
     _check_bf16(x)
     tokens, channels = x.shape
     if out is None:
-        out = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device)
+        out = alloc_nvfp4(channels, tokens, BLOCK_1X16, False, x.device, layout)
     _check_nvfp4_buffers(out, channels, tokens, BLOCK_1X16, x.device)
     _check_scalar_out(amax_in, "amax_in", x.device)
     d = out.descriptor()

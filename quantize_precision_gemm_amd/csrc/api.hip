@@ -17,6 +17,18 @@ inline bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintp
 
 inline int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 
+// The code layout of a descriptor: a known value, and for the interleaved
+// layout code rows of whole 32-byte pieces.
+int check_layout(const nvfp4_tensor* t, bool with_t)
+{
+    if (t->layout == NVFP4_LAYOUT_ROW_MAJOR) return NVFP4_OK;
+    if (t->layout != NVFP4_LAYOUT_INTERLEAVED) return NVFP4_ERR_MODE;
+    if (t->ld_codes % 32 != 0 || (with_t && t->ld_codes_t % 32 != 0)) return NVFP4_ERR_ALIGN;
+    return NVFP4_OK;
+}
+
+inline bool interleaved(const nvfp4_tensor* t) { return t->layout == NVFP4_LAYOUT_INTERLEAVED; }
+
 int launch_status()
 {
     hipError_t e = hipGetLastError();
@@ -33,6 +45,8 @@ int check_out(const nvfp4_tensor* o, int64_t rows, int64_t cols, int block)
     if (!aligned(o->scales, 4) || o->ld_scales % 4 != 0) return NVFP4_ERR_ALIGN;
     if (!aligned(o->amax, 4) || !aligned(o->s_enc, 4)) return NVFP4_ERR_ALIGN;
     if (o->ld_codes < round_up(cols, 32) / 2 || o->ld_scales < cols / 16) return NVFP4_ERR_SHAPE;
+    const int lst = check_layout(o, o->codes_t != nullptr);
+    if (lst != NVFP4_OK) return lst;
     if (o->codes_t || o->scales_t) {
         if (block != NVFP4_BLOCK_16X16) return NVFP4_ERR_MODE;
         if (!empty && (!o->codes_t || !o->scales_t)) return NVFP4_ERR_NULL;
@@ -57,6 +71,7 @@ QOut qout_of(const nvfp4_tensor* o)
     q.ld_scales_t = o->ld_scales_t;
     q.amax = o->amax;
     q.s_enc = o->s_enc;
+    q.il = interleaved(o);
     return q;
 }
 
@@ -73,7 +88,7 @@ int check_operand(const nvfp4_tensor* t)
     if (!aligned(t->scales, 4) || t->ld_scales % 4 != 0) return NVFP4_ERR_ALIGN;
     if (t->ld_codes < round_up(t->cols, 32) / 2 || t->ld_scales < t->cols / 16)
         return NVFP4_ERR_SHAPE;
-    return NVFP4_OK;
+    return check_layout(t, false);
 }
 
 
@@ -84,6 +99,7 @@ int check_mx(const nvfp4_tensor* t, int64_t rows, int64_t cols)
     if (!t) return NVFP4_ERR_NULL;
     if (rows > 0 && cols > 0 && (!t->codes || !t->scales)) return NVFP4_ERR_NULL;
     if (t->codes_t || t->scales_t) return NVFP4_ERR_MODE;
+    if (t->layout != NVFP4_LAYOUT_ROW_MAJOR) return NVFP4_ERR_MODE;
     if (!aligned(t->codes, 16) || t->ld_codes % 16 != 0) return NVFP4_ERR_ALIGN;
     if (!aligned(t->scales, 4) || t->ld_scales % 4 != 0) return NVFP4_ERR_ALIGN;
     if (t->ld_codes < round_up(cols, 32) / 2 || t->ld_scales < cols / 32) return NVFP4_ERR_SHAPE;
@@ -326,7 +342,7 @@ int resolve_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, Gem
     if (st != NVFP4_OK) return st;
     if (a->block != NVFP4_BLOCK_1X16) return NVFP4_ERR_MISMATCH;
 
-    A = GemmOperand{a->codes, a->ld_codes, a->scales, a->ld_scales, 0, a->s_enc};
+    A = GemmOperand{a->codes, a->ld_codes, a->scales, a->ld_scales, 0, a->s_enc, interleaved(a)};
     M = a->rows;
     K = a->cols;
     if (pass == NVFP4_DGRAD) {
@@ -336,21 +352,24 @@ int resolve_gemm(int32_t pass, const nvfp4_tensor* a, const nvfp4_tensor* b, Gem
         if (b->rows != a->cols) return NVFP4_ERR_MISMATCH;
         if (!aligned(b->codes_t, 16) || b->ld_codes_t % 16 != 0) return NVFP4_ERR_ALIGN;
         if (!aligned(b->scales_t, 4) || b->ld_scales_t % 4 != 0) return NVFP4_ERR_ALIGN;
+        if (interleaved(b) && b->ld_codes_t % 32 != 0) return NVFP4_ERR_ALIGN;
         if (b->ld_codes_t < round_up(b->rows, 32) / 2 || b->ld_scales_t < b->rows / 16)
             return NVFP4_ERR_SHAPE;
-        B = GemmOperand{b->codes_t, b->ld_codes_t, b->scales_t, b->ld_scales_t, 4, b->s_enc};
+        B = GemmOperand{b->codes_t, b->ld_codes_t, b->scales_t, b->ld_scales_t, 4, b->s_enc,
+                        interleaved(b)};
         N = b->cols;
     } else {
         if (b->cols != a->cols) return NVFP4_ERR_MISMATCH;
         if (pass == NVFP4_WGRAD && b->block != NVFP4_BLOCK_1X16) return NVFP4_ERR_MISMATCH;
         B = GemmOperand{b->codes, b->ld_codes, b->scales, b->ld_scales,
-                        b->block == NVFP4_BLOCK_16X16 ? 4 : 0, b->s_enc};
+                        b->block == NVFP4_BLOCK_16X16 ? 4 : 0, b->s_enc, interleaved(b)};
         N = b->rows;
     }
     // the kernels address an operand's codes and scales with 32-bit offsets
     const int64_t span = int64_t(1) << 32;
     const int64_t b_scale_rows = B.scale_row_shift ? (N + 15) >> 4 : N;
-    if (M * A.ld_codes > span || N * B.ld_codes > span || M * A.ld_scales > span ||
+    const int64_t a_code_rows = A.il ? round_up(M, 4) : M, b_code_rows = B.il ? round_up(N, 4) : N;
+    if (a_code_rows * A.ld_codes > span || b_code_rows * B.ld_codes > span || M * A.ld_scales > span ||
         b_scale_rows * B.ld_scales > span)
         return NVFP4_ERR_SHAPE;
     return NVFP4_OK;

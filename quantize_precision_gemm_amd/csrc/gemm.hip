@@ -75,7 +75,16 @@ struct OpArgs {
     int64_t ld_scales;
     int scale_shift;        // NVFP4: scale row = row >> scale_shift
     const float* s_enc;     // NVFP4: tensor encode scale
+    int64_t kst;            // NVFP4: code bytes from one 64-element K step of a row to the next
+    bool il;                // NVFP4: codes 4-row interleaved (code_offset)
 };
+
+// The kernel arguments of an NVFP4 operand of k_gemm_nv.
+OpArgs nv_args(const GemmOperand& g)
+{
+    return OpArgs{g.codes, g.ld_codes, g.scales, g.ld_scales, g.scale_row_shift, g.s_enc,
+                  g.il ? 128 : 32, g.il};
+}
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f)
 {
@@ -380,8 +389,8 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
         const int64_t nst = (K + kKS - 1) / kKS;
         const int64_t s0 = nst * part / split, s1 = nst * (part + 1) / split;
         const int64_t k0 = s0 * kKS, k1 = s1 * kKS < K ? s1 * kKS : K;
-        A.data = static_cast<const uint8_t*>(A.data) + (k0 >> 1);
-        B.data = static_cast<const uint8_t*>(B.data) + (k0 >> 1);
+        A.data = static_cast<const uint8_t*>(A.data) + s0 * A.kst;
+        B.data = static_cast<const uint8_t*>(B.data) + s0 * B.kst;
         A.scales += k0 >> 4;
         B.scales += k0 >> 4;
         K = k1 - k0;
@@ -397,22 +406,22 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
     // scales each span less than 4 GiB (the ABI checks it).
     const uint8_t* const Ad = static_cast<const uint8_t*>(A.data);
     const uint8_t* const Bd = static_cast<const uint8_t*>(B.data);
-    const uint32_t oa = (uint32_t)(ra * A.ld) + 16u * h;           // codes of the half row
+    const uint32_t oa = (uint32_t)code_offset(ra, 16 * h, A.ld, A.il);  // codes of the half row
     const uint32_t qa = (uint32_t)((ra >> A.scale_shift) * A.ld_scales);  // the row's scales
     uint32_t ob[kRB], qb[kRB];
 #pragma unroll
     for (int j = 0; j < kRB; ++j) {
         int64_t rb = tile_n * kBN + row + kTM * j;
         rb = rb < N ? rb : N - 1;
-        ob[j] = (uint32_t)(rb * B.ld) + 16u * h;
+        ob[j] = (uint32_t)code_offset(rb, 16 * h, B.ld, B.il);
         qb[j] = (uint32_t)((rb >> B.scale_shift) * B.ld_scales);
     }
     const int64_t nblk = K >> 4;
 
     auto load_full = [&](int64_t k0, NvRow<kRB>& w) {
-        w.ca = *reinterpret_cast<const uint4*>(Ad + (k0 >> 1) + oa);
+        w.ca = *reinterpret_cast<const uint4*>(Ad + (k0 >> 6) * A.kst + oa);
 #pragma unroll
-        for (int j = 0; j < kRB; ++j) w.cb[j] = *reinterpret_cast<const uint4*>(Bd + (k0 >> 1) + ob[j]);
+        for (int j = 0; j < kRB; ++j) w.cb[j] = *reinterpret_cast<const uint4*>(Bd + (k0 >> 6) * B.kst + ob[j]);
         w.sa = *reinterpret_cast<const uint16_t*>(A.scales + (k0 >> 4) + (qa + 2u * h));
 #pragma unroll
         for (int j = 0; j < kRB; ++j)
@@ -423,14 +432,14 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
     // inside the row, whose length is rounded up to 32 codes)
     auto load_tail = [&](int64_t k0, NvRow<kRB>& w) {
         const int64_t b0 = (k0 >> 4) + 2 * h;
-        w.ca = b0 < nblk ? *reinterpret_cast<const uint4*>(Ad + (k0 >> 1) + oa) : make_uint4(0, 0, 0, 0);
+        w.ca = b0 < nblk ? *reinterpret_cast<const uint4*>(Ad + (k0 >> 6) * A.kst + oa) : make_uint4(0, 0, 0, 0);
         uint32_t sa = 0u;
         for (int i = 0; i < 2; ++i)
             if (b0 + i < nblk) sa |= (uint32_t)A.scales[b0 + i + qa] << (8 * i);
         w.sa = sa;
 #pragma unroll
         for (int j = 0; j < kRB; ++j) {
-            w.cb[j] = b0 < nblk ? *reinterpret_cast<const uint4*>(Bd + (k0 >> 1) + ob[j]) : make_uint4(0, 0, 0, 0);
+            w.cb[j] = b0 < nblk ? *reinterpret_cast<const uint4*>(Bd + (k0 >> 6) * B.kst + ob[j]) : make_uint4(0, 0, 0, 0);
             uint32_t sb = 0u;
             for (int i = 0; i < 2; ++i)
                 if (b0 + i < nblk) sb |= (uint32_t)B.scales[b0 + i + qb[j]] << (8 * i);
@@ -574,9 +583,9 @@ __global__ __launch_bounds__(2 * kTM, 256 / kTM) void k_gemm_nv(OpArgs A, OpArgs
             NvRow<kRB>& done = r == 0 ? g0 : (r == 1 ? g1 : g2);  // step t, already in LDS
             NvRow<kRB>& next = r == 0 ? g1 : (r == 1 ? g2 : g0);  // step t + 1
             const int64_t k3 = (t + 3) * kKS;  // a whole step: t + 3 < nfull
-            done.ca = *reinterpret_cast<const uint4*>(Ad + (k3 >> 1) + oa);
+            done.ca = *reinterpret_cast<const uint4*>(Ad + (k3 >> 6) * A.kst + oa);
 #pragma unroll
-            for (int j = 0; j < kRB; ++j) done.cb[j] = *reinterpret_cast<const uint4*>(Bd + (k3 >> 1) + ob[j]);
+            for (int j = 0; j < kRB; ++j) done.cb[j] = *reinterpret_cast<const uint4*>(Bd + (k3 >> 6) * B.kst + ob[j]);
             if constexpr (r == 0) {
                 Na = *reinterpret_cast<const uint3*>(A.scales + 4 * (t + 3) + qa);
 #pragma unroll
@@ -1250,8 +1259,7 @@ void launch_gemm_nt(const GemmOperand& a, const GemmOperand& b, int64_t M, int64
 {
     if (M == 0 || N == 0) return;
     if (K == 0) return launch_fill_zero(M, N, c, ldc, out_fp32, s);
-    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc};
-    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc};
+    const OpArgs A = nv_args(a), B = nv_args(b);
     const dim3 grid = tile_grid(M, N, kNvTM), block(2 * kNvTM);
     if (out_fp32)
         hipLaunchKernelGGL((k_gemm_nv<kNvTM, true>), grid, block, 0, s, A, B, M, N, K, c, ldc);
@@ -1368,8 +1376,7 @@ void launch_gemm_nt_split(const GemmOperand& a, const GemmOperand& b, int64_t M,
                           int64_t full_tiles, int split, hipStream_t s)
 {
     if (split < 2) return launch_gemm_nt(a, b, M, N, K, c, ldc, out_fp32, s);
-    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc};
-    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc};
+    const OpArgs A = nv_args(a), B = nv_args(b);
     const int64_t T = ((M + kBM - 1) / kBM) * ((N + kBN - 1) / kBN);
     const int64_t rem = T - full_tiles;
     const dim3 grid((unsigned)(full_tiles + rem * split)), block(512);
@@ -1403,8 +1410,7 @@ void launch_gemm_nt_amax(const GemmOperand& a, const GemmOperand& b, int64_t M, 
     hipLaunchKernelGGL(k_zero_amax, dim3(1), dim3(1), 0, s, ab, rb);
     if (M == 0 || N == 0) return;
     if (K == 0) return launch_fill_zero(M, N, c, ldc, false, s);  // maxima stay 0
-    const OpArgs A{a.codes, a.ld_codes, a.scales, a.ld_scales, a.scale_row_shift, a.s_enc};
-    const OpArgs B{b.codes, b.ld_codes, b.scales, b.ld_scales, b.scale_row_shift, b.s_enc};
+    const OpArgs A = nv_args(a), B = nv_args(b);
     const dim3 grid = tile_grid(M, N, kNvTM), block(2 * kNvTM);
     if (rb)
         hipLaunchKernelGGL((k_gemm_nv<kNvTM, false, 2>), grid, block, 0, s, A, B, M, N, K,

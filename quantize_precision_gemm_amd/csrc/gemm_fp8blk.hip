@@ -99,8 +99,9 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fp8blk(GemmOperand A, GemmOpera
     int64_t ra = tile_m * kT + crow, rb = tile_n * kT + crow;
     ra = ra < M ? ra : M - 1;
     rb = rb < N ? rb : N - 1;
-    const uint8_t* pa = A.codes + ra * A.ld_codes + 16 * chalf;
-    const uint8_t* pb = B.codes + rb * B.ld_codes + 16 * chalf;
+    const uint8_t* pa = A.codes + code_offset(ra, 16 * chalf, A.ld_codes, A.il);
+    const uint8_t* pb = B.codes + code_offset(rb, 16 * chalf, B.ld_codes, B.il);
+    const int64_t ka = A.il ? 128 : 32, kb = B.il ? 128 : 32;  // code bytes per K step of a row
     const bool s_is_b = tid >= kT;
     int64_t rs = (s_is_b ? tile_n : tile_m) * kT + (tid & (kT - 1));
     rs = rs < (s_is_b ? N : M) ? rs : (s_is_b ? N : M) - 1;
@@ -111,13 +112,13 @@ __global__ __launch_bounds__(256, 2) void k_gemm_fp8blk(GemmOperand A, GemmOpera
     auto load = [&](int64_t step, Row16& r) {
         const int64_t b0 = step * 4;
         if (b0 + 4 <= nblk) {
-            r.ca = *reinterpret_cast<const uint4*>(pa + 32 * step);
-            r.cb = *reinterpret_cast<const uint4*>(pb + 32 * step);
+            r.ca = *reinterpret_cast<const uint4*>(pa + ka * step);
+            r.cb = *reinterpret_cast<const uint4*>(pb + kb * step);
             r.s = *reinterpret_cast<const uint32_t*>(ps + b0);
         } else {  // partial last step: blocks past K get zero codes and scales
             const bool in = b0 + 2 * chalf < nblk;  // this thread's two blocks
-            r.ca = in ? *reinterpret_cast<const uint4*>(pa + 32 * step) : make_uint4(0, 0, 0, 0);
-            r.cb = in ? *reinterpret_cast<const uint4*>(pb + 32 * step) : make_uint4(0, 0, 0, 0);
+            r.ca = in ? *reinterpret_cast<const uint4*>(pa + ka * step) : make_uint4(0, 0, 0, 0);
+            r.cb = in ? *reinterpret_cast<const uint4*>(pb + kb * step) : make_uint4(0, 0, 0, 0);
             r.s = 0u;
             for (int j = 0; j < 4; ++j)
                 if (b0 + j < nblk) r.s |= (uint32_t)ps[b0 + j] << (8 * j);

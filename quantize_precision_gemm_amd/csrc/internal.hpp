@@ -19,10 +19,12 @@ struct QOut {
     int64_t ld_scales_t;
     float* amax;
     float* s_enc;
+    bool il;  // codes (and codes_t) 4-row interleaved (code_offset), else row-major
 };
 
-// One GEMM operand: rows x K NVFP4 codes with 16-element blocks along K.
-// The scale of block b of row r is scales[(r >> scale_row_shift) * ld_scales + b].
+// One GEMM operand: rows x K NVFP4 codes with 16-element blocks along K,
+// row-major or 4-row interleaved (il; see code_offset).  The scale of block b
+// of row r is scales[(r >> scale_row_shift) * ld_scales + b].
 struct GemmOperand {
     const uint8_t* codes;
     int64_t ld_codes;
@@ -30,6 +32,7 @@ struct GemmOperand {
     int64_t ld_scales;
     int scale_row_shift;
     const float* s_enc;
+    bool il = false;
 };
 
 void launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,

@@ -28,6 +28,17 @@ typedef float float2_t __attribute__((vector_size(8)));
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
+// Where byte j of code row r lies in a codes buffer with rows ld bytes long.
+// Row-major: r * ld + j.  Interleaved (il): rows in groups of 4, each
+// 128-byte piece holding 32 bytes (64 codes, one K step of the GEMMs) of the
+// 4 rows in turn, so that a K step of 4 rows is one whole cache line:
+// (r / 4) * 4 * ld + (j / 32) * 128 + (r % 4) * 32 + j % 32, ld a multiple of
+// 32.  A write of up to 32 aligned bytes stays inside one piece.
+__device__ __forceinline__ int64_t code_offset(int64_t r, int64_t j, int64_t ld, bool il)
+{
+    return il ? (r >> 2) * 4 * ld + ((j >> 5) << 7) + ((r & 3) << 5) + (j & 31) : r * ld + j;
+}
+
 // |bf16| ordering equals the unsigned ordering of the 15 magnitude bits.
 __device__ __forceinline__ uint32_t bf16_absmax2(uint32_t w)
 {

@@ -189,7 +189,13 @@ __device__ __forceinline__ uint2 encode16_sr(const float (&v)[16], float f, uint
 }
 
 // ---------------------------------------------------------------------------
-// 1x16 quantiser: one thread per 16-element block.
+// 1x16 quantiser: one thread per 16-element block.  A wave covers 4 rows x 16
+// blocks: lane l takes row 4 g + (l / 4) % 4 and block 16 c + 4 (l / 16) +
+// l % 4, so that its codes fill whole 128-byte lines in either code layout
+// (one K step of 4 rows interleaved; 4 row-major rows of 128 bytes) and each
+// row is read in 512-byte runs.  With one row per wave, interleaved pieces of
+// one line came from waves far apart (often on other XCDs, whose L2s each
+// wrote back a part of the line): 30 % slower on the 12B-layer dY.
 // ---------------------------------------------------------------------------
 
 // kRht: the 16-point RHT of the block first (the fprop / dgrad ablation;
@@ -198,10 +204,11 @@ template <bool kSR, bool kRht = false>
 __global__ __launch_bounds__(256) void k_quant_1x16(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
-    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    int64_t ld_codes, bool il, uint8_t* __restrict__ scales, int64_t ld_scales,
     float* __restrict__ amax_out, float* __restrict__ s_enc_out, uint32_t mask = 0u)
 {
     const int64_t nb = cols >> 4;
+    const int64_t nchunk = (nb + 15) >> 4;  // 16-block chunks per row
     const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const float amax = *amax_src;
     const float s_enc = tensor_scale(amax);
@@ -209,9 +216,12 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
         *amax_out = amax;
         *s_enc_out = s_enc;
     }
-    if (t >= rows * nb) return;
-    const int64_t r = t / nb;
-    const int64_t b = t - r * nb;
+    const int l = (int)(t & 63);
+    const int64_t u = t >> 6;                // this wave's (row group, chunk)
+    const int64_t g = u / nchunk, c = u - g * nchunk;
+    const int64_t r = 4 * g + ((l >> 2) & 3);
+    const int64_t b = 16 * c + 4 * (l >> 4) + (l & 3);
+    if (r >= rows || b >= nb) return;
     const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 16);
     float v[16];
     unpack16(ld_stream(src), ld_stream(src + 1), v);
@@ -223,7 +233,7 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
         pk = encode16_sr(v, f, seed, (uint64_t)(r * cols + b * 16) >> 3);
     else
         pk = encode16_rne(v, f);
-    *reinterpret_cast<uint2*>(codes + r * ld_codes + b * 8) = pk;
+    *reinterpret_cast<uint2*>(codes + code_offset(r, b * 8, ld_codes, il)) = pk;
     scales[r * ld_scales + b] = (uint8_t)sb;
 }
 
@@ -245,7 +255,7 @@ template <bool kSR, bool kRht = false>
 __global__ __launch_bounds__(kW2TC * kW2RG) void k_quant_16x16(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
     const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
-    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    int64_t ld_codes, bool il, uint8_t* __restrict__ scales, int64_t ld_scales,
     uint8_t* __restrict__ codes_t, int64_t ld_codes_t, uint8_t* __restrict__ scales_t,
     int64_t ld_scales_t, float* __restrict__ amax_out, float* __restrict__ s_enc_out,
     uint32_t mask = 0u)
@@ -293,7 +303,7 @@ __global__ __launch_bounds__(kW2TC * kW2RG) void k_quant_16x16(
             pk[i] = encode16_sr(v[i], f, seed, (uint64_t)((row0 + i) * cols + col0) >> 3);
         else
             pk[i] = encode16_rne(v[i], f);
-        if (valid) *reinterpret_cast<uint2*>(codes + (row0 + i) * ld_codes + (col0 >> 1)) = pk[i];
+        if (valid) *reinterpret_cast<uint2*>(codes + code_offset(row0 + i, col0 >> 1, ld_codes, il)) = pk[i];
     }
     const int64_t tr = row0 >> 4, tc = col0 >> 4;
     if (valid && (rg & 3) == 0) {
@@ -328,7 +338,7 @@ __global__ __launch_bounds__(kW2TC * kW2RG) void k_quant_16x16(
         const int64_t nrow = (int64_t)blockIdx.y * kW2Rows + q * 32;
         if (kcol < cols && nrow < rows) {
             const uint4 val = *reinterpret_cast<const uint4*>(&tcodes[kr][q * 16]);
-            uint8_t* dst = codes_t + kcol * ld_codes_t + (nrow >> 1);
+            uint8_t* dst = codes_t + code_offset(kcol, nrow >> 1, ld_codes_t, il);
             if (nrow + 32 <= rows) {
                 *reinterpret_cast<uint4*>(dst) = val;
             } else {
@@ -451,7 +461,7 @@ template <bool kSR>
 __global__ __launch_bounds__(256) void k_rht_quant(
     const uint16_t* __restrict__ x, int64_t tokens, int64_t channels, int64_t ld, uint32_t mask,
     const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
-    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    int64_t ld_codes, bool il, uint8_t* __restrict__ scales, int64_t ld_scales,
     float* __restrict__ amax_out, float* __restrict__ s_enc_out)
 {
     __shared__ uint2 scodes[kRhtCh][17];    // [channel][chunk], padded
@@ -495,7 +505,7 @@ __global__ __launch_bounds__(256) void k_rht_quant(
         const int row = idx >> 4, q = idx & 15;
         const int64_t ch = chb + row, tk = tokb + q * 16;
         if (ch < channels && tk < tokens) {
-            *reinterpret_cast<uint2*>(codes + ch * ld_codes + (tk >> 1)) = scodes[row][q];
+            *reinterpret_cast<uint2*>(codes + code_offset(ch, tk >> 1, ld_codes, il)) = scodes[row][q];
             scales[ch * ld_scales + (tk >> 4)] = sscale[row][q];
         }
     }
@@ -582,7 +592,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
                 pk = encode8_sr(v, f, seed, (uint64_t)(tok * channels + ch0) >> 3);
             else
                 pk = encode8_rne(v, f);
-            *reinterpret_cast<uint32_t*>(o.codes + tok * o.ld_codes + (ch0 >> 1)) = pk;
+            *reinterpret_cast<uint32_t*>(o.codes + code_offset(tok, ch0 >> 1, o.ld_codes, o.il)) = pk;
             if ((cg & 1) == 0) o.scales[tok * o.ld_scales + (ch0 >> 4)] = (uint8_t)sb;
         }
 
@@ -610,7 +620,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void k
         const int row = idx >> 4, q = idx & 15;
         const int64_t ch = chb + row, tk = tokb + q * 16;
         if (ch < channels && tk < tokens) {
-            *reinterpret_cast<uint2*>(o_rht.codes + ch * o_rht.ld_codes + (tk >> 1)) = scodes[row][q];
+            *reinterpret_cast<uint2*>(o_rht.codes + code_offset(ch, tk >> 1, o_rht.ld_codes, o_rht.il)) = scodes[row][q];
             o_rht.scales[ch * o_rht.ld_scales + (tk >> 4)] = sscale[row][q];
         }
     }
@@ -698,7 +708,7 @@ template <bool kSR, int D>
 __global__ __launch_bounds__(256) void k_rhtd_quant(
     const uint16_t* __restrict__ x, int64_t tokens, int64_t channels, int64_t ld, uint64_t signs,
     const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
-    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    int64_t ld_codes, bool il, uint8_t* __restrict__ scales, int64_t ld_scales,
     float* __restrict__ amax_out, float* __restrict__ s_enc_out)
 {
     __shared__ uint2 scodes[kRhtCh][17];
@@ -740,7 +750,7 @@ __global__ __launch_bounds__(256) void k_rhtd_quant(
         const int row = idx >> 4, q = idx & 15;
         const int64_t ch = chb + row, tk = tokb + q * 16;
         if (ch < channels && tk < tokens) {
-            *reinterpret_cast<uint2*>(codes + ch * ld_codes + (tk >> 1)) = scodes[row][q];
+            *reinterpret_cast<uint2*>(codes + code_offset(ch, tk >> 1, ld_codes, il)) = scodes[row][q];
             scales[ch * ld_scales + (tk >> 4)] = sscale[row][q];
         }
     }
@@ -888,6 +898,12 @@ static int grid_for(int64_t work, int64_t per_block, int64_t cap)
     return (int)(g < cap ? g : cap);
 }
 
+// Threads of a k_quant_1x16 launch: a wave per 4 rows x 16 blocks.
+static int64_t quant_1x16_threads(int64_t rows, int64_t cols)
+{
+    return ((rows + 3) / 4) * (((cols >> 4) + 15) / 16) * 64;
+}
+
 void launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
                       hipStream_t s)
 {
@@ -913,23 +929,22 @@ void launch_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int
         return;
     }
     if (block == 0) {
-        const int64_t work = rows * (cols >> 4);
-        dim3 g(grid_for(work, 256, INT32_MAX));
+        dim3 g(grid_for(quant_1x16_threads(rows, cols), 256, INT32_MAX));
         if (sr)
             hipLaunchKernelGGL(k_quant_1x16<true>, g, dim3(256), 0, s, x, rows, cols, ld, amax_src,
-                               seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc);
+                               seed, o.codes, o.ld_codes, o.il, o.scales, o.ld_scales, o.amax, o.s_enc);
         else
             hipLaunchKernelGGL(k_quant_1x16<false>, g, dim3(256), 0, s, x, rows, cols, ld, amax_src,
-                               seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc);
+                               seed, o.codes, o.ld_codes, o.il, o.scales, o.ld_scales, o.amax, o.s_enc);
     } else {
         dim3 g((unsigned)((cols + kW2Cols - 1) / kW2Cols), (unsigned)((rows + kW2Rows - 1) / kW2Rows));
         if (sr)
             hipLaunchKernelGGL(k_quant_16x16<true>, g, dim3(kW2TC * kW2RG), 0, s, x, rows, cols, ld,
-                               amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales,
+                               amax_src, seed, o.codes, o.ld_codes, o.il, o.scales, o.ld_scales,
                                o.codes_t, o.ld_codes_t, o.scales_t, o.ld_scales_t, o.amax, o.s_enc);
         else
             hipLaunchKernelGGL(k_quant_16x16<false>, g, dim3(kW2TC * kW2RG), 0, s, x, rows, cols, ld,
-                               amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales,
+                               amax_src, seed, o.codes, o.ld_codes, o.il, o.scales, o.ld_scales,
                                o.codes_t, o.ld_codes_t, o.scales_t, o.ld_scales_t, o.amax, o.s_enc);
     }
 }
@@ -966,11 +981,11 @@ void launch_rht_quant(const uint16_t* x, int64_t tokens, int64_t channels, int64
     dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
     if (rounding == 1)
         hipLaunchKernelGGL(k_rht_quant<true>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
-                           amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax,
+                           amax_src, seed, o.codes, o.ld_codes, o.il, o.scales, o.ld_scales, o.amax,
                            o.s_enc);
     else
         hipLaunchKernelGGL(k_rht_quant<false>, g, dim3(256), 0, s, x, tokens, channels, ld, mask,
-                           amax_src, seed, o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax,
+                           amax_src, seed, o.codes, o.ld_codes, o.il, o.scales, o.ld_scales, o.amax,
                            o.s_enc);
 }
 
@@ -1047,7 +1062,7 @@ void launch_rhtd_quant(const uint16_t* x, int64_t tokens, int64_t channels, int6
     dim3 g((unsigned)((channels + kRhtCh - 1) / kRhtCh), (unsigned)((tokens + kRhtTok - 1) / kRhtTok));
     auto go = [&](auto kern) {
         hipLaunchKernelGGL(kern, g, dim3(256), 0, s, x, tokens, channels, ld, signs, amax_src, seed,
-                           o.codes, o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc);
+                           o.codes, o.ld_codes, o.il, o.scales, o.ld_scales, o.amax, o.s_enc);
     };
     const bool sr = rounding == 1;
     switch (size) {
@@ -1079,17 +1094,17 @@ void launch_quant_rht_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_
         return;
     }
     if (block == 0) {
-        dim3 g(grid_for(rows * (cols >> 4), 256, INT32_MAX));
+        dim3 g(grid_for(quant_1x16_threads(rows, cols), 256, INT32_MAX));
         auto go = [&](auto kern) {
             hipLaunchKernelGGL(kern, g, dim3(256), 0, s, x, rows, cols, ld, amax_src, seed, o.codes,
-                               o.ld_codes, o.scales, o.ld_scales, o.amax, o.s_enc, mask);
+                               o.ld_codes, o.il, o.scales, o.ld_scales, o.amax, o.s_enc, mask);
         };
         sr ? go(k_quant_1x16<true, true>) : go(k_quant_1x16<false, true>);
     } else {
         dim3 g((unsigned)((cols + kW2Cols - 1) / kW2Cols), (unsigned)((rows + kW2Rows - 1) / kW2Rows));
         auto go = [&](auto kern) {
             hipLaunchKernelGGL(kern, g, dim3(kW2TC * kW2RG), 0, s, x, rows, cols, ld, amax_src, seed, o.codes,
-                               o.ld_codes, o.scales, o.ld_scales, o.codes_t, o.ld_codes_t, o.scales_t,
+                               o.ld_codes, o.il, o.scales, o.ld_scales, o.codes_t, o.ld_codes_t, o.scales_t,
                                o.ld_scales_t, o.amax, o.s_enc, mask);
         };
         sr ? go(k_quant_16x16<true, true>) : go(k_quant_16x16<false, true>);

@@ -31,7 +31,7 @@ class NVFP4Linear:
     """
 
     def __init__(self, q, torch, x, w, dy, seed, fused_quant=False, split_tail=False,
-                 rht_x_forward=False):
+                 rht_x_forward=False, layout=None):
         self.q, self.torch = q, torch
         self.fused_quant = fused_quant
         self.split_tail = split_tail
@@ -48,11 +48,15 @@ class NVFP4Linear:
         self.M, self.K, self.N = M, K, N
         dev = x.device
         self.seed = seed
-        self.gx = q.alloc_nvfp4(M, K, q.BLOCK_1X16, device=dev)
-        self.gw = q.alloc_nvfp4(N, K, q.BLOCK_16X16, with_transpose=True, device=dev)
-        self.gdy = q.alloc_nvfp4(M, N, q.BLOCK_1X16, device=dev)
-        self.gdyt = q.alloc_nvfp4(N, M, q.BLOCK_1X16, device=dev)
-        self.gxt = q.alloc_nvfp4(K, M, q.BLOCK_1X16, device=dev)
+        # codes 4-row interleaved unless asked otherwise: the GEMMs then read
+        # each 64-element K step of 4 rows as one whole cache line
+        lay = q.LAYOUT_INTERLEAVED if layout is None else layout
+        self.layout = lay
+        self.gx = q.alloc_nvfp4(M, K, q.BLOCK_1X16, device=dev, layout=lay)
+        self.gw = q.alloc_nvfp4(N, K, q.BLOCK_16X16, with_transpose=True, device=dev, layout=lay)
+        self.gdy = q.alloc_nvfp4(M, N, q.BLOCK_1X16, device=dev, layout=lay)
+        self.gdyt = q.alloc_nvfp4(N, M, q.BLOCK_1X16, device=dev, layout=lay)
+        self.gxt = q.alloc_nvfp4(K, M, q.BLOCK_1X16, device=dev, layout=lay)
         self.y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
         self.dx = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         self.dw = torch.empty((N, K), dtype=torch.float32, device=dev)

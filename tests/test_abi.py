@@ -279,3 +279,50 @@ def test_mfma_sustain_validation(lib):
     assert f(4, 8, 3, FAKE, None) == -4             # unknown operand kind
     assert f(4, 8, -1, FAKE, None) == -4
     assert f(4, 8, 1, FAKE + 2, None) == -3         # misaligned out
+
+
+def test_layout_validation(lib):
+    """The code layout field: unknown values are refused, interleaved code
+    rows must be whole 32-byte pieces, and the MXFP4 entry points take the
+    row-major layout only."""
+    base = dict(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, ld_codes=16, ld_scales=4)
+    q = lambda d: lib.nvfp4_quantize(FAKE, 16, 32, 32, 0, 0, 0, None, ctypes.byref(d), None)
+    assert q(_desc(**base, layout=2)) == -4
+    assert q(_desc(**base, layout=-1)) == -4
+    assert q(_desc(**base, layout=1)) == -3          # 16-byte code rows
+    w = _desc(**dict(base, ld_codes=32, codes_t=FAKE, scales_t=FAKE, ld_codes_t=48, ld_scales_t=4,
+                     layout=1))
+    assert lib.nvfp4_quantize(FAKE, 32, 64, 64, 1, 0, 0, None, ctypes.byref(w), None) == -3
+    r = _desc(**base, layout=1)  # channels x tokens = 16 x 32: 16-byte rows
+    assert lib.nvfp4_rht_quantize(FAKE, 32, 16, 16, 1, 0, 0, None, ctypes.byref(r), None) == -3
+    assert lib.nvfp4_rht_quantize_sized(FAKE, 32, 16, 16, 16, 0, 0, 0, None, ctypes.byref(r),
+                                        None) == -3
+    assert lib.nvfp4_quantize_rht_rows(FAKE, 16, 32, 32, 0, 1, 0, 0, None, ctypes.byref(r),
+                                       None) == -3
+    d = _desc(**dict(base, ld_codes=32))
+    assert lib.nvfp4_quantize_dual(FAKE, 32, 32, 32, 1, 0, 0, 0, None, None, ctypes.byref(d),
+                                   ctypes.byref(_desc(**base, layout=1)), None) == -3
+
+    def op(rows, cols, block=0, **kw):
+        b = dict(codes=FAKE, scales=FAKE, amax=FAKE, s_enc=FAKE, rows=rows, cols=cols,
+                 ld_codes=max(16, ((cols + 31) // 32) * 16), ld_scales=max(4, cols // 16),
+                 block=block)
+        b.update(kw)
+        return _desc(**b)
+    for fn in ("nvfp4_gemm", "nvfp4_gemm_fp8blk"):
+        g = getattr(lib, fn)
+        assert g(0, ctypes.byref(op(32, 32, layout=1)), ctypes.byref(op(48, 32, 1)), FAKE, 64, 0,
+                 None) == -3
+        assert g(0, ctypes.byref(op(32, 64, layout=5)), ctypes.byref(op(48, 64, 1)), FAKE, 64, 0,
+                 None) == -4
+        wt = op(48, 64, 1, layout=1, ld_codes=32, codes_t=FAKE, scales_t=FAKE, ld_codes_t=48,
+                ld_scales_t=4)  # dgrad reads the transposed copy: 48-byte rows
+        assert g(1, ctypes.byref(op(32, 48)), ctypes.byref(wt), FAKE, 64, 0, None) == -3
+
+    mx = lambda rows, cols, **kw: _desc(**dict(dict(codes=FAKE, scales=FAKE, ld_codes=32,
+                                                    ld_scales=4, rows=rows, cols=cols, block=2),
+                                               **kw))
+    assert lib.nvfp4_mx_quantize(FAKE, 32, 64, 64, 0, 0, 0, 0, ctypes.byref(mx(0, 0, layout=1)),
+                                 None) == -4
+    assert lib.nvfp4_mx_gemm(ctypes.byref(mx(16, 64, layout=1)), ctypes.byref(mx(8, 64)), FAKE,
+                             64, 1, None) == -4

@@ -71,8 +71,12 @@ def _sample_rows(n, seed, total=256):
     return rows
 
 
-def _same(g_codes, g_scales, o, what):
-    gc = g_codes[:, : o.codes.shape[1]].cpu().numpy()
+def _same(g, o, what, transposed=False):
+    """Every code and scale of the device tensor g (its transposed copy if
+    `transposed`) equals the oracle's o; codes read back in row-major order
+    whatever the tensor's code layout."""
+    gc = g.codes_t_host() if transposed else g.codes_host()
+    g_scales = g.scales_t if transposed else g.scales
     if not np.array_equal(gc, o.codes):
         bad = np.argwhere(gc != o.codes)
         raise AssertionError(f"{what}: {len(bad)} code bytes differ, first at {tuple(bad[0])}")
@@ -103,24 +107,24 @@ def _check_nvfp4_layer(torch, oracle, q, L, idx):
     print(f"{tag}: X, W and W^T in full", flush=True)
     qx = oracle.quantize(X, oracle.BLOCK_1X16, oracle.RNE)
     _check_scalars(L.gx, qx, f"{tag} X")
-    _same(L.gx.codes, L.gx.scales, qx, f"{tag} X")
+    _same(L.gx, qx, f"{tag} X")
     qw = oracle.quantize(W, oracle.BLOCK_16X16, oracle.RNE)
     _check_scalars(L.gw, qw, f"{tag} W")
-    _same(L.gw.codes, L.gw.scales, qw, f"{tag} W")
+    _same(L.gw, qw, f"{tag} W")
     qwt = oracle.quantize(np.ascontiguousarray(W.T), oracle.BLOCK_16X16, oracle.RNE)
-    _same(L.gw.codes_t, L.gw.scales_t, qwt, f"{tag} W^T (dgrad operand)")
+    _same(L.gw, qwt, f"{tag} W^T (dgrad operand)", transposed=True)
     del qwt
     print(f"{tag}: dY (SR) in full", flush=True)
     qdy = oracle.quantize(DY, oracle.BLOCK_1X16, oracle.SR, L.seed + SR_SEED_DY)
     _check_scalars(L.gdy, qdy, f"{tag} dY")
-    _same(L.gdy.codes, L.gdy.scales, qdy, f"{tag} dY")
+    _same(L.gdy, qdy, f"{tag} dY")
     print(f"{tag}: RHT operands in full", flush=True)
     qdyt = oracle.rht_quantize(DY, L.mask, oracle.SR, L.seed + SR_SEED_DY_RHT)
     _check_scalars(L.gdyt, qdyt, f"{tag} RHT(dY)^T")
-    _same(L.gdyt.codes, L.gdyt.scales, qdyt, f"{tag} RHT(dY)^T")
+    _same(L.gdyt, qdyt, f"{tag} RHT(dY)^T")
     qxt = oracle.rht_quantize(X, L.mask, oracle.RNE)
     _check_scalars(L.gxt, qxt, f"{tag} RHT(X)^T")
-    _same(L.gxt.codes, L.gxt.scales, qxt, f"{tag} RHT(X)^T")
+    _same(L.gxt, qxt, f"{tag} RHT(X)^T")
     del X, W, DY
 
     print(f"{tag}: GEMMs on 256 rows each", flush=True)
