@@ -189,17 +189,18 @@ __device__ __forceinline__ uint2 encode16_sr(const float (&v)[16], float f, uint
 }
 
 // ---------------------------------------------------------------------------
-// 1x16 quantiser: one thread per 16-element block.  A wave covers 4 rows x 16
-// blocks: lane l takes row 4 g + (l / 4) % 4 and block 16 c + 4 (l / 16) +
-// l % 4, so that its codes fill whole 128-byte lines in either code layout
-// (one K step of 4 rows interleaved; 4 row-major rows of 128 bytes) and each
-// row is read in 512-byte runs.  With one row per wave, interleaved pieces of
-// one line came from waves far apart (often on other XCDs, whose L2s each
-// wrote back a part of the line): 30 % slower on the 12B-layer dY.
+// 1x16 quantiser: one thread per 16-element block.  A workgroup of 4 waves
+// covers 4 rows x 64 blocks, one row per wave, so each wave reads 2 KB of a
+// row.  Interleaved codes go through LDS, and each wave then writes 4 whole
+// 128-byte lines (one K step of the 4 rows in each).  Measured on the
+// 12B-layer dY (RNE, cold): 83 us; a wave per 4 rows x 16 blocks writing
+// whole lines straight from registers took 87 us (4 rows x 512-byte reads
+// per wave); the row-major form's mapping (a wave per 64 blocks of one row,
+// rows of a line group in workgroups far apart, often on other XCDs whose
+// L2s each wrote back a part of the line) took 108 us.  Row-major codes are
+// written straight from registers (a wave writes 512 bytes of its row).
 // ---------------------------------------------------------------------------
 
-// kRht: the 16-point RHT of the block first (the fprop / dgrad ablation;
-// the transform runs along the rows, i.e. within the block).
 template <bool kSR, bool kRht = false>
 __global__ __launch_bounds__(256) void k_quant_1x16(
     const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
@@ -207,34 +208,43 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
     int64_t ld_codes, bool il, uint8_t* __restrict__ scales, int64_t ld_scales,
     float* __restrict__ amax_out, float* __restrict__ s_enc_out, uint32_t mask = 0u)
 {
+    __shared__ uint2 sc[4][64];  // interleaved codes of the workgroup's 4 rows
     const int64_t nb = cols >> 4;
-    const int64_t nchunk = (nb + 15) >> 4;  // 16-block chunks per row
-    const int64_t t = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t nchunk = (nb + 63) >> 6;  // 64-block chunks per row
     const float amax = *amax_src;
     const float s_enc = tensor_scale(amax);
-    if (t == 0) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
         *amax_out = amax;
         *s_enc_out = s_enc;
     }
-    const int l = (int)(t & 63);
-    const int64_t u = t >> 6;                // this wave's (row group, chunk)
-    const int64_t g = u / nchunk, c = u - g * nchunk;
-    const int64_t r = 4 * g + ((l >> 2) & 3);
-    const int64_t b = 16 * c + 4 * (l >> 4) + (l & 3);
-    if (r >= rows || b >= nb) return;
-    const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 16);
-    float v[16];
-    unpack16(ld_stream(src), ld_stream(src + 1), v);
-    if constexpr (kRht) rht16(v, mask);
-    const uint32_t sb = block_scale(absmax16(v), s_enc);
-    const float f = block_factor(sb, s_enc);
-    uint2 pk;
-    if constexpr (kSR)
-        pk = encode16_sr(v, f, seed, (uint64_t)(r * cols + b * 16) >> 3);
-    else
-        pk = encode16_rne(v, f);
-    *reinterpret_cast<uint2*>(codes + code_offset(r, b * 8, ld_codes, il)) = pk;
-    scales[r * ld_scales + b] = (uint8_t)sb;
+    const int64_t g = blockIdx.x / nchunk, c = blockIdx.x - g * nchunk;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int64_t r = 4 * g + w;
+    const int64_t b = 64 * c + l;
+    if (r < rows && b < nb) {
+        const uint4* src = reinterpret_cast<const uint4*>(x + r * ld + b * 16);
+        float v[16];
+        unpack16(ld_stream(src), ld_stream(src + 1), v);
+        if constexpr (kRht) rht16(v, mask);
+        const uint32_t sb = block_scale(absmax16(v), s_enc);
+        const float f = block_factor(sb, s_enc);
+        uint2 pk;
+        if constexpr (kSR)
+            pk = encode16_sr(v, f, seed, (uint64_t)(r * cols + b * 16) >> 3);
+        else
+            pk = encode16_rne(v, f);
+        scales[r * ld_scales + b] = (uint8_t)sb;
+        if (!il) *reinterpret_cast<uint2*>(codes + r * ld_codes + b * 8) = pk;
+        else sc[w][l] = pk;
+    }
+    if (!il) return;  // uniform over the launch
+    __syncthreads();
+    // thread t: line t / 16 of the chunk, row (t / 4) % 4, block 4 (t / 16) + t % 4
+    const int t = threadIdx.x;
+    const int orow = (t >> 2) & 3, oblk = 4 * (t >> 4) + (t & 3);
+    const int64_t ro = 4 * g + orow, bo = 64 * c + oblk;
+    if (ro < rows && bo < nb)
+        *reinterpret_cast<uint2*>(codes + code_offset(ro, bo * 8, ld_codes, true)) = sc[orow][oblk];
 }
 
 // ---------------------------------------------------------------------------
@@ -898,10 +908,10 @@ static int grid_for(int64_t work, int64_t per_block, int64_t cap)
     return (int)(g < cap ? g : cap);
 }
 
-// Threads of a k_quant_1x16 launch: a wave per 4 rows x 16 blocks.
+// Threads of a k_quant_1x16 launch: a workgroup of 256 per 4 rows x 64 blocks.
 static int64_t quant_1x16_threads(int64_t rows, int64_t cols)
 {
-    return ((rows + 3) / 4) * (((cols >> 4) + 15) / 16) * 64;
+    return ((rows + 3) / 4) * (((cols >> 4) + 63) / 64) * 256;
 }
 
 void launch_amax_rows(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, float* amax,
