@@ -252,15 +252,16 @@ class BF16Linear:
 class TrainingStep:
     """Fprop of every layer in order, then the backward pass in reverse order.
 
-    The weights do not depend on anything else in the step: their
-    quantisation runs on a second stream from the start, beside the
-    activations' amax and quantisation on the main stream, and each layer's
-    fprop waits for its own weight.  Per layer in the backward pass, the
-    work both branches wait for runs on the main stream (the amax pass over
-    dY, plus the dual encode when the layer fuses its quantisers); then the
-    main stream quantises dY (SR, unless already done) and runs dgrad while
-    the wgrad branch (RHT operands, which need only the maxima, unless
-    already encoded, and the wgrad GEMM) runs on the second stream.  Wgrad feeds nothing later in the step, so it overlaps with dgrad
+    The weights do not depend on anything else in the step: the first
+    layer's weight is quantised on the main stream while its activation's
+    amax and quantisation run on a second stream, and every later layer's
+    weight follows on the second stream; each fprop waits for both of its
+    operands.  Per layer in the backward pass, the
+    main stream first runs the amax pass over dY and dY's dgrad operand (the
+    SR encode, or the dual encode when the layer fuses its quantisers); then
+    it runs dgrad while the wgrad branch (RHT operands, unless already
+    encoded, and the wgrad GEMM) runs on the second stream.  Wgrad feeds
+    nothing later in the step, so it overlaps with dgrad
     and with the next layer's backward work: each GEMM's last, partial wave
     of workgroups is filled by the other's.  The step ends with the main
     stream waiting for the second one.
@@ -295,27 +296,47 @@ class TrainingStep:
             e.record()
             marks[name].append((s, e))
 
+        # Before the first fprop both its operands are quantised concurrently;
+        # the longer of the two (the weight: amax, then the 16x16 encode with
+        # the transposed copy) runs on the main stream, so the fprop launch
+        # does not wait on the other stream for it (that wait cost ~17 us on
+        # the 12B layer).  The other layers' weights follow on the second
+        # stream, each ready long before its fprop.
         self.side.wait_stream(main)
-        ready = []
+        first = self.layers[0]
+        ops0 = first.forward_ops()
+        ready = [None]
         with torch.cuda.stream(self.side):
-            for layer in self.layers:
+            for n, f in ops0[:-1]:
+                call(n, f)
+            x0 = torch.cuda.Event()
+            x0.record()
+            for layer in self.layers[1:]:
                 for n, f in layer.weight_ops():
                     call(n, f)
                 ev = torch.cuda.Event()
                 ev.record()
                 ready.append(ev)
-        for layer, ev in zip(self.layers, ready):
+        for n, f in first.weight_ops():
+            call(n, f)
+        main.wait_event(x0)
+        call(*ops0[-1])  # the first layer's fprop
+        for layer, ev in zip(self.layers[1:], ready[1:]):
             ops = layer.forward_ops()
             for n, f in ops[:-1]:
                 call(n, f)
             main.wait_event(ev)
             call(*ops[-1])  # the layer's fprop
         for layer in reversed(self.layers):
-            for n, f in layer.backward_shared_ops():
+            # dY's amax and its dgrad operand first, alone on the main stream
+            # (the SR encode is on the path to dgrad; started beside it, the
+            # wgrad branch's encodes slowed it); then the wgrad branch on the
+            # second stream beside dgrad
+            for n, f in layer.backward_shared_ops() + layer.backward_quant_ops():
                 call(n, f)
             self.side.wait_stream(main)
             wg = layer.wgrad_ops()
-            for n, f in layer.backward_quant_ops() + layer.dgrad_ops():
+            for n, f in layer.dgrad_ops():
                 call(n, f)
             with torch.cuda.stream(self.side):
                 for n, f in (wg[:-1] if self.serial_gemms else wg):
