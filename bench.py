@@ -589,7 +589,7 @@ def main():
     ap.add_argument("--steps", type=int, default=None,
                     help="timed steps (default 20 for the layer, 5 for the MLP step)")
     ap.add_argument("--warmup", type=int, default=None,
-                    help="untimed warm-up steps (default 3 for the layer, 2 for the MLP step)")
+                    help="untimed warm-up steps (default 10 for the layer, 2 for the MLP step)")
     ap.add_argument("--workload", choices=["layer", "mlp"], default="layer",
                     help="layer: one 12B-style linear layer (the default bench line); "
                          "mlp: the 4-block MLP training step at 16384 tokens")
@@ -612,7 +612,10 @@ def main():
         sys.exit(2)
     mlp = args.workload == "mlp"
     steps = args.steps if args.steps is not None else (5 if mlp else 20)
-    warmup = args.warmup if args.warmup is not None else (2 if mlp else 3)
+    # the first steps after the inputs are made run ~0.4 % slower than later
+    # ones (clock and power settling): 10 untimed steps before the layer's
+    # timed ones
+    warmup = args.warmup if args.warmup is not None else (2 if mlp else 10)
 
     import torch
     import quantize_precision_gemm_amd as q

@@ -264,7 +264,8 @@ class TrainingStep:
     nothing later in the step, so it overlaps with dgrad
     and with the next layer's backward work: each GEMM's last, partial wave
     of workgroups is filled by the other's.  The step ends with the main
-    stream waiting for the second one.
+    stream waiting for the second one (with serial_gemms it already has, at
+    each wgrad).
     """
 
     def __init__(self, torch, layers, device, serial_gemms=False):
@@ -344,7 +345,8 @@ class TrainingStep:
             if self.serial_gemms:
                 main.wait_stream(self.side)
                 call(*wg[-1])
-        main.wait_stream(self.side)
+        if not self.serial_gemms:  # (serial: every launch on the second stream is waited for already)
+            main.wait_stream(self.side)
 
     def serial_ops(self):
         """(layer index, name, call) of the whole step in one serial order."""
