@@ -340,6 +340,15 @@ def _check_gemm_out(out, shape, device, dtypes=(torch.float32, torch.bfloat16)):
         raise ValueError(f"out: on {out.device}, expected {device}")
 
 
+def _new_gemm_out(shape, dtype, device):
+    """A GEMM output of `shape`: row pitch rounded up to 4 elements (the ABI's
+    ldc % 4 rule), so the result is a [:, :cols] view when cols % 4 != 0."""
+    rows, cols = shape
+    if cols % 4 == 0:
+        return torch.empty(shape, dtype=dtype, device=device)
+    return torch.empty((rows, _round_up(cols, 4)), dtype=dtype, device=device)[:, :cols]
+
+
 def _check_scalar_out(t, what, device):
     if t is not None:
         _check_buf(t, what, device, torch.float32, (1,))
@@ -479,7 +488,7 @@ def nvfp4_mx_gemm(a, b, out_dtype=torch.bfloat16, out=None, stream=None):
     _check_operand(a, "a")
     _check_operand(b, "b")
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+        out = _new_gemm_out((M, N), out_dtype, a.codes.device)
     _check_gemm_out(out, (M, N), a.codes.device)
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     da, db = a.descriptor(), b.descriptor()
@@ -500,7 +509,7 @@ def nvfp4_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None, fp8
     if pass_ == DGRAD:
         _check_nvfp4_buffers(b, b.rows, b.cols, b.block, a.codes.device, True, "b")
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+        out = _new_gemm_out((M, N), out_dtype, a.codes.device)
     _check_gemm_out(out, (M, N), a.codes.device)
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     da, db = a.descriptor(), b.descriptor()
@@ -537,7 +546,7 @@ def nvfp4_gemm_split(pass_, a, b, workspace=None, out_dtype=torch.bfloat16, out=
     if workspace is not None:
         _check_buf(workspace, "workspace", a.codes.device, torch.uint8, (need,))
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+        out = _new_gemm_out((M, N), out_dtype, a.codes.device)
     _check_gemm_out(out, (M, N), a.codes.device)
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     da, db = a.descriptor(), b.descriptor()
@@ -560,7 +569,7 @@ def nvfp4_gemm_split_noalloc(pass_, a, b, out_dtype=torch.bfloat16, out=None, st
     if pass_ == DGRAD:
         _check_nvfp4_buffers(b, b.rows, b.cols, b.block, a.codes.device, True, "b")
     if out is None:
-        out = torch.empty((M, N), dtype=out_dtype, device=a.codes.device)
+        out = _new_gemm_out((M, N), out_dtype, a.codes.device)
     _check_gemm_out(out, (M, N), a.codes.device)
     dt = OUT_FP32 if out.dtype == torch.float32 else OUT_BF16
     da, db = a.descriptor(), b.descriptor()
@@ -586,7 +595,7 @@ def nvfp4_gemm_amax(pass_, a, b, sign_mask=0, rht=True, out=None, amax=None, ama
     if pass_ == DGRAD:
         _check_nvfp4_buffers(b, b.rows, b.cols, b.block, dev, True, "b")
     if out is None:
-        out = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+        out = _new_gemm_out((M, N), torch.bfloat16, dev)
     _check_gemm_out(out, (M, N), dev, (torch.bfloat16,))
     _check_scalar_out(amax, "amax", dev)
     _check_scalar_out(amax_rht if rht else None, "amax_rht", dev)
@@ -625,7 +634,7 @@ def nvfp4_bf16_gemm(pass_, a, b, out_dtype=torch.bfloat16, out=None, stream=None
     else:
         raise ValueError(f"unknown pass {pass_}")
     if out is None:
-        out = torch.empty(shape, dtype=out_dtype, device=a.device)
+        out = _new_gemm_out(shape, out_dtype, a.device)
     _check_gemm_out(out, shape, a.device)
     if not _same_device(b.device, a.device):
         raise ValueError(f"b: on {b.device}, expected {a.device}")

@@ -92,3 +92,14 @@ def test_scalar_outputs():
         q._check_scalar_out(torch.empty(1, dtype=torch.float64), "amax_in", CPU)
     with pytest.raises(ValueError):
         q._check_scalar_out(torch.empty(0), "amax_in", CPU)
+
+
+@pytest.mark.parametrize("cols", [0, 1, 4, 203, 208])
+def test_allocated_gemm_output_pitch(cols):
+    # The C ABI takes an output row pitch that is a multiple of 4 elements; the
+    # binding's own outputs keep the logical shape and round only the pitch.
+    out = q._new_gemm_out((5, cols), torch.bfloat16, CPU)
+    assert tuple(out.shape) == (5, cols) and out.dtype == torch.bfloat16
+    if cols:
+        assert out.stride(1) == 1 and out.stride(0) == (cols + 3) // 4 * 4
+    q._check_gemm_out(out, (5, cols), CPU)

@@ -240,6 +240,36 @@ def test_padded_leading_dimensions(env, fp8):
     np.testing.assert_array_equal(b16, bf16_rne_bits(g32))
 
 
+@pytest.mark.parametrize("case", ["ldc % 8 == 4", "8-byte aligned view", "N % 8 == 3"])
+def test_bf16_output_alignment(env, case):
+    # The bf16 epilogue stores 16-byte row pieces when the output's rows allow
+    # it, else element by element: every placement gives the RNE of the same
+    # call's fp32 output, and nothing outside the logical output is written.
+    torch, oracle, q, wl, dev = env
+    rng = np.random.default_rng(23)
+    M, K = 300, 336
+    N = 203 if case == "N % 8 == 3" else 208
+    x = wl.student_t_unit_var(rng, (M, K), 4)
+    w = wl.normal(rng, (N, K), 0.02)
+    print(f"bf16 output placement: {case}", flush=True)
+    gx = q.nvfp4_quantize(to_dev(x, dev), layout=q.LAYOUT_INTERLEAVED)
+    gw = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_1X16, q.RNE, layout=q.LAYOUT_INTERLEAVED)
+    y32 = q.nvfp4_gemm(q.FPROP, gx, gw, torch.float32)
+    ld = {"ldc % 8 == 4": N + 4, "8-byte aligned view": N + 24, "N % 8 == 3": 216}[case]
+    assert ld % 4 == 0
+    off = 4 if case == "8-byte aligned view" else 0
+    buf = torch.full((M, ld + off), -3.0, dtype=torch.bfloat16, device=dev)
+    out = buf[:, off:off + N]
+    assert out.data_ptr() % 16 == (8 if off else 0)
+    q.nvfp4_gemm(q.FPROP, gx, gw, out=out)
+    torch.cuda.synchronize()
+    assert (buf[:, :off] == -3.0).all().item() and (buf[:, off + N:] == -3.0).all().item()
+    b16 = out.contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+    np.testing.assert_array_equal(b16, bf16_rne_bits(y32.cpu().numpy()))
+    want = oracle.gemm(oracle.FPROP, oracle.quantize(x), oracle.quantize(w))
+    assert rel_fro(y32.cpu().numpy(), want) <= TOL
+
+
 def _scaled(wl, bits, f):
     return wl.f32_to_bf16_bits((wl.bf16_bits_to_f32(bits).astype(np.float64) * f).astype(np.float32))
 
