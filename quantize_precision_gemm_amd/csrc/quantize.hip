@@ -255,7 +255,8 @@ __global__ __launch_bounds__(256) void k_quant_1x16(
 // leave as 128 contiguous bytes.  The transposed copy and its scales are
 // assembled in LDS and written as 64-byte code rows and 8-byte scale rows.
 // (128 x 128 tiles of 256 threads, with the transposed scales written byte
-// by byte, ran 4 % slower on the 12B-layer weight.)
+// by byte, ran 4 % slower on the 12B-layer weight.)  Interleaved outputs
+// without a transform go to k_quant_16x16_il below.
 // ---------------------------------------------------------------------------
 
 constexpr int kW2TC = 16, kW2RG = 32;  // tile columns x row groups of 4 per workgroup
@@ -354,6 +355,176 @@ __global__ __launch_bounds__(kW2TC * kW2RG) void k_quant_16x16(
             } else {
                 *reinterpret_cast<uint2*>(dst) = make_uint2(val.x, val.y);
             }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// 16x16 quantiser for interleaved codes (weights, no transform).  A wave
+// covers one tile row (16 rows) by 512 columns: lane l holds 8 columns (16
+// bytes) of each of the 16 rows, so every load instruction reads 1 KB of one
+// row, and lanes 2k and 2k+1 hold the two halves of tile column k (its
+// maximum is one lane-pair exchange).  A lane encodes one 32-bit word of 8
+// codes per row, then transposes its 16 x 8 nibbles in registers into the 8
+// columns' 8-byte pieces of the transposed copy.  The workgroup's 4 waves
+// take 4 consecutive tile rows, so it holds whole 128-byte lines (4 rows of
+// 64 elements) of both copies; they are assembled in LDS and leave as 16-byte
+// stores, 8 whole lines per instruction.  Inputs are finite, so the integer
+// maximum of the bf16 magnitudes is their float maximum.  Measured on the
+// 12B-layer weight (20480 x 5120, cold, kernel alone): 66 us against 80 us
+// for the row-major kernel above on the same layout; stored straight from
+// registers (8-byte pieces, 64 lines per store instruction for the
+// transposed copy) it took 86 us, with only the transposed copy staged 68 us.
+// ---------------------------------------------------------------------------
+
+constexpr int kW3Cols = 512, kW3Waves = 4;
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+// In-place 8 x 8 transpose of 4-bit elements: element (i, j) is nibble j of
+// w[i].  Swapping the off-diagonal 4 x 4, then 2 x 2, then 1 x 1 blocks.
+__device__ __forceinline__ void transpose_nibbles8(uint32_t* w)
+{
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t t = ((w[i] >> 16) ^ w[i + 4]) & 0x0000FFFFu;
+        w[i] ^= t << 16;
+        w[i + 4] ^= t;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = (k & 1) + 4 * (k >> 1);
+        const uint32_t t = ((w[i] >> 8) ^ w[i + 2]) & 0x00FF00FFu;
+        w[i] ^= t << 8;
+        w[i + 2] ^= t;
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const int i = 2 * k;
+        const uint32_t t = ((w[i] >> 4) ^ w[i + 1]) & 0x0F0F0F0Fu;
+        w[i] ^= t << 4;
+        w[i + 1] ^= t;
+    }
+}
+
+template <bool kSR>
+__global__ __launch_bounds__(64 * kW3Waves) void k_quant_16x16_il(
+    const uint16_t* __restrict__ x, int64_t rows, int64_t cols, int64_t ld,
+    const float* __restrict__ amax_src, uint64_t seed, uint8_t* __restrict__ codes,
+    int64_t ld_codes, uint8_t* __restrict__ scales, int64_t ld_scales,
+    uint8_t* __restrict__ codes_t, int64_t ld_codes_t, uint8_t* __restrict__ scales_t,
+    int64_t ld_scales_t, float* __restrict__ amax_out, float* __restrict__ s_enc_out)
+{
+    const int64_t nbx = (cols + kW3Cols - 1) / kW3Cols;
+    const int64_t bx = blockIdx.x % nbx, by = blockIdx.x / nbx;  // column chunks fastest
+    const int l = threadIdx.x & 63;
+    const int64_t tr = by * kW3Waves + (threadIdx.x >> 6);       // tile row
+    const int64_t r0 = 16 * tr, c0 = bx * kW3Cols + 8 * l;
+    const bool valid = r0 < rows && c0 < cols;  // lanes 2k, 2k+1 agree: cols % 16 == 0
+    const float amax = *amax_src;
+    const float s_enc = tensor_scale(amax);
+    if (blockIdx.x == 0 && threadIdx.x == 0) {
+        *amax_out = amax;
+        *s_enc_out = s_enc;
+    }
+
+    uint4 raw[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+        raw[i] = valid ? ld_stream(x + (r0 + i) * ld + c0) : make_uint4(0u, 0u, 0u, 0u);
+    u16x2_t m2 = {0, 0};
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t u[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+            m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2_t, u[k] & 0x7FFF7FFFu));
+    }
+    uint32_t mb = max((uint32_t)m2.x, (uint32_t)m2.y);
+    mb = max(mb, (uint32_t)__shfl_xor((int)mb, 1, 64));
+    const uint32_t sb = block_scale(__uint_as_float(mb << 16), s_enc);
+    const float f = block_factor(sb, s_enc);
+
+    uint32_t wd[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const uint32_t u[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+        if constexpr (kSR) {
+            float y[8];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                y[2 * k] = bf16_lo(u[k]) * f;
+                y[2 * k + 1] = bf16_hi(u[k]) * f;
+            }
+            wd[i] = e2m1_sr8(y, sr_draws8(seed, (uint64_t)((r0 + i) * cols + c0) >> 3).w);
+        } else {
+            uint32_t c = 0u;
+            c = e2m1_rne_pk<0>(c, bf16_lo(u[0]) * f, bf16_hi(u[0]) * f);
+            c = e2m1_rne_pk<1>(c, bf16_lo(u[1]) * f, bf16_hi(u[1]) * f);
+            c = e2m1_rne_pk<2>(c, bf16_lo(u[2]) * f, bf16_hi(u[2]) * f);
+            c = e2m1_rne_pk<3>(c, bf16_lo(u[3]) * f, bf16_hi(u[3]) * f);
+            wd[i] = c;
+        }
+    }
+    if (valid && (l & 1) == 0) {
+        const int64_t tc = c0 >> 4;
+        scales[tr * ld_scales + tc] = (uint8_t)sb;
+        if (scales_t) scales_t[tc * ld_scales_t + tr] = (uint8_t)sb;
+    }
+    // Both code copies are staged in LDS in line order (136-byte pitch
+    // against bank conflicts) and stored 16 bytes a lane, 8 whole lines per
+    // instruction.  The workgroup's codes are 128 lines (4 rows x 64
+    // elements): 16 row groups x 8 line columns.
+    constexpr int kPitch = 136;
+    __shared__ __attribute__((aligned(16))) uint8_t cl[128 * kPitch];
+    __shared__ __attribute__((aligned(16))) uint8_t tl[kW3Cols / 4 * kPitch];
+    const int w = threadIdx.x >> 6;
+#pragma unroll
+    for (int i = 0; i < 16; ++i)  // local row 16w + i, bytes 4l .. 4l+3 of the chunk
+        *reinterpret_cast<uint32_t*>(&cl[((4 * w + (i >> 2)) * 8 + (l >> 3)) * kPitch + (i & 3) * 32 + 4 * (l & 7)]) = wd[i];
+    const bool with_t = codes_t != nullptr;  // uniform over the launch
+    if (with_t) {
+        transpose_nibbles8(wd);      // rows 0-7: wd[j] = column j's 8 codes
+        transpose_nibbles8(wd + 8);  // rows 8-15
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int kc = 8 * l + j;
+            *reinterpret_cast<uint2*>(&tl[(kc >> 2) * kPitch + (kc & 3) * 32 + 8 * w]) = make_uint2(wd[j], wd[8 + j]);
+        }
+    }
+    __syncthreads();
+    const int64_t tr_end = rows >> 4;  // tile rows of the tensor
+#pragma unroll
+    for (int it = 0; it < 128 * 8 / (64 * kW3Waves); ++it) {
+        const int id = it * 64 * kW3Waves + threadIdx.x;
+        const int g = id >> 3, c = id & 7;         // line (row group g / 8, line column g % 8), chunk
+        const int64_t rg = by * 4 * kW3Waves + (g >> 3);                // global row group
+        const int64_t jb = bx * (kW3Cols / 64) + (g & 7);               // global line column
+        const int64_t nbytes = (cols >> 1) - (jb * 32 + 16 * (c & 1));  // 0, 8, 16 or more valid
+        if (4 * rg >= rows || nbytes <= 0) continue;
+        uint8_t* dst = codes + rg * 4 * ld_codes + jb * 128 + 16 * c;
+        const uint2 a = *reinterpret_cast<const uint2*>(&cl[g * kPitch + 16 * c]);
+        if (nbytes >= 16) {
+            const uint2 b = *reinterpret_cast<const uint2*>(&cl[g * kPitch + 16 * c + 8]);
+            *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
+        } else {
+            *reinterpret_cast<uint2*>(dst) = a;
+        }
+    }
+    if (!with_t) return;
+#pragma unroll
+    for (int it = 0; it < kW3Cols / 4 * 8 / (64 * kW3Waves); ++it) {
+        const int id = it * 64 * kW3Waves + threadIdx.x;
+        const int g = id >> 3, c = id & 7;           // line, 16-byte chunk: column 4g + c/2
+        const int64_t kcol = bx * kW3Cols + 4 * g + (c >> 1);
+        const int64_t t0 = by * kW3Waves + 2 * (c & 1);  // the chunk's first tile row
+        if (kcol >= cols || t0 >= tr_end) continue;
+        const uint2 a = *reinterpret_cast<const uint2*>(&tl[g * kPitch + 16 * c]);
+        uint8_t* dst = codes_t + code_offset(kcol, 8 * t0, ld_codes_t, true);
+        if (t0 + 1 < tr_end) {
+            const uint2 b = *reinterpret_cast<const uint2*>(&tl[g * kPitch + 16 * c + 8]);
+            *reinterpret_cast<uint4*>(dst) = make_uint4(a.x, a.y, b.x, b.y);
+        } else {
+            *reinterpret_cast<uint2*>(dst) = a;
         }
     }
 }
@@ -946,6 +1117,15 @@ void launch_quant(const uint16_t* x, int64_t rows, int64_t cols, int64_t ld, int
         else
             hipLaunchKernelGGL(k_quant_1x16<false>, g, dim3(256), 0, s, x, rows, cols, ld, amax_src,
                                seed, o.codes, o.ld_codes, o.il, o.scales, o.ld_scales, o.amax, o.s_enc);
+    } else if (o.il) {
+        const int64_t tiles = ((cols + kW3Cols - 1) / kW3Cols) * ((rows + 16 * kW3Waves - 1) / (16 * kW3Waves));
+        dim3 g(grid_for(tiles, 1, INT32_MAX));
+        auto go = [&](auto kern) {
+            hipLaunchKernelGGL(kern, g, dim3(64 * kW3Waves), 0, s, x, rows, cols, ld, amax_src, seed,
+                               o.codes, o.ld_codes, o.scales, o.ld_scales, o.codes_t, o.ld_codes_t,
+                               o.scales_t, o.ld_scales_t, o.amax, o.s_enc);
+        };
+        sr ? go(k_quant_16x16_il<true>) : go(k_quant_16x16_il<false>);
     } else {
         dim3 g((unsigned)((cols + kW2Cols - 1) / kW2Cols), (unsigned)((rows + kW2Rows - 1) / kW2Rows));
         if (sr)

@@ -100,6 +100,59 @@ def test_quantize_16x16_with_transpose(env, shape, rounding):
                           transposed=oracle.quantize(np.ascontiguousarray(w.T), oracle.BLOCK_16X16))
 
 
+def _logical(buf, rows, nbytes):
+    """Row-major view (all buffer rows x ld) of an interleaved buffer, and a
+    mask of the bytes outside the logical rows x nbytes."""
+    raw = buf.cpu().numpy()
+    full = raw.reshape(-1)[_offsets(raw.shape[0], raw.shape[1], raw.shape[1])]
+    outside = np.ones(full.shape, bool)
+    outside[:rows, :nbytes] = False
+    return full, outside
+
+
+@pytest.mark.parametrize("shape", [(16, 16), (272, 208), (64, 1056), (160, 2064), (336, 528)])
+@pytest.mark.parametrize("rounding", [0, 1])
+@pytest.mark.parametrize("transpose", [True, False])
+def test_quantize_16x16_interleaved_against_oracle(env, shape, rounding, transpose):
+    # The interleaved 16x16 encoder against the oracle: ragged tile rows
+    # (a workgroup takes 4) and column chunks (512 per wave), magnitudes over
+    # 80 binades, and nothing written outside the logical codes and scales.
+    torch, oracle, q, wl, dev = env
+    rows, cols = shape
+    rng = np.random.default_rng(rows * 3 + cols + 11 * rounding)
+    tile_mag = np.exp(rng.uniform(-40, 40, (rows // 16, cols // 16)))
+    x = rng.standard_normal(shape) * tile_mag.repeat(16, 0).repeat(16, 1)
+    w = wl.f32_to_bf16_bits(x.astype(np.float32))
+    print(f"16x16 interleaved {shape} rounding={rounding} transpose={transpose}", flush=True)
+    out = q.alloc_nvfp4(rows, cols, q.BLOCK_16X16, transpose, dev, IL)
+    for t in (out.codes, out.scales, out.codes_t, out.scales_t):
+        if t is not None:
+            t.fill_(0xAB)
+    g = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_16X16, rounding, 31, with_transpose=transpose,
+                         out=out, layout=IL)
+    torch.cuda.synchronize()
+    o = oracle.quantize(w, oracle.BLOCK_16X16, rounding, 31)
+    assert_same_quant(g, o, "16x16 il")
+    full, outside = _logical(g.codes, rows, cols // 2)
+    assert (full[outside] == 0xAB).all(), "codes written outside the tensor"
+    sc = g.scales.cpu().numpy()
+    assert (sc[:, cols // 16:] == 0xAB).all() and (sc[rows // 16:] == 0xAB).all()
+    if not transpose:
+        return
+    if rounding == 0:
+        ot = oracle.quantize(np.ascontiguousarray(w.T), oracle.BLOCK_16X16)
+        np.testing.assert_array_equal(g.codes_t_host(), ot.codes)
+        np.testing.assert_array_equal(g.scales_t_host(), ot.scales)
+    else:  # SR draws are indexed in W's layout: the copy is the same codes, transposed
+        codes = oracle.unpack_codes(o.codes, cols)
+        np.testing.assert_array_equal(oracle.unpack_codes(g.codes_t_host(), rows), codes.T)
+        np.testing.assert_array_equal(g.scales_t_host(), o.scales.T)
+    full, outside = _logical(g.codes_t, cols, rows // 2)
+    assert (full[outside] == 0xAB).all(), "transposed codes written outside the tensor"
+    st = g.scales_t.cpu().numpy()
+    assert (st[:, rows // 16:] == 0xAB).all() and (st[cols // 16:] == 0xAB).all()
+
+
 @pytest.mark.parametrize("shape", [(16, 8), (64, 72), (272, 264), (1040, 136)])
 @pytest.mark.parametrize("rounding", [0, 1])
 def test_rht_quantize(env, shape, rounding):
