@@ -110,6 +110,30 @@ def _logical(buf, rows, nbytes):
     return full, outside
 
 
+@pytest.mark.parametrize("shape", [(1, 16), (3, 48), (37, 336), (300, 1040), (129, 4112), (64, 5120)])
+@pytest.mark.parametrize("rounding", [0, 1])
+def test_quantize_1x16_interleaved_against_oracle(env, shape, rounding):
+    # The interleaved 1x16 encoder against the oracle: ragged 4-row groups
+    # and 512-column chunks, magnitudes over 80 binades per block, and
+    # nothing written outside the logical codes and scales.
+    torch, oracle, q, wl, dev = env
+    rows, cols = shape
+    rng = np.random.default_rng(rows * 13 + cols + rounding)
+    mag = np.exp(rng.uniform(-40, 40, (rows, cols // 16))).repeat(16, 1)
+    w = wl.f32_to_bf16_bits((rng.standard_normal(shape) * mag).astype(np.float32))
+    print(f"1x16 interleaved {shape} rounding={rounding}", flush=True)
+    out = q.alloc_nvfp4(rows, cols, q.BLOCK_1X16, False, dev, IL)
+    out.codes.fill_(0xAB)
+    out.scales.fill_(0xAB)
+    g = q.nvfp4_quantize(to_dev(w, dev), q.BLOCK_1X16, rounding, 77, out=out, layout=IL)
+    torch.cuda.synchronize()
+    assert_same_quant(g, oracle.quantize(w, oracle.BLOCK_1X16, rounding, 77), "1x16 il")
+    full, outside = _logical(g.codes, rows, cols // 2)
+    assert (full[outside] == 0xAB).all(), "codes written outside the tensor"
+    sc = g.scales.cpu().numpy()
+    assert (sc[:, cols // 16:] == 0xAB).all() and (sc[rows:] == 0xAB).all()
+
+
 @pytest.mark.parametrize("shape", [(16, 16), (272, 208), (64, 1056), (160, 2064), (336, 528)])
 @pytest.mark.parametrize("rounding", [0, 1])
 @pytest.mark.parametrize("transpose", [True, False])
